@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Attention-forward bench on one MI355X (gfx950).
+
+A step is one call of the hot path -- the HIP attention forward (``attn_fwd``, or
+``attn_fwd_varlen`` for the packed workload) -- over one batch of seeded synthetic BF16
+inputs that are already resident in HBM. W untimed warm-up steps, then exactly K timed
+steps between device synchronisations. Throughput counts 4*B*H*N^2*d flops per step
+(packed: sum over segments of 4*H*n^2*d) and is reported in TFLOP/s against the MI355X
+dense BF16 MFMA peak; the kernel's own duration is measured with HIP events recorded on
+the stream it is launched on.
+
+Beside it: the FP64 CPU oracle timed on a bounded seeded sample of query rows of the same
+workload (host cores), and a parity check of those rows against the GPU output.
+
+One JSON line is printed (rank 0). Run several GPUs? This bench is single-GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0          # MI355X published dense BF16 MFMA peak
+METRIC = "attention TFLOP/s (4·B·H·N²·d) and % of BF16 MFMA peak, 720p-like N"
+KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_dit_amd", "csrc", "attn_fwd_gfx950.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="video_720p")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="query rows of the seeded sample the FP64 oracle is timed and checked on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the attention kernel is sharded over heads by the caller, not here.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import video_diffusion_dit_amd as vd
+    from workloads import WORKLOADS, make_dense, make_varlen, sample_rows
+
+    w = WORKLOADS[args.workload]
+    t0 = time.time()
+    if w.kind == "dense":
+        qb, kb, vb = make_dense(w)
+        cu = None
+    else:
+        qb, kb, vb, cu = make_varlen(w)
+    print(f"[bench] generated {w.description} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    out = torch.empty_like(q)
+    if w.kind == "dense":
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    else:
+        lse = torch.empty((w.H, w.total_tokens), dtype=torch.float32, device="cuda:0")
+    cu_d = None if cu is None else torch.from_numpy(cu).to("cuda:0")
+    cu_host = None if cu is None else [int(x) for x in cu]
+    vd.load_library()
+    kernel = "attn_fwd_dense_kernel" if w.kind == "dense" else "attn_fwd_varlen_kernel"
+
+    def step():
+        if w.kind == "dense":
+            vd.attention._launch_dense(q, k, v, out, lse, w.scale)
+        else:
+            vd.attention._launch_varlen(q, k, v, cu_d, out, lse, w.scale, cu_host)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall_ms / args.steps
+    avg_kernel_ms = float(np.mean(kernel_ms))
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall, kernel avg {avg_kernel_ms:.3f} ms "
+          f"(min {min(kernel_ms):.3f}, max {max(kernel_ms):.3f}) -> {achieved:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.description,
+            "B": w.B, "H": w.H, "N": w.N if w.kind == "dense" else w.total_tokens, "d": w.d,
+            "segments": list(w.seqlens) if w.seqlens else None,
+            "flops_per_step": flops,
+            "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": kernel,
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(w.name, kernel),
+            "kernel_ms": {"avg": round(avg_kernel_ms, 4), "min": round(min(kernel_ms), 4),
+                          "max": round(max(kernel_ms), 4)},
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import attention_dense, attention_varlen, compare
+        from threadpoolctl import threadpool_info
+        rows = sample_rows(w, args.cpu_rows)
+        t1 = time.perf_counter()
+        if w.kind == "dense":
+            o_ref, lse_ref = attention_dense(qb, kb, vb, w.scale, rows=rows)
+        else:
+            o_ref, lse_ref = attention_varlen(qb, kb, vb, cu, w.scale, rows=rows)
+        cpu_s = time.perf_counter() - t1
+        if w.kind == "dense":
+            keys_per_row = np.full(rows.size, w.N, dtype=np.float64)
+        else:
+            T = w.total_tokens
+            seg = np.searchsorted(cu, rows % T, side="right") - 1
+            keys_per_row = (cu[seg + 1] - cu[seg]).astype(np.float64)
+        cpu_flops = float(np.sum(4.0 * w.d * keys_per_row))
+        blas_threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        result["cpu_baseline"] = {
+            "value": round(cpu_flops / cpu_s / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": min(blas_threads, host_cores()),
+            "kind": "oracle",
+            "sample": f"{rows.size} seeded query rows of {w.name} (each over its full key range), "
+                      f"FP64 NumPy/OpenBLAS, {cpu_s:.1f} s",
+        }
+        # parity of the same rows on the GPU output of the last timed step
+        og = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        og = (og.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        lg = lse.cpu().numpy().astype(np.float64)
+        if w.kind == "dense":
+            og, lg = og.reshape(-1, w.d)[rows], lg.reshape(-1)[rows]
+        else:
+            T = w.total_tokens
+            og, lg = og[rows % T, rows // T], lg[rows // T, rows % T]
+        m = compare(og, o_ref, lg, lse_ref)
+        result["parity"] = {k: (round(v, 8) if isinstance(v, float) else v) for k, v in m.items()}
+        print(f"[bench] oracle {rows.size} rows in {cpu_s:.1f}s; parity {result['parity']}",
+              file=sys.stderr, flush=True)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,103 @@
+/*
+ * attn.h -- C ABI of libattn: non-causal scaled-dot-product attention forward,
+ * BF16 Q/K/V at head_dim 128, written for AMD CDNA4 (gfx950).
+ *
+ * What is computed (per query row i of one sequence, over the keys j of that sequence):
+ *     x_ij = scale * <q_i, k_j>,   o_i = sum_j softmax_j(x_ij) v_j,   lse_i = ln sum_j exp(x_ij)
+ * Page "[sglang] SANA-Video 2.0 anchor attention ... FP32 upcast" (blog on sglang PR #49219),
+ * code analysis item 1: scaled_dot_product_attention(q, k, v, dropout_p=0.0) on 4-D,
+ * equal-shape BF16 tensors -- non-causal, no mask, no dropout. Its "lessons" list: QK^T,
+ * softmax and PV accumulate in FP32 from BF16 inputs. Its documentation item: the
+ * probabilities are rounded to BF16 before the PV product. Page "PR #33702 report",
+ * motivation and breakdown item 2: packed variable-length batches (THD layout, segment
+ * offsets) attend within each segment only; head size 128 only.
+ *
+ * Numerics: QK^T in FP32 (BF16 MFMA), softmax statistics in FP32, probabilities
+ * exp(x - m_ref) rounded to BF16 (round-to-nearest-even) before the PV product, where
+ * m_ref is a per-row running reference never above the row's running maximum; the
+ * normaliser l sums the FP32 probabilities; O = (PV accumulator) / l rounded to BF16 RNE.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library keeps no
+ *     reference after the call returns and allocates nothing.
+ *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     Only launch failures are reported (ATTN_ERR_HIP).
+ *   - All argument validation happens on the host before any HIP call; on an error
+ *     nothing is launched and no output is touched.
+ *   - Deterministic: the same inputs on the same device give the same output bits.
+ *   - Thread-safe and re-entrant; concurrent calls must not share output buffers.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, non-finite scale,
+                                   aliasing output, malformed segment arguments */
+    ATTN_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement (d != 128,
+                                   sizes beyond the kernel's index range); callers may fall back */
+    ATTN_ERR_WORKSPACE = -3,    /* workspace null or smaller than attn_fwd_varlen_workspace_bytes() */
+    ATTN_ERR_HIP = -4           /* the HIP runtime rejected a launch; see attn_last_error() */
+} attn_status_t;
+
+/*
+ * Dense attention forward.
+ *   q, k, v : BF16 [B, H, N, d], contiguous (d fastest), read only.
+ *   out     : BF16 [B, H, N, d], contiguous; every element is written. Must not overlap
+ *             q, k, v or lse.
+ *   lse     : FP32 [B, H, N] log-sum-exp of the scaled logits (natural log), or NULL.
+ *   B, H, N : batch, heads, tokens; each >= 1.
+ *   d       : head dimension; only 128 is supported (else ATTN_ERR_UNSUPPORTED).
+ *   scale   : multiplier of q.k (finite; 1/sqrt(d) is the usual value).
+ *   stream  : hipStream_t to launch on.
+ * Returns an attn_status_t.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int N, int d, float scale, void* stream);
+
+/*
+ * Packed variable-length attention forward (THD layout), attention confined to each segment.
+ *   q, k, v     : BF16 [T, H, d], contiguous, T = total_tokens (token-major, then head).
+ *   out         : BF16 [T, H, d]; every element of every token is written.
+ *   lse         : FP32 [H, T] or NULL.
+ *   cu_seqlens  : DEVICE int32 [nseg + 1] segment offsets: cu[0] = 0, non-decreasing,
+ *                 cu[nseg] = T. Empty segments are allowed. The kernel trusts these values;
+ *                 callers validate them (the Python binding does, on a host copy).
+ *   nseg        : number of segments, >= 1.
+ *   H, d        : heads (>= 1) and head dim (only 128).
+ *   total_tokens: T >= 0; T = 0 is a no-op that returns ATTN_OK.
+ *   workspace   : DEVICE scratch of at least attn_fwd_varlen_workspace_bytes(nseg, H, T)
+ *                 bytes, 256-byte aligned; holds the tile schedule (longest segment first).
+ *                 Its contents need no initialisation; it must not be shared by calls that
+ *                 may run concurrently.
+ * Returns an attn_status_t.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_varlen needs for these sizes (0 if the sizes are invalid). */
+size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Detail message of the most recent failing call on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Query rows per workgroup tile and keys per inner tile of the compiled kernel. */
+int attn_tile_rows(void);
+int attn_tile_keys(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,235 @@
+"""Python binding of libattn (include/attn.h): argument marshalling only.
+
+Every step of the attention forward runs in the gfx950 HIP kernels of libattn.so. This
+module checks tensor dtype/shape/device/contiguity, picks the current torch stream, and
+passes raw device pointers through ctypes. There is no CPU or PyTorch fallback: if the
+library is missing, every call raises.
+
+Guard semantics follow the pages' fast-path convention (page "[sglang] SANA-Video 2.0
+anchor attention ... FP32 upcast", code analysis item 1: a ``try_*`` call returns ``None``
+so the caller can fall back when dtype/shape/device do not fit) and the varlen backend's
+hard errors (page "PR #33702 report", risks: ValueError for a head size other than 128,
+TypeError for non-BF16 input).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+from .build import LIB_PATH
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_HIP = -4
+
+_lib = None
+_lib_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+class AttnError(RuntimeError):
+    """A libattn call returned a failure status."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"libattn status {status}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_LIBRARY", LIB_PATH)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libattn.so (once). Raises if it has not been built -- no fallback exists."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libattn.so not found at {path}; build it first "
+                               "(python -m video_diffusion_dit_amd.build)")
+        lib = ctypes.CDLL(path)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        lib.attn_fwd.restype = i32
+        lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+        lib.attn_fwd_varlen.restype = i32
+        lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.attn_fwd_varlen_workspace_bytes.restype = sz
+        lib.attn_status_string.argtypes = [i32]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_tile_rows.restype = i32
+        lib.attn_tile_keys.restype = i32
+        _lib = lib
+        return lib
+
+
+def _raise_for(lib, status: int):
+    if status == ATTN_OK:
+        return
+    detail = (lib.attn_last_error() or b"").decode() or lib.attn_status_string(status).decode()
+    if status == ATTN_ERR_UNSUPPORTED:
+        raise ValueError(f"libattn: unsupported request: {detail}")
+    if status == ATTN_ERR_INVALID_ARG:
+        raise ValueError(f"libattn: invalid argument: {detail}")
+    raise AttnError(status, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensors(q, k, v, ndim: int):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if t.dim() != ndim:
+            raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+
+
+def _default_scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+             return_lse: bool = False, out: torch.Tensor | None = None):
+    """Dense attention forward: q, k, v BF16 [B, H, N, 128] contiguous on one GPU.
+
+    Returns out (BF16 [B,H,N,128]) or (out, lse FP32 [B,H,N]). Launches on the current
+    torch stream of q's device and returns without synchronising.
+    """
+    _check_tensors(q, k, v, 4)
+    B, H, N, d = q.shape
+    if d != 128:
+        raise ValueError(f"head dimension {d} is not supported (only 128)")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _launch_dense(q, k, v, out, lse, _default_scale(d, scale))
+    return (out, lse) if return_lse else out
+
+
+def _launch_dense(q, k, v, out, lse, scale: float):
+    """One C-ABI call on already-checked tensors (the library validates again on the host)."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                          _stream_handle(q.device))
+    _raise_for(lib, st)
+
+
+def try_attn_fwd(q, k, v, scale=None, return_lse=False):
+    """attn_fwd, or None when the request is outside what the kernel implements (caller falls back)."""
+    try:
+        if not all(isinstance(t, torch.Tensor) for t in (q, k, v)):
+            return None
+        if not (q.is_cuda and q.dtype == k.dtype == v.dtype == torch.bfloat16 and q.dim() == 4
+                and q.shape == k.shape == v.shape and q.shape[-1] == 128):
+            return None
+        if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+            return None
+        return attn_fwd(q, k, v, scale=scale, return_lse=return_lse)
+    except ValueError:
+        return None
+
+
+def varlen_workspace_bytes(nseg: int, H: int, total_tokens: int) -> int:
+    return int(load_library().attn_fwd_varlen_workspace_bytes(nseg, H, total_tokens))
+
+
+def _workspace(device, nbytes: int) -> torch.Tensor:
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def check_cu_seqlens(cu_host, total_tokens: int):
+    """Validate segment offsets on the host: int32, cu[0] = 0, non-decreasing, cu[-1] = T."""
+    cu = [int(x) for x in cu_host]
+    if len(cu) < 2:
+        raise ValueError("cu_seqlens needs at least 2 entries")
+    if cu[0] != 0:
+        raise ValueError("cu_seqlens[0] must be 0")
+    if any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if cu[-1] != total_tokens:
+        raise ValueError(f"cu_seqlens[-1] = {cu[-1]} must equal the token count {total_tokens}")
+    if cu[-1] > 2**31 - 1:
+        raise ValueError("token count exceeds int32")
+    return cu
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                    scale: float | None = None, return_lse: bool = False,
+                    out: torch.Tensor | None = None, cu_seqlens_host=None):
+    """Packed varlen forward: q, k, v BF16 [T, H, 128] (THD), attention within each segment.
+
+    cu_seqlens: int32 tensor [nseg + 1] on q's device. The offsets are validated on a host
+    copy (``cu_seqlens_host`` if given, else copied from the device, which synchronises).
+    Returns out (BF16 [T,H,128]) or (out, lse FP32 [H,T]).
+    """
+    _check_tensors(q, k, v, 3)
+    T, H, d = q.shape
+    if d != 128:
+        raise ValueError(f"head dimension {d} is not supported (only 128)")
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dtype == torch.int32
+            and cu_seqlens.device == q.device and cu_seqlens.dim() == 1 and cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on q's device")
+    host = cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens.cpu().tolist()
+    if len(host) != cu_seqlens.numel():
+        raise ValueError("cu_seqlens_host does not match cu_seqlens")
+    check_cu_seqlens(host, T)
+    nseg = cu_seqlens.numel() - 1
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    _launch_varlen(q, k, v, cu_seqlens, out, lse, _default_scale(d, scale))
+    return (out, lse) if return_lse else out
+
+
+def _launch_varlen(q, k, v, cu_seqlens, out, lse, scale: float, cu_seqlens_host=None):
+    """One C-ABI call on already-checked tensors; cu_seqlens_host, if given, is re-validated."""
+    lib = load_library()
+    T, H, d = q.shape
+    nseg = cu_seqlens.numel() - 1
+    if cu_seqlens_host is not None:
+        check_cu_seqlens(cu_seqlens_host, T)
+    nbytes = int(lib.attn_fwd_varlen_workspace_bytes(nseg, H, T))
+    with torch.cuda.device(q.device):
+        ws = _workspace(q.device, nbytes)
+        st = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                                 nseg, H, T, d, scale, _ptr(ws), ws.numel(), _stream_handle(q.device))
+    _raise_for(lib, st)

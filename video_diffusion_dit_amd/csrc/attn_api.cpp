@@ -1,0 +1,142 @@
+// C ABI of libattn (declared in include/attn.h): host-side validation, then one launch.
+// No HIP call happens before every argument has been checked, so invalid requests are
+// rejected on any machine, GPU or not.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* msg) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+    return status;
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+    if (a == nullptr || b == nullptr || abytes == 0 || bbytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// Elements of a [d0, d1, d2, d3] tensor, or -1 past 2^62.
+long long product(long long a, long long b, long long c, long long d) {
+    const long long lim = 1LL << 62;
+    long long r = a;
+    for (long long x : {b, c, d}) {
+        if (x != 0 && r > lim / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+int check_common(const void* q, const void* k, const void* v, void* out, int H, int d, float scale) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be non-null device pointers");
+    if (H <= 0) return fail(ATTN_ERR_INVALID_ARG, "H must be >= 1");
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (d <= 0) return fail(ATTN_ERR_INVALID_ARG, "d must be >= 1");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
+    return ATTN_OK;
+}
+
+int check_aliasing(const void* q, const void* k, const void* v, void* out, float* lse,
+                   size_t tensor_bytes, size_t lse_bytes) {
+    if (overlaps(out, tensor_bytes, q, tensor_bytes) || overlaps(out, tensor_bytes, k, tensor_bytes) ||
+        overlaps(out, tensor_bytes, v, tensor_bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
+    if (lse != nullptr &&
+        (overlaps(lse, lse_bytes, out, tensor_bytes) || overlaps(lse, lse_bytes, q, tensor_bytes) ||
+         overlaps(lse, lse_bytes, k, tensor_bytes) || overlaps(lse, lse_bytes, v, tensor_bytes)))
+        return fail(ATTN_ERR_INVALID_ARG, "lse overlaps q, k, v or out");
+    return ATTN_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    return fail(ATTN_ERR_HIP, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+             int N, int d, float scale, void* stream) {
+    g_last_error[0] = '\0';
+    int st = check_common(q, k, v, out, H, d, scale);
+    if (st != ATTN_OK) return st;
+    if (B <= 0 || N <= 0) return fail(ATTN_ERR_INVALID_ARG, "B and N must be >= 1");
+    const long long elems = product(B, H, N, d);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const long long tiles = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
+    if (tiles < 0 || tiles > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    st = check_aliasing(q, k, v, out, lse, (size_t)elems * 2, (size_t)product(B, H, N, 1) * 4);
+    if (st != ATTN_OK) return st;
+    return hip_status(attn_impl::launch_dense(q, k, v, out, lse, B, H, N, scale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
+    if (nseg <= 0 || H <= 0 || total_tokens < 0) return 0;
+    return attn_impl::varlen_workspace_bytes(nseg, total_tokens);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (nseg <= 0) return fail(ATTN_ERR_INVALID_ARG, "nseg must be >= 1");
+    if (total_tokens == 0) {
+        // nothing to compute; still reject requests that would be invalid at any size
+        if (H <= 0) return fail(ATTN_ERR_INVALID_ARG, "H must be >= 1");
+        if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+        if (d != 128) return fail(d <= 0 ? ATTN_ERR_INVALID_ARG : ATTN_ERR_UNSUPPORTED,
+                                  "only head dimension 128 is supported");
+        return ATTN_OK;
+    }
+    int st = check_common(q, k, v, out, H, d, scale);
+    if (st != ATTN_OK) return st;
+    if (cu_seqlens == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens must be a non-null device pointer");
+    const long long elems = product(total_tokens, H, d, 1);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const long long grid = product((long long)total_tokens / attn_impl::tile_rows() + nseg, H, 1, 1);
+    if (grid < 0 || grid > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    const size_t need = attn_impl::varlen_workspace_bytes(nseg, total_tokens);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_fwd_varlen_workspace_bytes()");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    st = check_aliasing(q, k, v, out, lse, (size_t)elems * 2, (size_t)product(H, total_tokens, 1, 1) * 4);
+    if (st != ATTN_OK) return st;
+    if (overlaps(workspace, need, out, (size_t)elems * 2) || overlaps(workspace, need, q, (size_t)elems * 2) ||
+        overlaps(workspace, need, k, (size_t)elems * 2) || overlaps(workspace, need, v, (size_t)elems * 2) ||
+        overlaps(workspace, need, cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)))
+        return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor argument");
+    return hip_status(attn_impl::launch_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens,
+                                               scale, workspace, static_cast<hipStream_t>(stream)));
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID_ARG: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported (valid request outside what this library implements)";
+        case ATTN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_tile_rows(void) { return attn_impl::tile_rows(); }
+int attn_tile_keys(void) { return attn_impl::tile_keys(); }
+
+}  // extern "C"
