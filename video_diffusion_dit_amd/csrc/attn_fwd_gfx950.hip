@@ -14,8 +14,8 @@
 //   S^T[key, q] = K_tile . Q_w^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
 //                                     B = the wave's Q rows, held in VGPRs all along
 //   P = exp2(S*c - m_ref)             c = scale*log2(e); FP32 VALU
-//   O^T[dv, q] += V^T_tile . P^T      A = V^T rows from LDS, B = P (BF16) straight from
-//                                     the S^T accumulator registers
+//   O^T[dv, q] += V^T_tile . P^T      A = V^T from LDS by transposing reads, B = P (BF16)
+//                                     straight from the S^T accumulator registers
 //
 // Computing S and O transposed puts one query row in each lane (plus its partner lane
 // l^32), so row statistics need no cross-lane reductions except one lane-pair exchange.
@@ -23,21 +23,23 @@
 // m = 8(r/4) + 4g + r%4. Loading K row swap23(m) (bits 2 and 3 of m exchanged) into A row m
 // makes register r hold key 16(r/8) + 8g + r%8: registers 8h..8h+7 of lane group g are then
 // exactly 8 consecutive keys, which is the B-operand layout of the PV MFMA for key step h.
-// The same exchange on V^T rows makes each lane's O^T registers 8 consecutive output dims.
+// The same exchange on the value dims makes each lane's O^T registers 8 consecutive dims.
 //
-// K tiles sit in LDS row-major [64 keys][128 dims]; V tiles are transposed on their way
-// into LDS ([128 dims][64 keys]) so that the PV A operand is one 16-byte LDS read.
-// 16-byte chunks are XOR-swizzled so those reads are bank-conflict free. Two LDS stages:
-// tile j+1 is fetched from HBM/L2 into VGPRs while tile j is computed, then written to the
-// other stage; one barrier per tile.
+// Data movement: K and V tiles ([64 keys][128 dims] BF16, 16 KiB each) go from HBM/L2
+// straight into LDS with buffer loads (no VGPR staging); lanes fetch the 16-byte chunk
+// that belongs at their LDS slot, so the XOR-swizzled layouts cost nothing to build.
+// Keys past the sequence end fall outside the buffer resource and read as zeros. V stays
+// key-major in LDS; ds_read_b64_tr_b16 delivers it transposed: within 16 lanes, lane 4r+c
+// reads 4 dims of key row r and lane j receives dim j of the 4 rows. Two LDS stages: the
+// loads of tile j+1 are in flight while tile j is computed; one barrier per tile.
 //
-// Row statistics: m_ref (per row, in log2 units of the scaled logit) and l (per lane
+// Row statistics: m_ref (per row, in log2 units of the scaled logit) and l (per-lane
 // partial). The common path computes P with the current m_ref and only checks that no
 // lane's partial tile sum exceeds 2^8 (then no probability exceeds 2^8 and FP32/BF16 stay
 // exact in relative terms); otherwise (always on a row's first tile, where m_ref = -inf)
-// the wave takes the exact path: true row max, rescale of O and l, recompute of P. The
-// result is the same softmax; only the reference the BF16 probabilities are relative to
-// differs, which BF16 rounding (relative) does not see.
+// the wave recomputes S from LDS and takes the exact path: true row max, rescale of O and
+// l, recompute of P. The result is the same softmax; only the reference the BF16
+// probabilities are relative to differs, which BF16 rounding (relative) does not see.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -48,8 +50,11 @@ namespace {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 128;          // head dim
 constexpr int BN = 64;          // keys per tile
@@ -58,26 +63,25 @@ constexpr int NW = 4;           // waves per workgroup
 constexpr int BM = NW * QW;     // query rows per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
 
-constexpr int K_BYTES = BN * D * 2;
-constexpr int V_BYTES = BN * D * 2;
-constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+constexpr int ROW_BYTES = D * 2;                 // one key row in LDS
+constexpr int K_BYTES = BN * ROW_BYTES;          // 16 KiB
+constexpr int STAGE_BYTES = 2 * K_BYTES;         // K then V
+constexpr int LOADS_PER_WAVE = K_BYTES / 1024 / NW;   // 1 KiB per buffer-load instruction
+constexpr int BUF_FLAGS = 0x00020000;            // raw buffer, 32-bit data format
 constexpr float RESCALE_LIMIT = 256.0f;
 constexpr float LN2 = 0.693147180559945309f;
 
-static_assert(BN * D / 8 == 4 * NT, "K tile: four 16-byte chunks per thread");
-static_assert((BN / 2) * (D / 8) == 2 * NT, "V tile: two key pairs x 8 dims per thread");
+static_assert(LOADS_PER_WAVE * NW * 1024 == K_BYTES, "tile load split");
 
 __device__ __forceinline__ int swap23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// Byte offset of 16-byte chunk c (dims 8c..8c+7) of key row r in a K tile.
-__device__ __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
-
-// Byte offset of 16-byte chunk c (keys 8c..8c+7) of value-dim row r in a V^T tile.
-__device__ __forceinline__ int vt_off(int r, int c) {
-    return r * 128 + ((c ^ (((r >> 1) ^ (r >> 4)) & 7)) << 4);
-}
+// LDS layout of a K tile: key row r, 16-byte chunk c (dims 8c..8c+7) at r*256 + 16*(c ^ (r%16)).
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+// LDS layout of a V tile: key row r, chunk c at r*256 + 16*(c ^ v_swz(r)); chosen so that
+// the transposing reads (4 key rows x 2 chunks per 16 lanes) hit 32 distinct bank pairs.
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -85,99 +89,119 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One tile's worth of K and V held in VGPRs between its global load and its LDS store.
-struct Staged {
-    u32x4 k[4];
-    u32x4 va[2], vb[2];
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const bf16* base, long bytes) {
+    const int nbytes = bytes > 0x7fffffffL ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, nbytes, BUF_FLAGS);
+}
+
+// Per-lane constants of one workgroup-slot of the kernel.
+struct Lane {
+    int m, g;
+    int kld[8];          // LDS byte offset of K fragment for d-step s (key block 0)
+    int vld[4][2];       // LDS byte offset of the transposing V read for dim block b, half t
+    int koff[LOADS_PER_WAVE], voff[LOADS_PER_WAVE];   // global byte offsets within a tile
 };
 
-__device__ __forceinline__ void load_tile(Staged& st, const bf16* __restrict__ K,
-                                          const bf16* __restrict__ V, long rs, int key0, int n,
-                                          int tid) {
+__device__ __forceinline__ void init_lane(Lane& L, int tid, int rs_bytes) {
+    const int lane = tid & 63, w = tid >> 6;
+    L.m = lane & 31;
+    L.g = lane >> 5;
+    const int row = swap23(L.m);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + NT * i, r = idx >> 4, c = idx & 15;
-        const int key = min(key0 + r, n - 1);
-        st.k[i] = *reinterpret_cast<const u32x4*>(K + key * rs + c * 8);
-    }
+    for (int s = 0; s < 8; ++s) L.kld[s] = row * ROW_BYTES + (((2 * s + L.g) ^ k_swz(row)) << 4);
+    const int j = lane & 15, r = j >> 2, c4 = j & 3, mh = (lane >> 4) & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = tid + NT * i, kp = idx >> 4, c = idx & 15;
-        const int ka = min(key0 + 2 * kp, n - 1), kb = min(key0 + 2 * kp + 1, n - 1);
-        st.va[i] = *reinterpret_cast<const u32x4*>(V + ka * rs + c * 8);
-        st.vb[i] = *reinterpret_cast<const u32x4*>(V + kb * rs + c * 8);
-    }
-}
-
-__device__ __forceinline__ void store_tile(const Staged& st, char* lds, int tid) {
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + NT * i, r = idx >> 4, c = idx & 15;
-        *reinterpret_cast<u32x4*>(lds + k_off(r, c)) = st.k[i];
-    }
-    char* vt = lds + K_BYTES;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = tid + NT * i, kp = idx >> 4, c = idx & 15;
-        const int kchunk = kp >> 2, kbyte = (kp & 3) * 4;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t a = st.va[i][w], b = st.vb[i][w];
-            const uint32_t lo = (a & 0xffffu) | (b << 16);          // dim 8c+2w, keys 2kp, 2kp+1
-            const uint32_t hi = (a >> 16) | (b & 0xffff0000u);      // dim 8c+2w+1
-            const int r0 = 8 * c + 2 * w;
-            *reinterpret_cast<uint32_t*>(vt + vt_off(r0, kchunk) + kbyte) = lo;
-            *reinterpret_cast<uint32_t*>(vt + vt_off(r0 + 1, kchunk) + kbyte) = hi;
+        for (int t = 0; t < 2; ++t) {
+            const int vrow = 8 * L.g + 4 * t + r;   // + 16h, which does not change v_swz
+            const int chunk = 4 * b + 2 * mh + (c4 & 1);
+            L.vld[b][t] = vrow * ROW_BYTES + ((chunk ^ v_swz(vrow)) << 4) + ((c4 >> 1) << 3);
         }
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+        const int slot_row = 4 * (LOADS_PER_WAVE * w + i) + (lane >> 4);
+        const int slot_chunk = lane & 15;
+        L.koff[i] = slot_row * rs_bytes + ((slot_chunk ^ k_swz(slot_row)) << 4);
+        L.voff[i] = slot_row * rs_bytes + ((slot_chunk ^ v_swz(slot_row)) << 4);
     }
 }
 
-// Key (within the tile) held by register r of lane group g in an S^T accumulator block kb.
+// Issue the buffer->LDS loads of key tile `tile` (this wave's quarter of K and of V).
+__device__ __forceinline__ void load_tile(const Lane& L, char* stage, const bf16* K, const bf16* V,
+                                          long rs_bytes, long seq_bytes, int tile, int w) {
+    const long skip = (long)tile * BN * rs_bytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)((const char*)K + skip), seq_bytes - skip);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)((const char*)V + skip), seq_bytes - skip);
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+        char* dk = stage + (LOADS_PER_WAVE * w + i) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dk, 16, L.koff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dk + K_BYTES), 16, L.voff[i], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ bf16x8 lds_vt(const char* p0, const char* p1) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
+// Key (within the tile) held by register r of lane group g in S^T accumulator block kb.
 __device__ __forceinline__ int key_of(int kb, int r, int g) {
     return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
 }
 
-template <bool MASK>
-__device__ __forceinline__ void tile_step(const char* __restrict__ lds, const bf16x8 (&qf)[8],
-                                          f32x16 (&oacc)[4], float& mref, float& lsum, float c,
-                                          int valid, int m, int g) {
-    // S^T = K_tile . Q^T
-    f32x16 sacc[2];
+__device__ __forceinline__ void qk(const char* __restrict__ kt, const Lane& L, const bf16x8 (&qf)[8],
+                                   f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = f32x16{};
-        const int row = 32 * kb + swap23(m);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(lds + k_off(row, 2 * s + g));
-            sacc[kb] = mfma(kf, qf[s], sacc[kb]);
-        }
+        for (int s = 0; s < 8; ++s)
+            sacc[kb] = mfma(lds_b128(kt + L.kld[s] + kb * 32 * ROW_BYTES), qf[s], sacc[kb]);
     }
+}
 
-    __builtin_amdgcn_sched_barrier(0);
-    // P = exp2(S*c - m_ref) with the current reference
-    float p[2][16];
-    float ts = 0.f;
-    float negm = -mref;
+template <bool MASK>
+__device__ __forceinline__ float exp_block(f32x16 (&sacc)[2], float c, float negm, int valid, int g) {
+    float ts[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums: no serial add chain
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float x = exp2_hw(__builtin_fmaf(sacc[kb][r], c, negm));
             if (MASK && key_of(kb, r, g) >= valid) x = 0.f;
-            p[kb][r] = x;
-            ts += x;
+            sacc[kb][r] = x;
+            ts[r & 3] += x;
         }
+    return (ts[0] + ts[1]) + (ts[2] + ts[3]);
+}
 
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const char* __restrict__ stage, const Lane& L,
+                                          const bf16x8 (&qf)[8], f32x16 (&oacc)[4], float& mref,
+                                          float& lsum, float c, int valid) {
+    f32x16 sacc[2];
+    qk(stage, L, qf, sacc);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float ts = exp_block<MASK>(sacc, c, -mref, valid, L.g);
     if (__any(!(ts <= RESCALE_LIMIT))) {
-        // exact path: new reference = running max, rescale accumulators, recompute P
+        // exact path: recompute S, take the running max as the new reference, rescale
+        qk(stage, L, qf, sacc);
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float t = sacc[kb][r] * c;
-                if (MASK && key_of(kb, r, g) >= valid) t = -INFINITY;
+                if (MASK && key_of(kb, r, L.g) >= valid) t = -INFINITY;
                 tmax = fmaxf(tmax, t);
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -189,17 +213,7 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ lds, const bf
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
         mref = mnew;
-        negm = -mnew;
-        ts = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = exp2_hw(__builtin_fmaf(sacc[kb][r], c, negm));
-                if (MASK && key_of(kb, r, g) >= valid) x = 0.f;
-                p[kb][r] = x;
-                ts += x;
-            }
+        ts = exp_block<MASK>(sacc, c, -mnew, valid, L.g);
     }
     lsum += ts;
 
@@ -208,62 +222,73 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ lds, const bf
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[h][i] = (bf16)p[h >> 1][8 * (h & 1) + i];
-
+        for (int i = 0; i < 8; ++i) pb[h][i] = (bf16)sacc[h >> 1][8 * (h & 1) + i];
     __builtin_amdgcn_sched_barrier(0);
+
     // O^T += V^T_tile . P^T
-    const char* vt = lds + K_BYTES;
+    const char* vt = stage + K_BYTES;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int row = 32 * b + swap23(m);
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + vt_off(row, 2 * h + g));
-            oacc[b] = mfma(vf, pb[h], oacc[b]);
-        }
-    }
+        for (int h = 0; h < 4; ++h)
+            oacc[b] = mfma(lds_vt(vt + L.vld[b][0] + h * 16 * ROW_BYTES, vt + L.vld[b][1] + h * 16 * ROW_BYTES),
+                           pb[h], oacc[b]);
+}
+
+// One full-tile iteration on LDS stage STAGE: wait for tile j, start tile j+1, compute j.
+template <int STAGE>
+__device__ __forceinline__ void full_step(char* smem, const Lane& L, const bf16* K, const bf16* V,
+                                          long rs_bytes, long seq_bytes, int j, int ntiles, int w,
+                                          const bf16x8 (&qf)[8], f32x16 (&oacc)[4], float& mref,
+                                          float& lsum, float c) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < ntiles) load_tile(L, smem + (1 - STAGE) * STAGE_BYTES, K, V, rs_bytes, seq_bytes, j + 1, w);
+    tile_step<false>(smem + STAGE * STAGE_BYTES, L, qf, oacc, mref, lsum, c, BN);
 }
 
 // One workgroup: query rows q0 .. q0+BM-1 of a sequence of n tokens whose rows are rs
-// elements apart (Q/K/V/O point at the sequence's first row; L at its first LSE entry).
+// elements apart (Q/K/V/O point at the sequence's first row; LSE at its first entry).
 __device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                            const bf16* __restrict__ V, bf16* __restrict__ O,
-                                           float* __restrict__ L, long rs, int n, int q0, float c) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int m = lane & 31, g = lane >> 5;
+                                           float* __restrict__ LSE, long rs, int n, int q0, float c) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    const int tid = threadIdx.x, w = tid >> 6;
+    const long rs_bytes = rs * 2;
+    const long seq_bytes = (long)n * rs_bytes;
+    Lane L;
+    init_lane(L, tid, (int)rs_bytes);
+    const int ntiles = (n + BN - 1) / BN;
+    const int nfull = n / BN;
+    load_tile(L, smem, K, V, rs_bytes, seq_bytes, 0, w);
 
-    const int qrow = q0 + w * QW + m;
+    const int qrow = q0 + w * QW + L.m;
     const bool qvalid = qrow < n;
     const int qr = min(qrow, n - 1);
     bf16x8 qf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        qf[s] = *reinterpret_cast<const bf16x8*>(Q + qr * rs + 16 * s + 8 * g);
+        qf[s] = *reinterpret_cast<const bf16x8*>(Q + qr * rs + 16 * s + 8 * L.g);
 
     f32x16 oacc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) oacc[b] = f32x16{};
     float mref = -INFINITY, lsum = 0.f;
 
-    // full tiles in the loop, a ragged last tile (if any) peeled after it
-    const int ntiles = (n + BN - 1) / BN;
-    const int nfull = n / BN;
-    Staged st;
-    load_tile(st, K, V, rs, 0, n, tid);
-    store_tile(st, smem, tid);
-    __syncthreads();
-
-    for (int j = 0; j < nfull; ++j) {
-        const char* cur = smem + (j & 1) * STAGE_BYTES;
-        const bool more = j + 1 < ntiles;
-        if (more) load_tile(st, K, V, rs, (j + 1) * BN, n, tid);
-        tile_step<false>(cur, qf, oacc, mref, lsum, c, BN, m, g);
-        if (more) store_tile(st, smem + ((j + 1) & 1) * STAGE_BYTES, tid);
-        __syncthreads();
+    int j = 0;
+    for (; j + 1 < nfull; j += 2) {
+        full_step<0>(smem, L, K, V, rs_bytes, seq_bytes, j, ntiles, w, qf, oacc, mref, lsum, c);
+        full_step<1>(smem, L, K, V, rs_bytes, seq_bytes, j + 1, ntiles, w, qf, oacc, mref, lsum, c);
     }
-    if (nfull < ntiles)
-        tile_step<true>(smem + (nfull & 1) * STAGE_BYTES, qf, oacc, mref, lsum, c, n - nfull * BN, m, g);
+    if (j < nfull) {
+        full_step<0>(smem, L, K, V, rs_bytes, seq_bytes, j, ntiles, w, qf, oacc, mref, lsum, c);
+        ++j;
+    }
+    if (j < ntiles) {   // ragged last tile, keys >= n masked (and read as zeros)
+        wait_vmem();
+        __syncthreads();
+        tile_step<true>(smem + (j & 1) * STAGE_BYTES, L, qf, oacc, mref, lsum, c, n - j * BN);
+    }
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float inv = 1.0f / ltot;
@@ -276,9 +301,9 @@ __device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf1
                 bf16x8 ov;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ov[i] = (bf16)(oacc[b][8 * hh + i] * inv);
-                *reinterpret_cast<bf16x8*>(orow + 32 * b + 16 * hh + 8 * g) = ov;
+                *reinterpret_cast<bf16x8*>(orow + 32 * b + 16 * hh + 8 * L.g) = ov;
             }
-        if (L != nullptr && g == 0) L[qrow] = (mref + __log2f(ltot)) * LN2;
+        if (LSE != nullptr && L.g == 0) LSE[qrow] = (mref + __log2f(ltot)) * LN2;
     }
 }
 
