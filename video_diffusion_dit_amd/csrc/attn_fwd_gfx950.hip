@@ -59,7 +59,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = 128;          // head dim
 constexpr int BN = 64;          // keys per tile
 constexpr int QW = 32;          // query rows per wave
-constexpr int NW = 4;           // waves per workgroup
+#ifndef ATTN_NW
+#define ATTN_NW 4
+#endif
+#ifndef ATTN_SETPRIO
+#define ATTN_SETPRIO 0
+#endif
+constexpr int NW = ATTN_NW;     // waves per workgroup
 constexpr int BM = NW * QW;     // query rows per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
 
@@ -157,82 +163,169 @@ __device__ __forceinline__ int key_of(int kb, int r, int g) {
     return 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
 }
 
-__device__ __forceinline__ void qk(const char* __restrict__ kt, const Lane& L, const bf16x8 (&qf)[8],
-                                   f32x16 (&sacc)[2]) {
+// S^T block kb (keys 32kb..32kb+31 of the tile) = K_block . Q^T: 8 MFMAs.
+__device__ __forceinline__ f32x16 qk_block(const char* __restrict__ kt, const Lane& L,
+                                           const bf16x8 (&qf)[8], int kb) {
+    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            sacc[kb] = mfma(lds_b128(kt + L.kld[s] + kb * 32 * ROW_BYTES), qf[s], sacc[kb]);
-    }
+    for (int s = 0; s < 8; ++s) acc = mfma(lds_b128(kt + L.kld[s] + kb * 32 * ROW_BYTES), qf[s], acc);
+    return acc;
 }
 
+// In place: p = exp2(S*c - m_ref) for one 32-key block; returns the lane's partial sum.
 template <bool MASK>
-__device__ __forceinline__ float exp_block(f32x16 (&sacc)[2], float c, float negm, int valid, int g) {
+__device__ __forceinline__ float exp_block(f32x16& sb, float c, float negm, int valid, int kb, int g) {
     float ts[4] = {0.f, 0.f, 0.f, 0.f};   // independent partial sums: no serial add chain
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = exp2_hw(__builtin_fmaf(sacc[kb][r], c, negm));
-            if (MASK && key_of(kb, r, g) >= valid) x = 0.f;
-            sacc[kb][r] = x;
-            ts[r & 3] += x;
-        }
+    for (int r = 0; r < 16; ++r) {
+        float x = exp2_hw(__builtin_fmaf(sb[r], c, negm));
+        if (MASK && key_of(kb, r, g) >= valid) x = 0.f;
+        sb[r] = x;
+        ts[r & 3] += x;
+    }
     return (ts[0] + ts[1]) + (ts[2] + ts[3]);
 }
 
+// Exact path for one 32-key block (rare): recompute its scores from LDS, move the
+// reference to the running max, rescale O and l, recompute the probabilities.
+template <bool MASK>
+__device__ __forceinline__ float exact_block(const char* __restrict__ kt, const Lane& L,
+                                                       const bf16x8 (&qf)[8], f32x16& sb,
+                                                       f32x16 (&oacc)[4], float& mref, float& lsum,
+                                                       float c, int valid, int kb) {
+    sb = qk_block(kt, L, qf, kb);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float t = sb[r] * c;
+        if (MASK && key_of(kb, r, L.g) >= valid) t = -INFINITY;
+        tmax = fmaxf(tmax, t);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(mref, tmax);
+    const float alpha = exp2_hw(mref - mnew);
+    lsum *= alpha;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    mref = mnew;
+    return exp_block<MASK>(sb, c, -mnew, valid, kb, L.g);
+}
+
+__device__ __forceinline__ void to_bf16(const f32x16& sb, bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[hh][i] = (bf16)sb[8 * hh + i];
+}
+
+// O^T += V^T . P^T over the 32 keys of block kb: 8 MFMAs (4 dim blocks x 2 key steps).
+__device__ __forceinline__ void pv_block(const char* __restrict__ vt, const Lane& L,
+                                         const bf16x8 (&pb)[2], f32x16 (&oacc)[4], int kb) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = 2 * kb + hh;
+            oacc[b] = mfma(lds_vt(vt + L.vld[b][0] + h * 16 * ROW_BYTES, vt + L.vld[b][1] + h * 16 * ROW_BYTES),
+                           pb[hh], oacc[b]);
+        }
+}
+
+// Two probabilities of one 32-key block, in place, accumulating the lane's partial sums.
+template <bool MASK>
+__device__ __forceinline__ void exp_pair(f32x16& sb, float c, float negm, int valid, int kb, int g,
+                                         int r0, float (&ts)[4]) {
+#pragma unroll
+    for (int r = r0; r < r0 + 2; ++r) {
+        float x = exp2_hw(__builtin_fmaf(sb[r], c, negm));
+        if (MASK && key_of(kb, r, g) >= valid) x = 0.f;
+        sb[r] = x;
+        ts[r & 3] += x;
+    }
+}
+
+__device__ __forceinline__ bf16x8 vt_frag(const char* __restrict__ vt, const Lane& L, int b, int h) {
+    return lds_vt(vt + L.vld[b][0] + h * 16 * ROW_BYTES, vt + L.vld[b][1] + h * 16 * ROW_BYTES);
+}
+
+template <int P>
+__device__ __forceinline__ void prio() {
+#if ATTN_SETPRIO
+    __builtin_amdgcn_s_setprio(P);
+#endif
+}
+
+// One 64-key tile, software-pipelined inside the wave so that the exp work of one 32-key
+// block issues while the matrix core runs the MFMAs of the other, and every LDS fragment
+// is read one region ahead of its MFMA:
+//   QK(b0) [+ read K b1] | QK(b1) + exp(b0) [+ read V b0] | check b0 |
+//   PV(b0) + exp(b1) [+ read V b1] | check b1 | PV(b1)
+// Every MFMA is followed by its share of VALU and LDS work; sched_barrier keeps that order.
 template <bool MASK>
 __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const Lane& L,
                                           const bf16x8 (&qf)[8], f32x16 (&oacc)[4], float& mref,
                                           float& lsum, float c, int valid) {
-    f32x16 sacc[2];
-    qk(stage, L, qf, sacc);
-    __builtin_amdgcn_sched_barrier(0);
-
-    float ts = exp_block<MASK>(sacc, c, -mref, valid, L.g);
-    if (__any(!(ts <= RESCALE_LIMIT))) {
-        // exact path: recompute S, take the running max as the new reference, rescale
-        qk(stage, L, qf, sacc);
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float t = sacc[kb][r] * c;
-                if (MASK && key_of(kb, r, L.g) >= valid) t = -INFINITY;
-                tmax = fmaxf(tmax, t);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(mref, tmax);
-        const float alpha = exp2_hw(mref - mnew);
-        lsum *= alpha;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-        mref = mnew;
-        ts = exp_block<MASK>(sacc, c, -mnew, valid, L.g);
-    }
-    lsum += ts;
-
-    // P^T fragments (BF16, round to nearest even)
-    bf16x8 pb[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[h][i] = (bf16)sacc[h >> 1][8 * (h & 1) + i];
-    __builtin_amdgcn_sched_barrier(0);
-
-    // O^T += V^T_tile . P^T
     const char* vt = stage + K_BYTES;
+    bf16x8 kf0[8], kf1[8], vf0[8], vf1[8];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int s = 0; s < 8; ++s) kf0[s] = lds_b128(stage + L.kld[s]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // QK(b0), reading K b1
+    prio<1>();
+    f32x16 s0 = f32x16{};
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-            oacc[b] = mfma(lds_vt(vt + L.vld[b][0] + h * 16 * ROW_BYTES, vt + L.vld[b][1] + h * 16 * ROW_BYTES),
-                           pb[h], oacc[b]);
+    for (int s = 0; s < 8; ++s) {
+        s0 = mfma(kf0[s], qf[s], s0);
+        kf1[s] = lds_b128(stage + L.kld[s] + 32 * ROW_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // QK(b1) beside exp(b0), reading V for PV(b0)
+    float negm = -mref;
+    float t0[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x16 s1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        s1 = mfma(kf1[s], qf[s], s1);
+        exp_pair<MASK>(s0, c, negm, valid, 0, L.g, 2 * s, t0);
+        vf0[s] = vt_frag(vt, L, s & 3, s >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    prio<0>();
+    float ts0 = (t0[0] + t0[1]) + (t0[2] + t0[3]);
+    if (__any(!(ts0 <= RESCALE_LIMIT))) ts0 = exact_block<MASK>(stage, L, qf, s0, oacc, mref, lsum, c, valid, 0);
+    lsum += ts0;
+    bf16x8 p0[2];
+    to_bf16(s0, p0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // PV(b0) beside exp(b1), reading V for PV(b1)
+    prio<1>();
+    negm = -mref;
+    float t1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        oacc[i & 3] = mfma(vf0[i], p0[i >> 2], oacc[i & 3]);
+        exp_pair<MASK>(s1, c, negm, valid, 1, L.g, 2 * i, t1);
+        vf1[i] = vt_frag(vt, L, i & 3, 2 + (i >> 2));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    prio<0>();
+    float ts1 = (t1[0] + t1[1]) + (t1[2] + t1[3]);
+    if (__any(!(ts1 <= RESCALE_LIMIT))) ts1 = exact_block<MASK>(stage, L, qf, s1, oacc, mref, lsum, c, valid, 1);
+    lsum += ts1;
+    bf16x8 p1[2];
+    to_bf16(s1, p1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // PV(b1)
+    prio<1>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oacc[i & 3] = mfma(vf1[i], p1[i >> 2], oacc[i & 3]);
+    prio<0>();
 }
 
 // One full-tile iteration on LDS stage STAGE: wait for tile j, start tile j+1, compute j.
@@ -317,7 +410,7 @@ struct DenseArgs {
     float c;
 };
 
-__global__ __launch_bounds__(NT, 2) void attn_fwd_dense_kernel(DenseArgs a) {
+__global__ __launch_bounds__(NT, 8 / NW) void attn_fwd_dense_kernel(DenseArgs a) {
     const int bh = blockIdx.x / a.ntq, qt = blockIdx.x - bh * a.ntq;
     const long base = (long)bh * a.N * D;
     attn_block(a.q + base, a.k + base, a.v + base, a.o + base,
@@ -403,7 +496,7 @@ struct VarlenArgs {
     float c;
 };
 
-__global__ __launch_bounds__(NT, 2) void attn_fwd_varlen_kernel(VarlenArgs a) {
+__global__ __launch_bounds__(NT, 8 / NW) void attn_fwd_varlen_kernel(VarlenArgs a) {
     const int e = blockIdx.x / a.H, h = blockIdx.x - e * a.H;
     if (e >= *reinterpret_cast<const int*>(a.ws)) return;
     const int2 t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
