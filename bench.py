@@ -57,6 +57,68 @@ def measured_traffic(workload: str, kernel: str):
         return None
 
 
+def _pmc_dispatches(csv_path: str, counter: str):
+    """[(dispatch id, kernel name, value in KiB)] for one counter of a rocprofv3 CSV, in order."""
+    import csv
+    acc = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+            acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+    return [(d, name, v) for (d, name), v in sorted(acc.items())]
+
+
+def write_traffic_profile(args) -> int:
+    """Scale FETCH_SIZE/WRITE_SIZE of the attention kernel by what the same counters read for a
+    copy of known size, and record the result with the kernel-source hash."""
+    fetch_csv, write_csv = args.write_traffic_profile
+    kernel = "attn_fwd_dense_kernel" if "varlen" not in args.workload else "attn_fwd_varlen_kernel"
+    copy_bytes = float(args.calibrate_copy_mib << 20)
+    if copy_bytes <= 0:
+        raise SystemExit("--calibrate-copy-mib (the copy size of the profiled run) is required")
+
+    def split(rows):
+        att = [v for _, name, v in rows if kernel in name]
+        others = [(d, name, v) for d, name, v in rows if kernel not in name]
+        return att, others[-1]           # the calibration copy is the last dispatch of the run
+
+    f_att, (_, copy_key, f_copy_kib) = split(_pmc_dispatches(fetch_csv, "FETCH_SIZE"))
+    w_att, (_, _, w_copy_kib) = split(_pmc_dispatches(write_csv, "WRITE_SIZE"))
+    f_copy, w_copy = f_copy_kib * 1024.0, w_copy_kib * 1024.0
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    fetch_b = sum(f_att) / len(f_att) * 1024.0 * f_scale
+    write_b = sum(w_att) / len(w_att) * 1024.0 * w_scale
+    from workloads import WORKLOADS
+    w = WORKLOADS[args.workload]
+    tokens = w.B * w.N if w.kind == "dense" else w.total_tokens
+    algorithmic = tokens * w.H * (8.0 * w.d + 4.0)
+    path = os.path.join(PROFILES, f"{kernel}_{args.workload}_hbm_traffic.txt")
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of {kernel} on the {args.workload} workload ({w.description})\n")
+        f.write("# from two rocprofv3 --pmc runs of bench.py, each also copying a buffer of known size\n")
+        for line in (args.profile_command or "").split(";"):
+            if line.strip():
+                f.write(f"# command: {line.strip()}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+        f.write(f"copy_kernel: {copy_key}\n")
+        f.write(f"copy_bytes: {copy_bytes:.0f}\n")
+        f.write(f"copy_fetch_kib_per_dispatch: {f_copy / 1024.0:.1f}\n")
+        f.write(f"copy_write_kib_per_dispatch: {w_copy / 1024.0:.1f}\n")
+        f.write(f"fetch_scale: {f_scale:.4f}\n")
+        f.write(f"write_scale: {w_scale:.4f}\n")
+        f.write(f"kernel_fetch_kib_per_dispatch_raw: {sum(f_att) / len(f_att):.1f}\n")
+        f.write(f"kernel_write_kib_per_dispatch_raw: {sum(w_att) / len(w_att):.1f}\n")
+        f.write(f"fetch_bytes_per_launch: {fetch_b:.0f}\n")
+        f.write(f"write_bytes_per_launch: {write_b:.0f}\n")
+        f.write(f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+        f.write(f"algorithmic_bytes_per_launch: {algorithmic:.0f}\n")
+        f.write(f"traffic_over_algorithmic: {(fetch_b + write_b) / algorithmic:.3f}\n")
+    print(open(path).read())
+    return 0
+
+
 def host_cores() -> int:
     try:
         return len(os.sched_getaffinity(0))
@@ -73,7 +135,18 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows of the seeded sample the FP64 oracle is timed and checked on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device-to-device copy of this many MiB "
+                         "(the known-size reference for the HBM byte counters)")
+    ap.add_argument("--write-traffic-profile", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
+                         "WRITE_SIZE) of a run with --calibrate-copy-mib into the profiles/ record; no GPU")
+    ap.add_argument("--profile-command", default="",
+                    help="the command lines that produced the counter files (recorded in the profile)")
     args = ap.parse_args()
+
+    if args.write_traffic_profile:
+        return write_traffic_profile(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -133,6 +206,14 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")   # contents irrelevant: bytes are counted
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_per_step = wall_ms / args.steps
     avg_kernel_ms = float(np.mean(kernel_ms))
     flops = w.flops()

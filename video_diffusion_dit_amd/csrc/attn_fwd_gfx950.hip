@@ -8,7 +8,7 @@
 // documentation item (probabilities rounded to BF16 before the PV GEMM); page "PR #33702
 // report", motivation (online softmax over KV blocks; packed varlen forward, THD layout).
 //
-// Work decomposition: one workgroup = 4 waves = 128 query rows of one (batch, head) or
+// Work decomposition: one workgroup = 8 waves = 256 query rows of one (batch, head) or
 // (segment, head); each wave owns 32 query rows for the whole key loop. Per 64-key tile:
 //
 //   S^T[key, q] = K_tile . Q_w^T      v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
@@ -32,6 +32,10 @@
 // key-major in LDS; ds_read_b64_tr_b16 delivers it transposed: within 16 lanes, lane 4r+c
 // reads 4 dims of key row r and lane j receives dim j of the 4 rows. Two LDS stages: the
 // loads of tile j+1 are in flight while tile j is computed; one barrier per tile.
+//
+// Schedule inside a tile (per wave), so the exp work issues while the matrix core is busy:
+//   QK(keys 0-31) | QK(keys 32-63) + exp(0-31) | PV(0-31) + exp(32-63) | PV(32-63)
+// every MFMA is followed by its share of exp work and the LDS reads one region ahead.
 //
 // Row statistics: m_ref (per row, in log2 units of the scaled logit) and l (per-lane
 // partial). The common path computes P with the current m_ref and only checks that no
@@ -59,13 +63,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = 128;          // head dim
 constexpr int BN = 64;          // keys per tile
 constexpr int QW = 32;          // query rows per wave
-#ifndef ATTN_NW
-#define ATTN_NW 4
-#endif
-#ifndef ATTN_SETPRIO
-#define ATTN_SETPRIO 0
-#endif
-constexpr int NW = ATTN_NW;     // waves per workgroup
+constexpr int NW = 8;           // waves per workgroup (two per SIMD)
 constexpr int BM = NW * QW;     // query rows per workgroup
 constexpr int NT = NW * 64;     // threads per workgroup
 
@@ -250,13 +248,6 @@ __device__ __forceinline__ bf16x8 vt_frag(const char* __restrict__ vt, const Lan
     return lds_vt(vt + L.vld[b][0] + h * 16 * ROW_BYTES, vt + L.vld[b][1] + h * 16 * ROW_BYTES);
 }
 
-template <int P>
-__device__ __forceinline__ void prio() {
-#if ATTN_SETPRIO
-    __builtin_amdgcn_s_setprio(P);
-#endif
-}
-
 // One 64-key tile, software-pipelined inside the wave so that the exp work of one 32-key
 // block issues while the matrix core runs the MFMAs of the other, and every LDS fragment
 // is read one region ahead of its MFMA:
@@ -274,7 +265,6 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const 
     __builtin_amdgcn_sched_barrier(0);
 
     // QK(b0), reading K b1
-    prio<1>();
     f32x16 s0 = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -294,7 +284,6 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const 
         vf0[s] = vt_frag(vt, L, s & 3, s >> 2);
         __builtin_amdgcn_sched_barrier(0);
     }
-    prio<0>();
     float ts0 = (t0[0] + t0[1]) + (t0[2] + t0[3]);
     if (__any(!(ts0 <= RESCALE_LIMIT))) ts0 = exact_block<MASK>(stage, L, qf, s0, oacc, mref, lsum, c, valid, 0);
     lsum += ts0;
@@ -303,7 +292,6 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const 
     __builtin_amdgcn_sched_barrier(0);
 
     // PV(b0) beside exp(b1), reading V for PV(b1)
-    prio<1>();
     negm = -mref;
     float t1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -313,7 +301,6 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const 
         vf1[i] = vt_frag(vt, L, i & 3, 2 + (i >> 2));
         __builtin_amdgcn_sched_barrier(0);
     }
-    prio<0>();
     float ts1 = (t1[0] + t1[1]) + (t1[2] + t1[3]);
     if (__any(!(ts1 <= RESCALE_LIMIT))) ts1 = exact_block<MASK>(stage, L, qf, s1, oacc, mref, lsum, c, valid, 1);
     lsum += ts1;
@@ -322,10 +309,8 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const 
     __builtin_amdgcn_sched_barrier(0);
 
     // PV(b1)
-    prio<1>();
 #pragma unroll
     for (int i = 0; i < 8; ++i) oacc[i & 3] = mfma(vf1[i], p1[i >> 2], oacc[i & 3]);
-    prio<0>();
 }
 
 // One full-tile iteration on LDS stage STAGE: wait for tile j, start tile j+1, compute j.
@@ -410,7 +395,7 @@ struct DenseArgs {
     float c;
 };
 
-__global__ __launch_bounds__(NT, 8 / NW) void attn_fwd_dense_kernel(DenseArgs a) {
+__global__ __launch_bounds__(NT, NW / 4) void attn_fwd_dense_kernel(DenseArgs a) {
     const int bh = blockIdx.x / a.ntq, qt = blockIdx.x - bh * a.ntq;
     const long base = (long)bh * a.N * D;
     attn_block(a.q + base, a.k + base, a.v + base, a.o + base,
@@ -496,7 +481,7 @@ struct VarlenArgs {
     float c;
 };
 
-__global__ __launch_bounds__(NT, 8 / NW) void attn_fwd_varlen_kernel(VarlenArgs a) {
+__global__ __launch_bounds__(NT, NW / 4) void attn_fwd_varlen_kernel(VarlenArgs a) {
     const int e = blockIdx.x / a.H, h = blockIdx.x - e * a.H;
     if (e >= *reinterpret_cast<const int*>(a.ws)) return;
     const int2 t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
