@@ -36,6 +36,9 @@
 // Schedule inside a tile (per wave), so the exp work issues while the matrix core is busy:
 //   QK(keys 0-31) | QK(keys 32-63) + exp(0-31) | PV(0-31) + exp(32-63) | PV(32-63)
 // every MFMA is followed by its share of exp work and the LDS reads one region ahead.
+// Two waves share each SIMD (w and w + NW/2). Issue arbitration favours the older one, which
+// would finish its tile early and wait at the barrier while the younger runs alone; the
+// younger wave therefore runs at raised priority (s_setprio) until its last exp block.
 //
 // Row statistics: m_ref (per row, in log2 units of the scaled logit) and l (per-lane
 // partial). The common path computes P with the current m_ref and only checks that no
@@ -257,7 +260,7 @@ __device__ __forceinline__ bf16x8 vt_frag(const char* __restrict__ vt, const Lan
 template <bool MASK>
 __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const Lane& L,
                                           const bf16x8 (&qf)[8], f32x16 (&oacc)[4], float& mref,
-                                          float& lsum, float c, int valid) {
+                                          float& lsum, float c, int valid, bool young) {
     const char* vt = stage + K_BYTES;
     bf16x8 kf0[8], kf1[8], vf0[8], vf1[8];
 #pragma unroll
@@ -301,6 +304,9 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ stage, const 
         vf1[i] = vt_frag(vt, L, i & 3, 2 + (i >> 2));
         __builtin_amdgcn_sched_barrier(0);
     }
+    // the younger wave of the SIMD drops back to normal priority (raised at the tile start)
+    if (young) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     float ts1 = (t1[0] + t1[1]) + (t1[2] + t1[3]);
     if (__any(!(ts1 <= RESCALE_LIMIT))) ts1 = exact_block<MASK>(stage, L, qf, s1, oacc, mref, lsum, c, valid, 1);
     lsum += ts1;
@@ -319,10 +325,17 @@ __device__ __forceinline__ void full_step(char* smem, const Lane& L, const bf16*
                                           long rs_bytes, long seq_bytes, int j, int ntiles, int w,
                                           const bf16x8 (&qf)[8], f32x16 (&oacc)[4], float& mref,
                                           float& lsum, float c) {
+    // Waves w and w + NW/2 share a SIMD. The older one wins issue arbitration and would run
+    // ahead, then idle at the barrier while the younger finishes alone; raising the younger
+    // wave's priority for the first three quarters of the tile keeps the two in step.
+    const bool young = w >= NW / 2;
     wait_vmem();
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (young) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < ntiles) load_tile(L, smem + (1 - STAGE) * STAGE_BYTES, K, V, rs_bytes, seq_bytes, j + 1, w);
-    tile_step<false>(smem + STAGE * STAGE_BYTES, L, qf, oacc, mref, lsum, c, BN);
+    tile_step<false>(smem + STAGE * STAGE_BYTES, L, qf, oacc, mref, lsum, c, BN, young);
 }
 
 // One workgroup: query rows q0 .. q0+BM-1 of a sequence of n tokens whose rows are rs
@@ -365,7 +378,7 @@ __device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf1
     if (j < ntiles) {   // ragged last tile, keys >= n masked (and read as zeros)
         wait_vmem();
         __syncthreads();
-        tile_step<true>(smem + (j & 1) * STAGE_BYTES, L, qf, oacc, mref, lsum, c, n - j * BN);
+        tile_step<true>(smem + (j & 1) * STAGE_BYTES, L, qf, oacc, mref, lsum, c, n - j * BN, false);
     }
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
