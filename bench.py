@@ -38,9 +38,16 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source; else None."""
+# Kernels one call of the hot path dispatches (the first is the dominant one).
+CALL_KERNELS = {
+    "dense": ("attn_fwd_dense_kernel", "attn_fwd_dense_split_kernel", "merge_kernel"),
+    "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule"),
+}
+
+
+def measured_traffic(workload: str, kernel: str, split_kv: bool):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source with the same split-KV setting; else None."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -51,8 +58,10 @@ def measured_traffic(workload: str, kernel: str):
             fields[key.strip()] = val.strip()
     if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
+    if fields.get("split_kv", "false") != ("true" if split_kv else "false"):
+        return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields["traffic_bytes_per_call"])
     except (KeyError, ValueError):
         return None
 
@@ -71,32 +80,43 @@ def _pmc_dispatches(csv_path: str, counter: str):
 
 
 def write_traffic_profile(args) -> int:
-    """Scale FETCH_SIZE/WRITE_SIZE of the attention kernel by what the same counters read for a
+    """Scale FETCH_SIZE/WRITE_SIZE of one call's kernels by what the same counters read for a
     copy of known size, and record the result with the kernel-source hash."""
     fetch_csv, write_csv = args.write_traffic_profile
-    kernel = "attn_fwd_dense_kernel" if "varlen" not in args.workload else "attn_fwd_varlen_kernel"
+    kind = "varlen" if "varlen" in args.workload else "dense"
+    names = CALL_KERNELS[kind]
+    kernel = names[0]
     copy_bytes = float(args.calibrate_copy_mib << 20)
     if copy_bytes <= 0:
         raise SystemExit("--calibrate-copy-mib (the copy size of the profiled run) is required")
 
-    def split(rows):
-        att = [v for _, name, v in rows if kernel in name]
-        others = [(d, name, v) for d, name, v in rows if kernel not in name]
-        return att, others[-1]           # the calibration copy is the last dispatch of the run
+    def base(name):
+        return name.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
 
-    f_att, (_, copy_key, f_copy_kib) = split(_pmc_dispatches(fetch_csv, "FETCH_SIZE"))
-    w_att, (_, _, w_copy_kib) = split(_pmc_dispatches(write_csv, "WRITE_SIZE"))
+    def of_call(name):
+        return base(name) in names
+
+    def split(rows):
+        att = [(name, v) for _, name, v in rows if of_call(name)]
+        others = [(d, name, v) for d, name, v in rows if not of_call(name)]
+        calls = sum(1 for name, _ in att if base(name) == names[0])
+        return att, calls, others[-1]    # the calibration copy is the last dispatch of the run
+
+    f_att, f_calls, (_, copy_key, f_copy_kib) = split(_pmc_dispatches(fetch_csv, "FETCH_SIZE"))
+    w_att, w_calls, (_, _, w_copy_kib) = split(_pmc_dispatches(write_csv, "WRITE_SIZE"))
+    split_kv = any("attn_fwd_dense_split_kernel" in name for name, _ in f_att)
     f_copy, w_copy = f_copy_kib * 1024.0, w_copy_kib * 1024.0
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
-    fetch_b = sum(f_att) / len(f_att) * 1024.0 * f_scale
-    write_b = sum(w_att) / len(w_att) * 1024.0 * w_scale
+    fetch_b = sum(v for _, v in f_att) / f_calls * 1024.0 * f_scale
+    write_b = sum(v for _, v in w_att) / w_calls * 1024.0 * w_scale
     from workloads import WORKLOADS
     w = WORKLOADS[args.workload]
     tokens = w.B * w.N if w.kind == "dense" else w.total_tokens
     algorithmic = tokens * w.H * (8.0 * w.d + 4.0)
     path = os.path.join(PROFILES, f"{kernel}_{args.workload}_hbm_traffic.txt")
     with open(path, "w") as f:
-        f.write(f"# HBM traffic of {kernel} on the {args.workload} workload ({w.description})\n")
+        f.write(f"# HBM traffic of one call ({', '.join(n for n in names)} as dispatched) on the "
+                f"{args.workload} workload ({w.description})\n")
         f.write("# from two rocprofv3 --pmc runs of bench.py, each also copying a buffer of known size\n")
         for line in (args.profile_command or "").split(";"):
             if line.strip():
@@ -108,12 +128,16 @@ def write_traffic_profile(args) -> int:
         f.write(f"copy_write_kib_per_dispatch: {w_copy / 1024.0:.1f}\n")
         f.write(f"fetch_scale: {f_scale:.4f}\n")
         f.write(f"write_scale: {w_scale:.4f}\n")
-        f.write(f"kernel_fetch_kib_per_dispatch_raw: {sum(f_att) / len(f_att):.1f}\n")
-        f.write(f"kernel_write_kib_per_dispatch_raw: {sum(w_att) / len(w_att):.1f}\n")
-        f.write(f"fetch_bytes_per_launch: {fetch_b:.0f}\n")
-        f.write(f"write_bytes_per_launch: {write_b:.0f}\n")
-        f.write(f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}\n")
-        f.write(f"algorithmic_bytes_per_launch: {algorithmic:.0f}\n")
+        f.write(f"split_kv: {'true' if split_kv else 'false'}\n")
+        for name in names:
+            fk = sum(v for n, v in f_att if base(n) == name) / f_calls
+            wk = sum(v for n, v in w_att if base(n) == name) / w_calls
+            if fk or wk:
+                f.write(f"raw_kib_per_call {name}: fetch {fk:.1f} write {wk:.1f}\n")
+        f.write(f"fetch_bytes_per_call: {fetch_b:.0f}\n")
+        f.write(f"write_bytes_per_call: {write_b:.0f}\n")
+        f.write(f"traffic_bytes_per_call: {fetch_b + write_b:.0f}\n")
+        f.write(f"algorithmic_bytes_per_call: {algorithmic:.0f}\n")
         f.write(f"traffic_over_algorithmic: {(fetch_b + write_b) / algorithmic:.3f}\n")
     print(open(path).read())
     return 0
@@ -135,6 +159,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows of the seeded sample the FP64 oracle is timed and checked on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-split-kv", action="store_true",
+                    help="dense workloads: plain attn_fwd, without cutting the last round's tiles over keys")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
                          "(the known-size reference for the HBM byte counters)")
@@ -181,10 +207,13 @@ def main() -> int:
     cu_d = None if cu is None else torch.from_numpy(cu).to("cuda:0")
     cu_host = None if cu is None else [int(x) for x in cu]
     vd.load_library()
-    kernel = "attn_fwd_dense_kernel" if w.kind == "dense" else "attn_fwd_varlen_kernel"
+    split = w.kind == "dense" and not args.no_split_kv and vd.splitkv_workspace_bytes(w.B, w.H, w.N) > 0
+    kernel = CALL_KERNELS[w.kind][0]
 
     def step():
-        if w.kind == "dense":
+        if w.kind == "dense" and split:
+            vd.attention._launch_dense_splitkv(q, k, v, out, lse, w.scale, 0)
+        elif w.kind == "dense":
             vd.attention._launch_dense(q, k, v, out, lse, w.scale)
         else:
             vd.attention._launch_varlen(q, k, v, cu_d, out, lse, w.scale, cu_host)
@@ -242,15 +271,19 @@ def main() -> int:
             "segments": list(w.seqlens) if w.seqlens else None,
             "flops_per_step": flops,
             "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+            "split_kv": bool(split),
         },
         "roofline": {
             "bound": "mfma",
             "kernel": kernel,
+            "timed": ("whole call on its stream: " + kernel +
+                      (" for whole query tiles, then attn_fwd_dense_split_kernel and merge_kernel"
+                       " for the last round's tiles" if split else "")),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name, kernel),
+            "traffic": measured_traffic(w.name, kernel, split),
             "kernel_ms": {"avg": round(avg_kernel_ms, 4), "min": round(min(kernel_ms), 4),
                           "max": round(max(kernel_ms), 4)},
         },

@@ -19,7 +19,8 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library keeps no
- *     reference after the call returns and allocates nothing.
+ *     reference after the call returns and allocates nothing (scratch comes from the
+ *     caller's workspace argument).
  *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *     Only launch failures are reported (ATTN_ERR_HIP).
  *   - All argument validation happens on the host before any HIP call; on an error
@@ -43,7 +44,7 @@ typedef enum {
                                    aliasing output, malformed segment arguments */
     ATTN_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement (d != 128,
                                    sizes beyond the kernel's index range); callers may fall back */
-    ATTN_ERR_WORKSPACE = -3,    /* workspace null or smaller than attn_fwd_varlen_workspace_bytes() */
+    ATTN_ERR_WORKSPACE = -3,    /* workspace null, misaligned or smaller than the *_workspace_bytes() query */
     ATTN_ERR_HIP = -4           /* the HIP runtime rejected a launch; see attn_last_error() */
 } attn_status_t;
 
@@ -61,6 +62,37 @@ typedef enum {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int N, int d, float scale, void* stream);
+
+/* Largest `slots` value attn_fwd_splitkv accepts. */
+#define ATTN_MAX_SLOTS 65536
+
+/*
+ * Dense attention forward with the key range of the last query tiles split across
+ * workgroups (split-KV), merged through each piece's running statistics. Page "PR #33702
+ * report", implementation breakdown item 2: the varlen backend there splits the key
+ * sequence of long sequences (a kv_splits setting chosen from the device and the length).
+ * Here the split serves the workgroups' last round on the device: the query tiles that
+ * would leave most compute units idle at the end are cut into equal shares of
+ * (query tile, key tile) pairs, one share per resident workgroup, and the pieces of a cut
+ * tile are combined as o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p (M = max_p m_p).
+ * The result equals attn_fwd's within rounding (BF16 P is taken relative to each piece's own
+ * reference); for the same inputs, slots and device it is bitwise repeatable.
+ *   q, k, v, out, lse, B, H, N, d, scale, stream : as for attn_fwd.
+ *   slots  : workgroups that run at once; <= 0 means the current device's compute units
+ *            (one workgroup each); at most ATTN_MAX_SLOTS.
+ *   workspace : DEVICE scratch of at least attn_fwd_splitkv_workspace_bytes(B, H, N, d, slots)
+ *            bytes, 256-byte aligned, holding the cut tiles' partial results between the
+ *            two kernels of the call; no initialisation needed; not to be shared by calls
+ *            that may run concurrently. May be NULL when that size is 0 (no tile is cut:
+ *            the call is then exactly attn_fwd).
+ * Returns an attn_status_t (ATTN_ERR_WORKSPACE for a missing, short or misaligned workspace).
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int H, int N, int d, float scale, int slots,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_splitkv needs (0: no split for these sizes, or invalid sizes). */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int slots);
 
 /*
  * Packed variable-length attention forward (THD layout), attention confined to each segment.

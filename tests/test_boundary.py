@@ -33,6 +33,9 @@ def lib():
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attn_fwd_varlen_workspace_bytes.restype = sz
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.restype = ctypes.c_char_p
     return lib
@@ -41,6 +44,7 @@ def lib():
 def test_header_declares_the_expected_api():
     fns = header_functions()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_varlen_workspace_bytes",
+                 "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -129,3 +133,53 @@ def test_python_guards_without_gpu():
         attn_fwd(q.float(), q.float(), q.float())            # non-BF16 is a TypeError
     with pytest.raises(ValueError):
         attn_fwd(q, q, q)                                     # CPU tensors are rejected
+
+
+# One partial result: 256 query rows x (128 O values + m_ref + l, padded to 132 floats).
+PART_BYTES = 256 * 132 * 4
+
+
+@pytest.mark.parametrize("B,H,N,slots,G", [
+    (1, 16, 180320, 256, 256),    # 11280 tiles = 44 rounds + 16: the last 272 over 256 workgroups
+    (1, 2, 180320, 256, 256),     # 1410 tiles = 5 rounds + 130
+    (1, 1, 8192, 64, 64),         # 32 tiles < 64 slots: each cut in two (64 key tiles a share)
+    (1, 1, 8192, 200, 200),       # shares of 20.48 key tiles: tiles cut into up to 8 pieces
+    (1, 1, 8192, 1000, 256),      # shares never shorter than 16 key tiles: at most 128*32/16
+])
+def test_splitkv_workspace_plan(lib, B, H, N, slots, G):
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, N, 128, slots) == 2 * G * PART_BYTES
+
+
+@pytest.mark.parametrize("B,H,N,slots", [
+    (1, 16, 32768, 256),          # 2048 tiles: whole rounds, nothing to cut
+    (4, 64, 512, 7),              # 8 key tiles per sequence: too short to cut
+    (1, 1, 8192, 1),              # one slot
+    (1, 1, 8192, 16),             # 32 tiles, 16 slots: two whole rounds
+    (1, 1, 8192, 65537),          # beyond ATTN_MAX_SLOTS
+    (0, 1, 8192, 64), (1, 0, 8192, 64), (1, 1, 0, 64),
+])
+def test_splitkv_no_workspace(lib, B, H, N, slots):
+    assert lib.attn_fwd_splitkv_workspace_bytes(B, H, N, 128, slots) == 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 8192, 64, 64) == 0      # d != 128
+
+
+def splitkv(lib, q=Q, o=O, N=8192, d=128, slots=64, ws=WS, wsb=None, lse=None):
+    if wsb is None:
+        wsb = lib.attn_fwd_splitkv_workspace_bytes(1, 1, N, 128, slots)
+    return lib.attn_fwd_splitkv(q, K, V, o, lse, 1, 1, N, d, 0.088, slots, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(d=64), UNSUPPORTED), (dict(slots=65537), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=WS + 16), WORKSPACE),
+    (dict(ws=O), INVALID), (dict(o=K), INVALID),
+])
+def test_splitkv_validation(lib, kw, code):
+    assert splitkv(lib, **kw) == code
+    assert lib.attn_last_error().decode()
+
+
+def test_python_splitkv_workspace_matches_c(lib):
+    from video_diffusion_dit_amd import splitkv_workspace_bytes
+    assert splitkv_workspace_bytes(1, 16, 180320, slots=256) == 2 * 256 * PART_BYTES
+    assert splitkv_workspace_bytes(1, 16, 32768, slots=256) == 0

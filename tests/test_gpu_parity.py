@@ -214,3 +214,83 @@ def test_varlen_empty_batch_is_noop(attn):
     out = attn.attn_fwd_varlen(z, z, z, dev_i32([0, 0, 0]))
     torch.cuda.synchronize()
     assert out.shape == (0, 2, 128)
+
+
+# ---- split-KV (attn_fwd_splitkv): the last, partly filled round of query tiles is cut over keys
+
+def split_plan(B, H, N, slots, min_tiles=16):
+    """(D, R, G, ntk) of the library's split plan (rows of 256 queries, 64-key tiles)."""
+    ntq, ntk = -(-N // 256), -(-N // 64)
+    items = B * H * ntq
+    full, r = divmod(items, slots)
+    if slots < 2 or r == 0 or ntk < min_tiles:
+        return items, 0, 0, ntk
+    if full >= 1:
+        R, G = slots + r, slots
+    else:
+        R, G = items, min(slots, items * ntk // min_tiles)
+        if G <= R:
+            return items, 0, 0, ntk
+    return items - R, R, G, ntk
+
+
+def cut_tiles(B, H, N, slots):
+    """Query tiles (flat index b*H*ntq + h*ntq + qt) whose key range the plan splits."""
+    D, R, G, ntk = split_plan(B, H, N, slots)
+    cut = set()
+    for i in range(R):
+        first, last = i * ntk, (i + 1) * ntk - 1
+        g0 = max(g for g in range(G) if g * R * ntk // G <= first)
+        g1 = max(g for g in range(G) if g * R * ntk // G <= last)
+        if g0 != g1:
+            cut.add(D + i)
+    return cut
+
+
+@pytest.mark.parametrize("B,H,N,slots", [
+    (1, 3, 4133, 7),      # 51 tiles: 42 whole, the last 9 cut over 7 workgroups; ragged last key tile
+    (2, 2, 3000, 5),      # 48 tiles: the last 8 over 5 workgroups
+    (1, 1, 8192, 64),     # 32 tiles, 64 workgroups: every tile cut in two
+    (1, 1, 8192, 200),    # shares of 20.48 key tiles: tiles cut in up to 8 pieces
+    (1, 2, 1100, 3),      # 10 tiles over 3 slots, 18 key tiles each (just above the minimum)
+])
+def test_splitkv_against_oracle_and_unsplit(attn, B, H, N, slots):
+    import torch
+    from gpu_util import bits_of, check, dev, f64_of
+    D, R, G, ntk = split_plan(B, H, N, slots)
+    assert G > 0 and attn.splitkv_workspace_bytes(B, H, N, slots=slots) > 0
+    qb, kb, vb = random_dense(B, H, N, seed=9000 + N + slots)
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    o, lse = attn.attn_fwd(q, k, v, scale=SCALE, return_lse=True, slots=slots)
+    o_plain, lse_plain = attn.attn_fwd(q, k, v, scale=SCALE, return_lse=True, split_kv=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_dense(qb, kb, vb, SCALE)
+    check(f64_of(o), o_ref, lse.cpu().numpy(), lse_ref, f"splitkv B={B} H={H} N={N} slots={slots}")
+    # query tiles computed whole are the plain kernel's rows, bit for bit; cut ones differ
+    # only by rounding (their probabilities are BF16 relative to each piece's reference)
+    cut = cut_tiles(B, H, N, slots)
+    assert cut
+    ntq = -(-N // 256)
+    ob, opb = bits_of(o).reshape(B * H, N, 128), bits_of(o_plain).reshape(B * H, N, 128)
+    lb, lpb = lse.cpu().numpy().reshape(B * H, N), lse_plain.cpu().numpy().reshape(B * H, N)
+    for t in range(B * H * ntq):
+        bh, qt = divmod(t, ntq)
+        rows = slice(qt * 256, min(N, (qt + 1) * 256))
+        if t not in cut:
+            assert np.array_equal(ob[bh, rows], opb[bh, rows]), t
+            assert np.array_equal(lb[bh, rows], lpb[bh, rows]), t
+
+
+def test_splitkv_deterministic_and_no_split_is_plain(attn):
+    import torch
+    from gpu_util import bits_of, dev
+    qb, kb, vb = random_dense(1, 1, 8192, seed=31)
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    a = attn.attn_fwd(q, k, v, slots=200)
+    b = attn.attn_fwd(q, k, v, slots=200)
+    c = attn.attn_fwd(q, k, v, slots=16)          # 32 tiles, 16 slots: whole rounds, no cut
+    d = attn.attn_fwd(q, k, v, split_kv=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(a), bits_of(b))
+    assert np.array_equal(bits_of(c), bits_of(d))
+    assert not np.array_equal(bits_of(a), bits_of(d))   # cut tiles do differ in rounding

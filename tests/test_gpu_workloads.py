@@ -38,14 +38,14 @@ def varlen_rows_with_tails(w, rows, cu, T):
     return np.unique(np.concatenate([rows, np.array(extra, dtype=np.int64)]))
 
 
-def run_dense_check(attn, w, label):
+def run_dense_check(attn, w, label, split_kv=True):
     import torch
     from gpu_util import check, dev, f64_of
     print(f"[case] {label}: generating {w.description}", flush=True)
     qb, kb, vb = make_dense(w)
     q, k, v = dev(qb), dev(kb), dev(vb)
     print(f"[case] {label}: launching", flush=True)
-    o, lse = attn.attn_fwd(q, k, v, scale=w.scale, return_lse=True)
+    o, lse = attn.attn_fwd(q, k, v, scale=w.scale, return_lse=True, split_kv=split_kv)
     torch.cuda.synchronize()
     rows = dense_rows_with_tails(w, sample_rows(w))
     o_ref, lse_ref = attention_dense(qb, kb, vb, w.scale, rows=rows)
@@ -80,7 +80,8 @@ def test_numerics_stress_dense_and_ragged(attn):
     import torch
     from gpu_util import bits_of, check, dev, dev_i32, f64_of
     w = WORKLOADS["numerics_stress"]
-    dense = run_dense_check(attn, w, "numerics_stress dense")
+    # the plain dense path (no key split), whose rows the varlen call must reproduce bit for bit
+    dense = run_dense_check(attn, w, "numerics_stress dense", split_kv=False)
     qb, kb, vb, o_dense, lse_dense = dense
     # realised logit range of the recipe, for the record
     qf = (qb[0, 0, :64].astype(np.uint32) << 16).view(np.float32).astype(np.float64)

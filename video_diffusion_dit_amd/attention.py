@@ -63,6 +63,10 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_varlen.restype = i32
         lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
         lib.attn_fwd_varlen_workspace_bytes.restype = sz
+        lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+        lib.attn_fwd_splitkv.restype = i32
+        lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.attn_fwd_splitkv_workspace_bytes.restype = sz
         lib.attn_status_string.argtypes = [i32]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -115,11 +119,15 @@ def _default_scale(d: int, scale):
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
-             return_lse: bool = False, out: torch.Tensor | None = None):
+             return_lse: bool = False, out: torch.Tensor | None = None, split_kv: bool = True,
+             slots: int = 0):
     """Dense attention forward: q, k, v BF16 [B, H, N, 128] contiguous on one GPU.
 
     Returns out (BF16 [B,H,N,128]) or (out, lse FP32 [B,H,N]). Launches on the current
-    torch stream of q's device and returns without synchronising.
+    torch stream of q's device and returns without synchronising. With split_kv (default)
+    the query tiles of the device's last, partly filled round of workgroups are split over
+    their key range (attn_fwd_splitkv; ``slots`` = concurrent workgroups, 0 = the device's
+    compute units); when no tile needs cutting this is the plain attn_fwd call.
     """
     _check_tensors(q, k, v, 4)
     B, H, N, d = q.shape
@@ -131,7 +139,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | N
     elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
-    _launch_dense(q, k, v, out, lse, _default_scale(d, scale))
+    if split_kv:
+        _launch_dense_splitkv(q, k, v, out, lse, _default_scale(d, scale), slots)
+    else:
+        _launch_dense(q, k, v, out, lse, _default_scale(d, scale))
     return (out, lse) if return_lse else out
 
 
@@ -142,6 +153,27 @@ def _launch_dense(q, k, v, out, lse, scale: float):
     with torch.cuda.device(q.device):
         st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
                           _stream_handle(q.device))
+    _raise_for(lib, st)
+
+
+def splitkv_workspace_bytes(B: int, H: int, N: int, slots: int = 0, device=None) -> int:
+    """Workspace of attn_fwd_splitkv (0: nothing is split). slots <= 0 queries the device."""
+    lib = load_library()
+    if slots <= 0:
+        with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+            return int(lib.attn_fwd_splitkv_workspace_bytes(B, H, N, 128, slots))
+    return int(lib.attn_fwd_splitkv_workspace_bytes(B, H, N, 128, slots))
+
+
+def _launch_dense_splitkv(q, k, v, out, lse, scale: float, slots: int = 0):
+    """One attn_fwd_splitkv call on already-checked tensors, with a cached workspace."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    with torch.cuda.device(q.device):
+        nbytes = int(lib.attn_fwd_splitkv_workspace_bytes(B, H, N, d, slots))
+        ws = _workspace(q.device, nbytes) if nbytes > 0 else None
+        st = lib.attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale, slots,
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream_handle(q.device))
     _raise_for(lib, st)
 
 

@@ -82,6 +82,45 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                                               static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int slots) {
+    if (B <= 0 || H <= 0 || N <= 0 || d != 128 || slots > ATTN_MAX_SLOTS) return 0;
+    if (product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1) < 0) return 0;
+    if (slots <= 0) slots = attn_impl::concurrent_workgroups();
+    return attn_impl::split_plan(B, H, N, slots).workspace_bytes;
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                     int N, int d, float scale, int slots, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    g_last_error[0] = '\0';
+    int st = check_common(q, k, v, out, H, d, scale);
+    if (st != ATTN_OK) return st;
+    if (B <= 0 || N <= 0) return fail(ATTN_ERR_INVALID_ARG, "B and N must be >= 1");
+    if (slots > ATTN_MAX_SLOTS) return fail(ATTN_ERR_INVALID_ARG, "slots exceeds ATTN_MAX_SLOTS");
+    const long long elems = product(B, H, N, d);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const long long tiles = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
+    if (tiles < 0 || tiles + ATTN_MAX_SLOTS > INT_MAX / 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    st = check_aliasing(q, k, v, out, lse, (size_t)elems * 2, (size_t)product(B, H, N, 1) * 4);
+    if (st != ATTN_OK) return st;
+    if (slots <= 0) slots = attn_impl::concurrent_workgroups();
+    const attn_impl::SplitPlan plan = attn_impl::split_plan(B, H, N, slots);
+    if (plan.G > 0) {
+        if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+            return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_fwd_splitkv_workspace_bytes()");
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+            return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        const size_t need = plan.workspace_bytes;
+        if (overlaps(workspace, need, out, (size_t)elems * 2) || overlaps(workspace, need, q, (size_t)elems * 2) ||
+            overlaps(workspace, need, k, (size_t)elems * 2) || overlaps(workspace, need, v, (size_t)elems * 2) ||
+            overlaps(workspace, need, lse, (size_t)product(B, H, N, 1) * 4))
+            return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor argument");
+    }
+    return hip_status(attn_impl::launch_dense_split(q, k, v, out, lse, B, H, N, scale, plan, workspace,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
     if (nseg <= 0 || H <= 0 || total_tokens < 0) return 0;
     return attn_impl::varlen_workspace_bytes(nseg, total_tokens);

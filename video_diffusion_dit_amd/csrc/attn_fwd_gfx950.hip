@@ -51,6 +51,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "attn_launch.h"
 
 namespace {
@@ -338,20 +340,28 @@ __device__ __forceinline__ void full_step(char* smem, const Lane& L, const bf16*
     tile_step<false>(smem + STAGE * STAGE_BYTES, L, qf, oacc, mref, lsum, c, BN, young);
 }
 
+// Row stride (floats) of a partial result: 128 unnormalised O values, then m_ref and l.
+constexpr int PART_STRIDE = 132;
+constexpr size_t PART_BYTES = sizeof(float) * PART_STRIDE * BM;   // one workgroup's rows
+
 // One workgroup: query rows q0 .. q0+BM-1 of a sequence of n tokens whose rows are rs
-// elements apart (Q/K/V/O point at the sequence's first row; LSE at its first entry).
-__device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                                           const bf16* __restrict__ V, bf16* __restrict__ O,
-                                           float* __restrict__ LSE, long rs, int n, int q0, float c) {
+// elements apart (Q/K/V/O point at the sequence's first row; LSE at its first entry), over
+// key tiles kt0 .. kt1-1. With part == nullptr the range is all keys and O (and LSE) get the
+// final rows; otherwise the workgroup's unnormalised O, m_ref and l go to part (PART_STRIDE
+// floats per row) for a later merge.
+__device__ __forceinline__ void attn_block_range(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                 const bf16* __restrict__ V, bf16* __restrict__ O,
+                                                 float* __restrict__ LSE, long rs, int n, int q0, float c,
+                                                 int kt0, int kt1, float* __restrict__ part) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
     const int tid = threadIdx.x, w = tid >> 6;
     const long rs_bytes = rs * 2;
     const long seq_bytes = (long)n * rs_bytes;
     Lane L;
     init_lane(L, tid, (int)rs_bytes);
-    const int ntiles = (n + BN - 1) / BN;
-    const int nfull = n / BN;
-    load_tile(L, smem, K, V, rs_bytes, seq_bytes, 0, w);
+    const int ntiles = kt1;
+    const int nfull = min(n / BN, kt1);
+    load_tile(L, smem, K, V, rs_bytes, seq_bytes, kt0, w);
 
     const int qrow = q0 + w * QW + L.m;
     const bool qvalid = qrow < n;
@@ -366,7 +376,8 @@ __device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf1
     for (int b = 0; b < 4; ++b) oacc[b] = f32x16{};
     float mref = -INFINITY, lsum = 0.f;
 
-    int j = 0;
+    // LDS stage of tile j is (j - kt0) & 1: tile kt0 went to stage 0.
+    int j = kt0;
     for (; j + 1 < nfull; j += 2) {
         full_step<0>(smem, L, K, V, rs_bytes, seq_bytes, j, ntiles, w, qf, oacc, mref, lsum, c);
         full_step<1>(smem, L, K, V, rs_bytes, seq_bytes, j + 1, ntiles, w, qf, oacc, mref, lsum, c);
@@ -378,10 +389,28 @@ __device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf1
     if (j < ntiles) {   // ragged last tile, keys >= n masked (and read as zeros)
         wait_vmem();
         __syncthreads();
-        tile_step<true>(smem + (j & 1) * STAGE_BYTES, L, qf, oacc, mref, lsum, c, n - j * BN, false);
+        tile_step<true>(smem + ((j - kt0) & 1) * STAGE_BYTES, L, qf, oacc, mref, lsum, c, n - j * BN, false);
     }
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (part != nullptr) {
+        if (qvalid) {
+            float* prow = part + (long)(qrow - q0) * PART_STRIDE;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float4* d = reinterpret_cast<float4*>(prow + 32 * b + 16 * hh + 8 * L.g);
+                    d[0] = make_float4(oacc[b][8 * hh + 0], oacc[b][8 * hh + 1], oacc[b][8 * hh + 2], oacc[b][8 * hh + 3]);
+                    d[1] = make_float4(oacc[b][8 * hh + 4], oacc[b][8 * hh + 5], oacc[b][8 * hh + 6], oacc[b][8 * hh + 7]);
+                }
+            if (L.g == 0) {
+                prow[128] = mref;
+                prow[129] = ltot;
+            }
+        }
+        return;
+    }
     const float inv = 1.0f / ltot;
     if (qvalid) {
         bf16* orow = O + qrow * rs;
@@ -408,11 +437,99 @@ struct DenseArgs {
     float c;
 };
 
+__device__ __forceinline__ void attn_block(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                           const bf16* __restrict__ V, bf16* __restrict__ O,
+                                           float* __restrict__ LSE, long rs, int n, int q0, float c) {
+    attn_block_range(Q, K, V, O, LSE, rs, n, q0, c, 0, (n + BN - 1) / BN, nullptr);
+}
+
 __global__ __launch_bounds__(NT, NW / 4) void attn_fwd_dense_kernel(DenseArgs a) {
     const int bh = blockIdx.x / a.ntq, qt = blockIdx.x - bh * a.ntq;
     const long base = (long)bh * a.N * D;
     attn_block(a.q + base, a.k + base, a.v + base, a.o + base,
                a.lse ? a.lse + (long)bh * a.N : nullptr, D, a.N, qt * BM, a.c);
+}
+
+// Split-KV launch (see attn_impl::split_plan): the plain kernel takes whole query tiles
+// 0 .. D-1 (D is a whole number of rounds). The last R query tiles are shared by the G
+// workgroups of attn_fwd_dense_split_kernel: each covers an equal contiguous share of the
+// R*ntk (query tile, key tile) pairs, so every workgroup of the last round does the same work. A workgroup's share is at least one query
+// tile long, so a tile is cut at most once per share boundary; a cut tile's pieces write
+// partial results (workspace slot 2g for the first piece of share g, 2g+1 for its last) that
+// merge_kernel combines.
+struct SplitArgs {
+    int D, R, G, ntk;
+    float* part;
+};
+constexpr int SPLIT_MIN_TILES = 16;   // no piece shorter than this many key tiles
+
+__device__ __forceinline__ long share_begin(const SplitArgs& sp, int g) {
+    return (long)g * sp.R * sp.ntk / sp.G;
+}
+
+__global__ __launch_bounds__(NT, NW / 4) void attn_fwd_dense_split_kernel(DenseArgs a, SplitArgs sp) {
+    const int g = blockIdx.x;
+    const long lo = share_begin(sp, g), hi = share_begin(sp, g + 1);
+    const int i0 = (int)(lo / sp.ntk), i1 = (int)((hi - 1) / sp.ntk);
+    for (int i = i0; i <= i1; ++i) {
+        const long t0 = lo > (long)i * sp.ntk ? lo - (long)i * sp.ntk : 0;
+        const long t1 = hi < (long)(i + 1) * sp.ntk ? hi - (long)i * sp.ntk : sp.ntk;
+        const int item = sp.D + i;
+        const int bh = item / a.ntq, qt = item - bh * a.ntq;
+        const long base = (long)bh * a.N * D;
+        float* part = nullptr;
+        if (t0 != 0 || t1 != sp.ntk) part = sp.part + (size_t)(2 * g + (i == i0 ? 0 : 1)) * (PART_BYTES / sizeof(float));
+        if (i != i0) __syncthreads();   // the previous piece's waves are done with LDS
+        attn_block_range(a.q + base, a.k + base, a.v + base, a.o + base,
+                         a.lse ? a.lse + (long)bh * a.N : nullptr, D, a.N, qt * BM, a.c, (int)t0, (int)t1, part);
+    }
+}
+
+// One block per (cut query tile, 16 rows): combines the tile's partial results,
+// O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with M = max_p m_p, LSE = (M + log2 l) ln 2.
+// Thread (row r, 8-dim chunk k) handles O[r, 8k .. 8k+7].
+__global__ __launch_bounds__(256) void merge_kernel(DenseArgs a, SplitArgs sp) {
+    const int i = blockIdx.x >> 4, rblk = blockIdx.x & 15;
+    const long first = (long)i * sp.ntk, last = first + sp.ntk - 1;
+    // shares containing the tile's first and last key tile
+    int g0 = (int)((first * sp.G) / ((long)sp.R * sp.ntk));
+    while (g0 + 1 < sp.G && share_begin(sp, g0 + 1) <= first) ++g0;
+    while (g0 > 0 && share_begin(sp, g0) > first) --g0;
+    int g1 = (int)((last * sp.G) / ((long)sp.R * sp.ntk));
+    while (g1 + 1 < sp.G && share_begin(sp, g1 + 1) <= last) ++g1;
+    while (g1 > 0 && share_begin(sp, g1) > last) --g1;
+    if (g0 == g1) return;   // the tile was computed whole
+
+    const int item = sp.D + i;
+    const int bh = item / a.ntq, qt = item - bh * a.ntq;
+    const int r = rblk * 16 + (threadIdx.x >> 4), k = threadIdx.x & 15;
+    const int row = qt * BM + r;
+    if (row >= a.N) return;
+    // the tile's piece in share g sits in slot 2g when the tile is g's first, else in 2g+1
+    float M = -INFINITY;
+    for (int g = g0; g <= g1; ++g) {
+        const int slot = 2 * g + (share_begin(sp, g) / sp.ntk == i ? 0 : 1);
+        M = fmaxf(M, sp.part[(size_t)slot * (PART_BYTES / sizeof(float)) + (size_t)r * PART_STRIDE + 128]);
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int g = g0; g <= g1; ++g) {
+        const int slot = 2 * g + (share_begin(sp, g) / sp.ntk == i ? 0 : 1);
+        const float* prow = sp.part + (size_t)slot * (PART_BYTES / sizeof(float)) + (size_t)r * PART_STRIDE;
+        const float wgt = exp2_hw(prow[128] - M);
+        l += wgt * prow[129];
+        const float4 x0 = reinterpret_cast<const float4*>(prow + 8 * k)[0];
+        const float4 x1 = reinterpret_cast<const float4*>(prow + 8 * k)[1];
+        acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
+        acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
+    }
+    const float inv = 1.0f / l;
+    bf16x8 ov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv);
+    const long base = (long)bh * a.N * D;
+    *reinterpret_cast<bf16x8*>(a.o + base + (long)row * D + 8 * k) = ov;
+    if (a.lse != nullptr && k == 0) a.lse[(long)bh * a.N + row] = (M + __log2f(l)) * LN2;
 }
 
 // Varlen schedule in the workspace: [0] entry count, then order[nseg] (segment ids, longest
@@ -528,6 +645,71 @@ hipError_t launch_dense(const void* q, const void* k, const void* v, void* out, 
     a.c = log2e_scale(scale);
     const long grid = (long)B * H * a.ntq;
     hipLaunchKernelGGL(attn_fwd_dense_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+SplitPlan split_plan(int B, int H, int N, int slots) {
+    SplitPlan p{};
+    const long ntq = (N + BM - 1) / BM, items = (long)B * H * ntq;
+    const int ntk = (N + BN - 1) / BN;
+    p.items = items;
+    p.D = items;
+    p.ntk = ntk;
+    if (slots < 2 || items <= 0) return p;
+    const long full = items / slots, r = items % slots;
+    if (r == 0 || ntk < SPLIT_MIN_TILES) return p;
+    long R, G;
+    if (full >= 1) {
+        R = slots + r;
+        G = slots;
+    } else {
+        R = items;
+        G = std::min<long>(slots, R * ntk / SPLIT_MIN_TILES);
+        if (G <= R) return p;   // no workgroup would be added
+    }
+    p.D = items - R;
+    p.R = R;
+    p.G = G;
+    p.workspace_bytes = 2 * (size_t)G * PART_BYTES;
+    return p;
+}
+
+int concurrent_workgroups() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;   // one 512-thread workgroup per compute unit (VGPR-bound)
+}
+
+hipError_t launch_dense_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int H, int N, float scale, const SplitPlan& p, void* workspace,
+                              hipStream_t stream) {
+    if (p.G == 0) return launch_dense(q, k, v, out, lse, B, H, N, scale, stream);
+    DenseArgs a;
+    a.q = static_cast<const bf16*>(q);
+    a.k = static_cast<const bf16*>(k);
+    a.v = static_cast<const bf16*>(v);
+    a.o = static_cast<bf16*>(out);
+    a.lse = lse;
+    a.N = N;
+    a.ntq = (N + BM - 1) / BM;
+    a.c = log2e_scale(scale);
+    SplitArgs sp;
+    sp.D = (int)p.D;
+    sp.R = (int)p.R;
+    sp.G = (int)p.G;
+    sp.ntk = p.ntk;
+    sp.part = static_cast<float*>(workspace);
+    hipError_t e;
+    if (p.D > 0) {   // whole tiles: the plain kernel, whose grid index is the tile index
+        hipLaunchKernelGGL(attn_fwd_dense_kernel, dim3((unsigned)p.D), dim3(NT), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(attn_fwd_dense_split_kernel, dim3((unsigned)p.G), dim3(NT), 0, stream, a, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(p.R * 16)), dim3(256), 0, stream, a, sp);
     return hipGetLastError();
 }
 

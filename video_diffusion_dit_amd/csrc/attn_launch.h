@@ -16,6 +16,21 @@ int tile_keys();   // keys per inner K/V tile (BN)
 hipError_t launch_dense(const void* q, const void* k, const void* v, void* out, float* lse,
                         int B, int H, int N, float scale, hipStream_t stream);
 
+// Split-KV plan of a dense launch for `slots` concurrently resident workgroups: the first D
+// query tiles run whole; the last R are shared evenly by G workgroups (G = 0: no split).
+struct SplitPlan {
+    long items, D, R, G;
+    int ntk;
+    size_t workspace_bytes;
+};
+SplitPlan split_plan(int B, int H, int N, int slots);
+// Workgroups the current device runs at once (0 if it cannot be queried).
+int concurrent_workgroups();
+// Dense forward under plan p (workspace >= p.workspace_bytes, 256-byte aligned).
+hipError_t launch_dense_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int B, int H, int N, float scale, const SplitPlan& p, void* workspace,
+                              hipStream_t stream);
+
 // Workspace layout of the varlen schedule (bytes).
 size_t varlen_workspace_bytes(int nseg, int total_tokens);
 
