@@ -1,0 +1,194 @@
+"""CPU checks of the hand-scheduled key loop (csrc/key_loop_gfx950.inc).
+
+The loop is written by csrc/gen_key_loop.py, which inserts the s_waitcnt and s_nop the
+hardware needs. These tests re-derive those requirements with a separate, simpler scan of the
+emitted text, so a mistake in the generator's bookkeeping shows up here:
+  * the committed file is exactly what the generator writes;
+  * every LDS read has landed (lgkmcnt) before an instruction touches its registers;
+  * the MFMA wait states (result read by non-MFMA code, VALU write before an MFMA read) hold
+    along the straight-line code;
+  * only the registers the asm declares are written, and the control flow (labels, branches,
+    barriers) is consistent.
+"""
+import importlib.util
+import os
+import re
+
+import pytest
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "video_diffusion_dit_amd", "csrc")
+
+
+def load_gen():
+    spec = importlib.util.spec_from_file_location("gen_key_loop", os.path.join(CSRC, "gen_key_loop.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    return gen
+
+
+@pytest.fixture(scope="module")
+def gen():
+    return load_gen()
+
+
+@pytest.fixture(scope="module")
+def asm_lines():
+    text = open(os.path.join(CSRC, "key_loop_gfx950.inc")).read()
+    out = []
+    for line in text.splitlines():
+        m = re.match(r'\s*"(.*)\\n"\s*$', line)
+        if m:
+            out.append(m.group(1).replace("\\t", "\t").strip())
+    return out
+
+
+def test_committed_file_is_generated(gen):
+    assert open(gen.OUT).read() == gen.render()
+
+
+def regs(tok):
+    tok = tok.strip(",")
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def parse(line):
+    op, _, rest = line.partition(" ")
+    ops = [t.strip() for t in rest.split(",")] if rest else []
+    return op, ops
+
+
+def ws_of(op, ops):
+    return int(ops[0]) + 1 if op == "s_nop" else 1
+
+
+def is_block_end(op):
+    return op.startswith("s_branch") or op.startswith("s_cbranch") or op == "s_setpc_b64"
+
+
+def lds_violations(asm_lines):
+    """Simulate lgkmcnt in program order (a path that reaches a label with more reads in
+    flight only waits longer, since LDS ops complete in order)."""
+    pending = []   # register sets of LDS ops in flight, oldest first
+    bad = []
+    for line in asm_lines:
+        if line.endswith(":"):
+            continue
+        op, ops = parse(line)
+        if op == "s_waitcnt":
+            m = re.search(r"lgkmcnt\((\d+)\)", line)
+            if m:
+                n = int(m.group(1))
+                pending = pending[len(pending) - n:] if n else []
+            continue
+        touched = set()
+        for t in ops:
+            touched |= regs(t)
+        if any(p & touched for p in pending):
+            bad.append(line)
+        if op.startswith("ds_read") or op.startswith("ds_bpermute"):
+            pending.append(regs(ops[0]))
+    return bad
+
+
+def mfma_violations(asm_lines):
+    """Straight-line check of the wait-state rules that protect MFMA data."""
+    ins = []
+    for line in asm_lines:
+        if line.endswith(":"):
+            ins.append(("<label>", []))
+            continue
+        ins.append(parse(line))
+    bad = []
+    for k, (op, ops) in enumerate(ins):
+        if not op.startswith("v_mfma"):
+            continue
+        dst = regs(ops[0])
+        srcs = regs(ops[1]) | regs(ops[2]) | regs(ops[3])
+        # (1) a VALU write of any source fewer than 2 wait states before
+        ws = 0
+        for j in range(k - 1, max(k - 6, -1), -1):
+            qop, qops = ins[j]
+            if qop == "<label>" or is_block_end(qop):
+                break
+            if qop.startswith("v_") and not qop.startswith("v_mfma") and qops and regs(qops[0]) & srcs and ws < 2:
+                bad.append(("valu->mfma", k, op))
+            ws += ws_of(qop, qops)
+            if ws >= 2:
+                break
+        # (2) a non-MFMA access of the result fewer than 12 wait states after
+        ws = 0
+        for j in range(k + 1, min(k + 30, len(ins))):
+            qop, qops = ins[j]
+            if qop == "<label>" or is_block_end(qop):
+                break
+            if qop.startswith("v_mfma"):
+                if (regs(qops[1]) | regs(qops[2])) & dst and ws < 12:
+                    bad.append(("mfma->mfma A/B", k, qop))
+                ws += 1
+                continue
+            touched = set()
+            for t in qops:
+                touched |= regs(t)
+            if touched & dst and ws < 12:
+                bad.append(("mfma->access", k, qop))
+            ws += ws_of(qop, qops)
+            if ws >= 12:
+                break
+    return bad
+
+
+def test_lds_results_waited(asm_lines):
+    assert lds_violations(asm_lines) == []
+
+
+def test_mfma_wait_states(asm_lines):
+    assert mfma_violations(asm_lines) == []
+
+
+def test_scans_catch_a_missing_wait(asm_lines):
+    """The scans are not vacuous: a dropped LDS wait, an MFMA result read at once and a
+    VALU write just before an MFMA reads it are all reported."""
+    i = next(k for k, l in enumerate(asm_lines) if l.startswith("s_waitcnt lgkmcnt(1)"))
+    assert lds_violations(asm_lines[:i] + asm_lines[i + 1:])
+    j = next(k for k, l in enumerate(asm_lines) if l.startswith("v_mfma_f32_32x32x16_bf16 v[0:15]"))
+    assert mfma_violations(asm_lines[:j + 1] + ["v_add_f32 v0, v0, v0"] + asm_lines[j + 1:])
+    assert mfma_violations(asm_lines[:j] + ["v_mov_b32 v130, 0"] + asm_lines[j:])
+
+
+def test_control_flow_and_registers(gen, asm_lines):
+    labels = {l[:-1] for l in asm_lines if l.endswith(":")}
+    for line in asm_lines:
+        m = re.match(r"s_(c)?branch\w*\s+(\S+)", line)
+        if m:
+            assert m.group(2) in labels, line
+    # one barrier in the set-up and one per tile of the four-tile loop body; none elsewhere
+    assert sum(1 for l in asm_lines if l == "s_barrier") == 5
+    # registers named stay inside what the asm statement declares (v0..v199, a0..a191)
+    for line in asm_lines:
+        _, ops = parse(line)
+        for t in ops:
+            for kind, i in regs(t):
+                assert (kind == "v" and i < gen.NV) or (kind == "a" and i < gen.NA), line
+    # every return address points at a label that follows its call
+    calls = [l for l in asm_lines if l.startswith("s_add_u32 s54")]
+    assert len(calls) == 9 and all(re.search(r"\.Lok\w+_%=-\.Lpc\w+_%=", c) for c in calls)
+
+
+def test_loop_schedule_shape(gen):
+    """Per tile of the loop: 64 MFMAs, 64 exps per lane, one barrier, eight buffer->LDS loads."""
+    lines, _ = gen.generate()
+    start = lines.index(".Lloop_%=:")
+    end = next(i for i in range(start, len(lines)) if lines[i].strip() == "s_branch .Lloop_%=")
+    body = [l.strip() for l in lines[start:end]]
+    assert sum(l.startswith("v_mfma") for l in body) == 4 * 64
+    assert sum(l.startswith("v_exp_f32") for l in body) == 4 * 64
+    assert sum(l == "s_barrier" for l in body) == 4
+    assert sum(l.startswith("buffer_load_dwordx4") for l in body) == 4 * 8
+    nops = sum(int(l.split()[1]) + 1 for l in body if l.startswith("s_nop"))
+    assert nops < 64, nops   # the schedule keeps hazards apart by itself

@@ -33,8 +33,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
+def write_key_loop() -> str:
+    """Regenerate csrc/key_loop_gfx950.inc (the hand-scheduled key loop) from its generator."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("gen_key_loop", os.path.join(CSRC, "gen_key_loop.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    text = gen.render()
+    old = open(gen.OUT).read() if os.path.exists(gen.OUT) else None
+    if text != old:
+        with open(gen.OUT, "w") as f:
+            f.write(text)
+    return gen.OUT
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 into LIB_PATH; always recompiles."""
+    """Regenerate the key loop, then compile every source for gfx950 into LIB_PATH; always
+    recompiles."""
+    write_key_loop()
     os.makedirs(LIB_DIR, exist_ok=True)
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -1,0 +1,621 @@
+#!/usr/bin/env python3
+"""Writes key_loop_gfx950.inc: the key loop of the attention forward kernel for gfx950, as one
+inline-asm block with fixed registers. attn_fwd_gfx950.hip includes the file inside
+attn_rows(); build.py runs this script before every compile, and a CPU test checks that the
+committed file is what this script writes.
+
+Method (online softmax with BF16 probabilities and FP32 accumulation): page "[sglang]
+SANA-Video 2.0 anchor attention ... FP32 upcast" (blog on sglang PR #49219), "lessons" list
+(QK^T, softmax and PV accumulate in FP32 from BF16 inputs) and documentation item (the
+probabilities are rounded to BF16 before the PV product); page "PR #33702 report",
+motivation (online softmax over KV blocks).
+
+One wave per SIMD owns 64 query rows (row blocks rb = 0, 1 of 32 rows) and walks all 64-key
+tiles t of its key range. Per tile:
+    QK(t+1): 32 MFMAs  S^T = K.Q^T into the other S buffer, beside the second softmax half of
+                       tile t (keys 32..63), then the rescale check of tile t
+    PV(t):   32 MFMAs  O^T += V^T.P^T, beside the first softmax half of tile t+1 (keys 0..31);
+                       in its middle the one barrier of the tile, then the loads of tile t+3
+so that about 3.5 VALU instructions issue in the shadow of every MFMA. K and V tiles sit in
+four LDS stages (K at 16 KiB * stage, V at 64 KiB + 16 KiB * stage) and arrive by
+buffer->LDS loads three tiles ahead. Tile t uses stage t%4 and S buffer t%2, so the loop body
+holds four tiles.
+
+Softmax bookkeeping (per row block): m (the reference the probabilities are taken against,
+log2 units of the scaled logit) and l (the lane's partial row sum). The common path computes
+p = exp2(S*c - m) and checks that no lane's tile sum exceeds 2^8; when one does (always on the
+first tile, where m = -inf) the wave calls the exact path, which recomputes S of the tile
+from LDS, moves m to the running row maximum, rescales O and l, and recomputes P.
+
+Register map (per lane):
+    v[0:63], v[64:127]   S buffers: block (rb, kb) at 16*(2*kb + rb); P packed to BF16 in
+                         place (pair j of a block at 8*(j/4) + j%4)
+    v[128:143]           K fragment ring (4 x 4)       v[144:159]   V fragment ring (4 x 4)
+    v160..v175           m, l, half sums, mask limit, -inf, tile sums
+    v176..v199           temporaries (check, exact path)
+    a[0:127]             O^T: block (db, rb) at 16*(2*db + rb)
+    a[128:191]           Q fragments: (rb, s) at 128 + 4*(8*rb + s)
+The block hands O^T back in v[0:127] (same numbering), m and l in operands.
+
+The script tracks the LDS reads in flight (inserting s_waitcnt lgkmcnt) and inserts s_nop
+for the gfx950 wait states that hand-written code must provide itself:
+    VALU write -> MFMA read of the register                            2
+    MFMA (8 passes) write -> non-MFMA access of the register           12
+    MFMA write -> MFMA read as A/B, or as a C that is not its own chain 12
+    MFMA read as C -> VALU write of the register                        12
+    transcendental write -> VALU read                                   1
+    SALU write of M0 -> buffer load to LDS                              1
+"""
+import os
+import sys
+
+# ---------------------------------------------------------------- register map
+S_BASE = (0, 64)
+KR, VR = 128, 144
+M = (160, 161)
+L = (162, 163)
+H1 = ((164, 165), (166, 167))      # first-half partial sums [rb][2]
+H2 = ((168, 169), (170, 171))      # second-half partial sums
+KLIM_R = 172                       # key limit the exact path masks with (1000: no mask)
+NEG_INF = 173
+TS = (174, 175)                    # tile sums
+TMP0 = 176
+NV = 200
+O_BASE, Q_BASE, NA = 0, 128, 192
+SK, SV = 40, 44                    # buffer-resource cursors s[40:43] (K), s[44:47] (V)
+S_T, S_TLAST, S_LIM = 49, 50, 52   # tile counter, last loop tile, 256.0
+S_RA = 54                          # exact-path return address s[54:55]
+S_C1, S_C2 = 56, 58                # check masks
+S_STG = 60                         # K stage offset handed to the exact path
+NS_LO, NS_HI = 40, 61
+
+K_STAGE = 16384
+V_BASE = 65536
+V_STAGE = 16384
+RESCALE_LIMIT_BITS = 0x43800000    # 256.0f
+
+
+def sblk(buf, rb, kb):
+    return S_BASE[buf] + 16 * (2 * kb + rb)
+
+
+def oblk(db, rb):
+    return O_BASE + 16 * (2 * db + rb)
+
+
+def qfrag(rb, s):
+    return Q_BASE + 4 * (8 * rb + s)
+
+
+def vr(lo, n=1):
+    return "v%d" % lo if n == 1 else "v[%d:%d]" % (lo, lo + n - 1)
+
+
+def ar(lo, n=1):
+    return "a%d" % lo if n == 1 else "a[%d:%d]" % (lo, lo + n - 1)
+
+
+def vset(lo, n=1):
+    return {("v", i) for i in range(lo, lo + n)}
+
+
+def aset(lo, n=1):
+    return {("a", i) for i in range(lo, lo + n)}
+
+
+VCC = {("vcc",)}
+
+
+class Ins:
+    __slots__ = ("text", "kind", "rd", "wr", "rdc", "lds", "m0w", "m0r", "ws")
+
+    def __init__(self, text, kind, rd=(), wr=(), rdc=(), lds=False, m0w=False, m0r=False, ws=1):
+        self.text, self.kind = text, kind
+        self.rd, self.wr, self.rdc = set(rd), set(wr), set(rdc)
+        self.lds, self.m0w, self.m0r, self.ws = lds, m0w, m0r, ws
+
+
+def need(prev, cur):
+    """Wait states required between an earlier instruction prev and cur."""
+    r = 0
+    if prev.kind in ("valu", "trans") and cur.kind == "mfma" and prev.wr & (cur.rd | cur.rdc):
+        r = max(r, 2)
+    if prev.kind == "mfma":
+        if cur.kind == "mfma":
+            if prev.wr & cur.rd:
+                r = max(r, 12)
+            if prev.wr & cur.rdc and not (prev.wr == cur.rdc == cur.wr):
+                r = max(r, 12)
+        elif prev.wr & (cur.rd | cur.wr | cur.rdc):
+            r = max(r, 12)
+        if cur.kind in ("valu", "trans", "lds") and prev.rdc & cur.wr:
+            r = max(r, 12)
+    if prev.kind == "trans" and cur.kind in ("valu", "trans") and prev.wr & cur.rd:
+        r = max(r, 1)
+    if prev.m0w and cur.m0r:
+        r = max(r, 1)
+    return r
+
+
+class Emitter:
+    """Appends instructions, inserting s_waitcnt lgkmcnt and s_nop where required. Wait
+    states are counted per incoming path (hists): a label reached from several places
+    carries the history of each."""
+
+    def __init__(self):
+        self.out = []
+        self.hists = [[]]
+        self.pending = []      # register sets written by LDS ops in flight, oldest first
+
+    def fresh(self):
+        self.hists = [[]]
+
+    def state(self):
+        return [list(h) for h in self.hists], list(self.pending)
+
+    def set_state(self, st):
+        self.hists, self.pending = [list(h) for h in st[0]], list(st[1])
+
+    def label(self, name):
+        self.out.append(name + ":")
+
+    def raw(self, text):
+        """An instruction outside the hazard model (branches, barriers, waits)."""
+        self.out.append("\t" + text)
+
+    def _push(self, ins):
+        self.out.append("\t" + ins.text)
+        for h in self.hists:
+            h.append(ins)
+            tot = 0
+            for i in range(len(h) - 1, -1, -1):
+                tot += h[i].ws
+                if tot > 14:
+                    del h[:i]
+                    break
+
+    def nop(self, n):
+        while n > 0:
+            k = min(n, 8)
+            self._push(Ins("s_nop %d" % (k - 1), "nop", ws=k))
+            n -= k
+
+    def wait_lgkm(self, regs):
+        idx = -1
+        for i, p in enumerate(self.pending):
+            if p & regs:
+                idx = i
+        if idx < 0:
+            return
+        after = min(len(self.pending) - 1 - idx, 15)
+        self._push(Ins("s_waitcnt lgkmcnt(%d)" % after, "waitcnt"))
+        self.pending = self.pending[len(self.pending) - after:] if after else []
+
+    def emit(self, ins):
+        self.wait_lgkm(ins.rd | ins.rdc | ins.wr)
+        req = 0
+        for hist in self.hists:
+            dist = 0
+            for p in reversed(hist):
+                r = need(p, ins)
+                if r > dist:
+                    req = max(req, r - dist)
+                dist += p.ws
+                if dist >= 12:
+                    break
+        if req:
+            self.nop(req)
+        self._push(ins)
+        if ins.lds:
+            self.pending.append(set(ins.wr))
+
+    def valu(self, text, rd=(), wr=()):
+        self.emit(Ins(text, "valu", rd, wr))
+
+    def trans(self, text, rd=(), wr=()):
+        self.emit(Ins(text, "trans", rd, wr))
+
+    def salu(self, text, m0w=False):
+        self.emit(Ins(text, "salu", m0w=m0w))
+
+
+# ---------------------------------------------------------------- building blocks
+def mfma_qk(E, buf, rb, kb, s, kslot):
+    """S^T block (rb, kb) += K fragment (kb, s) . Q fragment (rb, s)."""
+    d = sblk(buf, rb, kb)
+    src_c = "0" if s == 0 else vr(d, 16)
+    E.emit(Ins("v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (vr(d, 16), vr(KR + 4 * kslot, 4), ar(qfrag(rb, s), 4), src_c),
+               "mfma", rd=vset(KR + 4 * kslot, 4) | aset(qfrag(rb, s), 4), wr=vset(d, 16),
+               rdc=(vset(d, 16) if s else ())))
+
+
+def mfma_pv(E, buf, db, rb, h, vslot):
+    """O^T block (db, rb) += V^T fragment (db, key step h) . P fragment (rb, h)."""
+    o = oblk(db, rb)
+    p = sblk(buf, rb, h >> 1) + 8 * (h & 1)
+    E.emit(Ins("v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (ar(o, 16), vr(VR + 4 * vslot, 4), vr(p, 4), ar(o, 16)),
+               "mfma", rd=vset(VR + 4 * vslot, 4) | vset(p, 4), wr=aset(o, 16), rdc=aset(o, 16)))
+
+
+def read_k(E, slot, s, kb, stage, base_reg=None):
+    """K fragment (kb, d-step s) of a stage into ring slot. Addresses: the ka operands (stage
+    0) plus an immediate, or per-call registers base_reg+s (exact path)."""
+    if base_reg is None:
+        addr, off, rd = "%%[ka%d]" % s, K_STAGE * stage + 8192 * kb, ()
+    else:
+        addr, off, rd = vr(base_reg + s), 8192 * kb, vset(base_reg + s)
+    E.emit(Ins("ds_read_b128 %s, %s offset:%d" % (vr(KR + 4 * slot, 4), addr, off), "lds",
+               rd=rd, wr=vset(KR + 4 * slot, 4), lds=True))
+
+
+def read_v(E, slot, db, h, stage):
+    """V^T fragment (dim block db, key step h): two transposing reads."""
+    off = V_STAGE * stage + 4096 * h
+    for t in range(2):
+        E.emit(Ins("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (vr(VR + 4 * slot + 2 * t, 2), 2 * db + t, off), "lds",
+                   wr=vset(VR + 4 * slot + 2 * t, 2), lds=True))
+
+
+def key_const(kb, r):
+    """Key (within the tile) of S register r of block kb, less the lane's 8*g."""
+    return 32 * kb + 16 * (r >> 3) + (r & 7)
+
+
+def softmax_half(buf, kb, masked, klim, hs):
+    """VALU stream for p = exp2(S*c - m) over blocks (0, kb) and (1, kb) of S buffer buf,
+    accumulating the partial sums hs[rb] and packing P to BF16 in place. masked: keys at or
+    past the limit klim = (operand text, registers read) give p = 0."""
+    def group(rb, j):
+        base = sblk(buf, rb, kb)
+        a, b = base + 2 * j, base + 2 * j + 1
+        m = M[rb]
+        st1 = [lambda E, x=x: E.valu("v_fma_f32 %s, %s, %%[c], -%s" % (vr(x), vr(x), vr(m)), rd=vset(x) | vset(m), wr=vset(x))
+               for x in (a, b)]
+        st2 = [lambda E, x=x: E.trans("v_exp_f32 %s, %s" % (vr(x), vr(x)), rd=vset(x), wr=vset(x)) for x in (a, b)]
+        if masked:
+            for x, r in ((a, 2 * j), (b, 2 * j + 1)):
+                st2.append(lambda E, x=x, kc=key_const(kb, r): (
+                    E.valu("v_cmp_lt_i32 vcc, %d, %s" % (kc, klim[0]), rd=klim[1], wr=VCC),
+                    E.valu("v_cndmask_b32 %s, 0, %s, vcc" % (vr(x), vr(x)), rd=vset(x) | VCC, wr=vset(x))))
+        h0, h1 = hs[rb]
+        if j == 0:
+            st3 = [lambda E: E.valu("v_mov_b32 %s, %s" % (vr(h0), vr(a)), rd=vset(a), wr=vset(h0)),
+                   lambda E: E.valu("v_mov_b32 %s, %s" % (vr(h1), vr(b)), rd=vset(b), wr=vset(h1))]
+        else:
+            st3 = [lambda E: E.valu("v_add_f32 %s, %s, %s" % (vr(h0), vr(h0), vr(a)), rd=vset(h0) | vset(a), wr=vset(h0)),
+                   lambda E: E.valu("v_add_f32 %s, %s, %s" % (vr(h1), vr(h1), vr(b)), rd=vset(h1) | vset(b), wr=vset(h1))]
+        dst = base + 8 * (j // 4) + (j % 4)
+        st3.append(lambda E: E.valu("v_cvt_pk_bf16_f32 %s, %s, %s" % (vr(dst), vr(a), vr(b)), rd=vset(a) | vset(b), wr=vset(dst)))
+        return [st1, st2, st3]
+
+    staged = [group(rb, j) for j in range(8) for rb in range(2)]
+    stream = []   # stage s of group g issues at step g + s
+    for step in range(len(staged) + 2):
+        for s in range(3):
+            g = step - s
+            if 0 <= g < len(staged):
+                stream.extend(staged[g][s])
+    return stream
+
+
+def check_ops():
+    """Tile sums per row block (into TS) and the rescale condition (into S_C1/S_C2)."""
+    t0, t1 = TMP0, TMP0 + 1
+
+    def add(d, x, y):
+        return lambda E: E.valu("v_add_f32 %s, %s, %s" % (vr(d), vr(x), vr(y)), rd=vset(x) | vset(y), wr=vset(d))
+    ops = [add(TS[0], *H1[0]), add(TS[1], *H1[1]), add(t0, *H2[0]), add(t1, *H2[1]),
+           add(TS[0], TS[0], t0), add(TS[1], TS[1], t1)]
+    for rb, sc in ((0, S_C1), (1, S_C2)):
+        ops.append(lambda E, rb=rb, sc=sc: E.valu("v_cmp_nge_f32_e64 s[%d:%d], s%d, %s" % (sc, sc + 1, S_LIM, vr(TS[rb])),
+                                                  rd=vset(TS[rb])))
+    return ops
+
+
+def distribute(E, mfmas, valu, extra=None, valu_slots=None):
+    """Issue the MFMAs in order; after MFMA i, whatever extra[i] holds, then an even share of
+    the VALU stream (spread over the first valu_slots MFMAs)."""
+    n = len(mfmas)
+    vs = n if valu_slots is None else valu_slots
+    pos = 0
+    for i in range(n):
+        mfmas[i](E)
+        for f in (extra or {}).get(i, []):
+            f(E)
+        if i < vs:
+            k = (len(valu) - pos + (vs - i) - 1) // (vs - i)
+            for f in valu[pos:pos + k]:
+                f(E)
+            pos += k
+    for f in valu[pos:]:
+        f(E)
+
+
+def qk_phase(E, buf, stage, valu, valu_slots=None, extra=None):
+    """S^T of a tile (K from stage) into S buffer buf; K fragments 0 and 1 are read before."""
+    mf = []
+    ex = {i: list(v) for i, v in (extra or {}).items()}
+    for f in range(16):
+        kb, s = f >> 3, f & 7
+        for rb in range(2):
+            mf.append(lambda E, rb=rb, kb=kb, s=s, f=f: mfma_qk(E, buf, rb, kb, s, f & 3))
+        if f + 2 < 16:
+            g = f + 2
+            ex.setdefault(2 * f + 1, []).insert(0, lambda E, g=g: read_k(E, g & 3, g & 7, g >> 3, stage))
+    distribute(E, mf, valu, ex, valu_slots)
+
+
+def pv_phase(E, buf, stage, valu, valu_slots=None, extra=None):
+    """O^T += V^T P^T for the tile whose P is in S buffer buf (V from stage); V fragments 0
+    and 1 are read before."""
+    mf = []
+    ex = {i: list(v) for i, v in (extra or {}).items()}
+    for v in range(16):
+        h, db = v >> 2, v & 3
+        for rb in range(2):
+            mf.append(lambda E, db=db, rb=rb, h=h, v=v: mfma_pv(E, buf, db, rb, h, v & 3))
+        if v + 2 < 16:
+            g = v + 2
+            ex.setdefault(2 * v + 1, []).insert(0, lambda E, g=g: read_v(E, g & 3, g & 3, g >> 2, stage))
+    distribute(E, mf, valu, ex, valu_slots)
+
+
+def prefetch_k(E, stage):
+    for g in range(2):
+        read_k(E, g, g, 0, stage)
+
+
+def prefetch_v(E, stage):
+    for g in range(2):
+        read_v(E, g, g, 0, stage)
+
+
+def tile_loads(stage):
+    """Buffer->LDS loads of one tile (this wave's quarter of K and of V) into a stage; then
+    both resource cursors move one tile on (records clamped at zero, so loads past the
+    sequence end read zeros)."""
+    ops = []
+    for i in range(4):
+        for base, cur, name in ((K_STAGE * stage, SK, "ko"), (V_BASE + V_STAGE * stage, SV, "vo")):
+            ops.append(lambda E, i=i, base=base, cur=cur, name=name: (
+                E.salu("s_add_u32 m0, %%[ldsw], %d" % (base + 1024 * i), m0w=True),
+                E.emit(Ins("buffer_load_dwordx4 %%[%s%d], s[%d:%d], 0 offen lds" % (name, i, cur, cur + 3), "vmem", m0r=True))))
+
+    def advance(E):
+        for cur in (SK, SV):
+            E.salu("s_add_u32 s%d, s%d, %%[tb]" % (cur, cur))
+            E.salu("s_addc_u32 s%d, s%d, 0" % (cur + 1, cur + 1))
+            E.salu("s_sub_i32 s%d, s%d, %%[tb]" % (cur + 2, cur + 2))
+            E.salu("s_max_i32 s%d, s%d, 0" % (cur + 2, cur + 2))
+    ops.append(advance)
+    return ops
+
+
+def rare_call(E, X, stage, uid):
+    """If the check failed (either mask set), call the exact path of S buffer X with the K
+    stage of the tile; it returns to the instruction after the call."""
+    E.salu("s_or_b64 s[%d:%d], s[%d:%d], s[%d:%d]" % (S_C1, S_C1 + 1, S_C1, S_C1 + 1, S_C2, S_C2 + 1))
+    E.raw("s_cbranch_scc0 .Lok%s_%%=" % uid)
+    E.raw("s_mov_b32 s%d, %d" % (S_STG, K_STAGE * stage))
+    E.raw("s_getpc_b64 s[%d:%d]" % (S_RA, S_RA + 1))
+    E.label(".Lpc%s_%%=" % uid)
+    E.raw("s_add_u32 s%d, s%d, .Lok%s_%%=-.Lpc%s_%%=" % (S_RA, S_RA, uid, uid))
+    E.raw("s_addc_u32 s%d, s%d, 0" % (S_RA + 1, S_RA + 1))
+    E.raw("s_branch .Lrare%d_%%=" % X)
+    E.label(".Lok%s_%%=" % uid)
+
+
+def add_l(E):
+    for rb in range(2):
+        E.valu("v_add_f32 %s, %s, %s" % (vr(L[rb]), vr(L[rb]), vr(TS[rb])), rd=vset(L[rb]) | vset(TS[rb]), wr=vset(L[rb]))
+
+
+KLIM_IN = ("%[klim]", set())
+KLIM_EXACT = (vr(KLIM_R), vset(KLIM_R))
+
+
+def rare_path(E, X):
+    """Exact path for the tile in S buffer X whose K sits at LDS offset s[S_STG] (+ the ka
+    operands): recompute S, take the row maximum (masked keys excluded), rescale O and l,
+    recompute P and the tile sums. Entered and left with all wait states satisfied."""
+    E.label(".Lrare%d_%%=" % X)
+    E.fresh()
+    E.nop(12)
+    E.raw("s_waitcnt lgkmcnt(0)")
+    E.pending = []
+    ka = TMP0 + 2
+    for s in range(8):
+        E.valu("v_add_u32 %s, s%d, %%[ka%d]" % (vr(ka + s), S_STG, s), wr=vset(ka + s))
+    for g in range(2):
+        read_k(E, g, g, 0, 0, base_reg=ka)
+    for f in range(16):
+        kb, s = f >> 3, f & 7
+        for rb in range(2):
+            mfma_qk(E, X, rb, kb, s, f & 3)
+        if f + 2 < 16:
+            g = f + 2
+            read_k(E, g & 3, g & 7, g >> 3, 0, base_reg=ka)
+    tm, tm2 = (TMP0 + 10, TMP0 + 11), (TMP0 + 12, TMP0 + 13)
+    tt = TMP0 + 14
+    for rb in range(2):
+        first = [True, True]
+        for kb in range(2):
+            for r in range(16):
+                x = sblk(X, rb, kb) + r
+                acc = (tm, tm2)[r & 1][rb]
+                E.valu("v_mul_f32 %s, %%[c], %s" % (vr(tt), vr(x)), rd=vset(x), wr=vset(tt))
+                E.valu("v_cmp_lt_i32 vcc, %d, %s" % (key_const(kb, r), vr(KLIM_R)), rd=vset(KLIM_R), wr=VCC)
+                E.valu("v_cndmask_b32 %s, %s, %s, vcc" % (vr(tt), vr(NEG_INF), vr(tt)), rd=vset(tt) | vset(NEG_INF) | VCC, wr=vset(tt))
+                if first[r & 1]:
+                    E.valu("v_mov_b32 %s, %s" % (vr(acc), vr(tt)), rd=vset(tt), wr=vset(acc))
+                    first[r & 1] = False
+                else:
+                    E.valu("v_max_f32 %s, %s, %s" % (vr(acc), vr(acc), vr(tt)), rd=vset(acc) | vset(tt), wr=vset(acc))
+        E.valu("v_max_f32 %s, %s, %s" % (vr(tm[rb]), vr(tm[rb]), vr(tm2[rb])), rd=vset(tm[rb]) | vset(tm2[rb]), wr=vset(tm[rb]))
+    for rb in range(2):   # the partner lane (l ^ 32) holds the other keys of each row
+        E.emit(Ins("ds_bpermute_b32 %s, %%[bperm], %s" % (vr(tm2[rb]), vr(tm[rb])), "lds", rd=vset(tm[rb]), wr=vset(tm2[rb]), lds=True))
+    alpha = (TMP0 + 15, TMP0 + 16)
+    for rb in range(2):
+        E.valu("v_max_f32 %s, %s, %s" % (vr(tm[rb]), vr(tm[rb]), vr(tm2[rb])), rd=vset(tm[rb]) | vset(tm2[rb]), wr=vset(tm[rb]))
+        E.valu("v_max_f32 %s, %s, %s" % (vr(tm[rb]), vr(tm[rb]), vr(M[rb])), rd=vset(tm[rb]) | vset(M[rb]), wr=vset(tm[rb]))
+        E.valu("v_sub_f32 %s, %s, %s" % (vr(alpha[rb]), vr(M[rb]), vr(tm[rb])), rd=vset(M[rb]) | vset(tm[rb]), wr=vset(alpha[rb]))
+        E.trans("v_exp_f32 %s, %s" % (vr(alpha[rb]), vr(alpha[rb])), rd=vset(alpha[rb]), wr=vset(alpha[rb]))
+        E.valu("v_mov_b32 %s, %s" % (vr(M[rb]), vr(tm[rb])), rd=vset(tm[rb]), wr=vset(M[rb]))
+    for rb in range(2):
+        E.valu("v_mul_f32 %s, %s, %s" % (vr(L[rb]), vr(L[rb]), vr(alpha[rb])), rd=vset(L[rb]) | vset(alpha[rb]), wr=vset(L[rb]))
+    tmps = [TMP0 + 17 + i for i in range(7)]
+    k = 0
+    for rb in range(2):
+        for db in range(4):
+            for r in range(16):
+                a, t = oblk(db, rb) + r, tmps[k % 7]
+                k += 1
+                E.valu("v_accvgpr_read_b32 %s, %s" % (vr(t), ar(a)), rd=aset(a), wr=vset(t))
+                E.valu("v_mul_f32 %s, %s, %s" % (vr(t), vr(t), vr(alpha[rb])), rd=vset(t) | vset(alpha[rb]), wr=vset(t))
+                E.valu("v_accvgpr_write_b32 %s, %s" % (ar(a), vr(t)), rd=vset(t), wr=aset(a))
+    for f in softmax_half(X, 0, True, KLIM_EXACT, H1) + softmax_half(X, 1, True, KLIM_EXACT, H2) + check_ops()[:6]:
+        f(E)
+    E.fresh()
+    E.nop(12)
+    E.raw("s_setpc_b64 s[%d:%d]" % (S_RA, S_RA + 1))
+
+
+def final_phase(E, Y, stage, uid):
+    """The last tile (S buffer Y, LDS stage): masked second softmax half, check, PV."""
+    for f in softmax_half(Y, 1, True, KLIM_IN, H2):
+        f(E)
+    prefetch_v(E, stage)
+    for f in check_ops():
+        f(E)
+    rare_call(E, Y, stage, uid)
+    add_l(E)
+    pv_phase(E, Y, stage, [])
+    E.raw("s_branch .Ldone_%=")
+
+
+def generate(backedge=None):
+    E = Emitter()
+    # ---- set-up: cursors, statistics, Q (to AGPRs), O = 0, tiles 0..2
+    for i in range(4):
+        E.salu("s_mov_b32 s%d, %%[rk%d]" % (SK + i, i))
+        E.salu("s_mov_b32 s%d, %%[rv%d]" % (SV + i, i))
+    E.salu("s_mov_b32 s%d, 0" % S_T)
+    E.salu("s_sub_u32 s%d, %%[T], 2" % S_TLAST)
+    E.salu("s_mov_b32 s%d, 0x%08x" % (S_LIM, RESCALE_LIMIT_BITS))
+    for rb in range(2):
+        E.valu("v_mov_b32 %s, 0xff800000" % vr(M[rb]), wr=vset(M[rb]))
+        E.valu("v_mov_b32 %s, 0" % vr(L[rb]), wr=vset(L[rb]))
+    E.valu("v_mov_b32 %s, 1000" % vr(KLIM_R), wr=vset(KLIM_R))
+    E.valu("v_mov_b32 %s, 0xff800000" % vr(NEG_INF), wr=vset(NEG_INF))
+    for rb in range(2):
+        for s in range(8):
+            E.emit(Ins("global_load_dwordx4 %s, %%[qa%d], off offset:%d" % (ar(qfrag(rb, s), 4), rb, 32 * s), "vmem",
+                       wr=aset(qfrag(rb, s), 4)))
+    for i in range(128):
+        E.valu("v_accvgpr_write_b32 %s, 0" % ar(O_BASE + i), wr=aset(O_BASE + i))
+    for u in range(3):
+        for f in tile_loads(u):
+            f(E)
+    E.raw("s_waitcnt vmcnt(0)")
+    E.raw("s_barrier")
+    prefetch_k(E, 0)
+    qk_phase(E, 0, 0, [])
+    E.raw("s_cmp_eq_u32 %[T], 1")
+    E.raw("s_cbranch_scc1 .LT1_%=")
+    for f in softmax_half(0, 0, False, None, H1):
+        f(E)
+    prefetch_k(E, 1)
+
+    # ---- loop: four tiles per trip; leaves after the QK phase of tile T-2
+    if backedge is not None:
+        E.hists = E.hists + [list(h) for h in backedge]
+    E.label(".Lloop_%=")
+    tail_state = {}
+    for k in range(4):
+        X, Y = k % 2, (k + 1) % 2
+        qk_phase(E, Y, (k + 1) % 4, softmax_half(X, 1, False, None, H2) + check_ops(), valu_slots=30,
+                 extra={31: [lambda E, st=k: prefetch_v(E, st)]})
+        rare_call(E, X, k, "A%d" % k)
+        add_l(E)
+        E.salu("s_cmp_eq_u32 s%d, s%d" % (S_T, S_TLAST))
+        E.raw("s_cbranch_scc1 .Ltail%d_%%=" % k)
+        tail_state[k] = E.state()
+        extra = {15: [lambda E: E.raw("s_waitcnt vmcnt(0)"), lambda E: E.raw("s_barrier")]}
+        for i, f in enumerate(tile_loads((k + 3) % 4)):
+            extra.setdefault(16 + i, []).append(f)
+        extra.setdefault(30, []).append(lambda E, st=(k + 2) % 4: prefetch_k(E, st))
+        pv_phase(E, X, k, softmax_half(Y, 0, False, None, H1), valu_slots=29, extra=extra)
+        E.salu("s_add_u32 s%d, s%d, 1" % (S_T, S_T))
+    loop_end = [list(h) for h in E.hists]
+    E.raw("s_branch .Lloop_%=")
+
+    # ---- tails: PV of tile T-2 beside the masked first half of tile T-1, then tile T-1
+    for k in range(4):
+        X, Y = k % 2, (k + 1) % 2
+        E.label(".Ltail%d_%%=" % k)
+        E.set_state(tail_state[k])
+        E.valu("v_mov_b32 %s, %%[klim]" % vr(KLIM_R), wr=vset(KLIM_R))
+        pv_phase(E, X, k, softmax_half(Y, 0, True, KLIM_IN, H1))
+        final_phase(E, Y, (k + 1) % 4, "F%d" % k)
+
+    # ---- a range of one tile
+    E.label(".LT1_%=")
+    E.fresh()
+    E.nop(12)
+    E.valu("v_mov_b32 %s, %%[klim]" % vr(KLIM_R), wr=vset(KLIM_R))
+    for f in softmax_half(0, 0, True, KLIM_IN, H1):
+        f(E)
+    final_phase(E, 0, 0, "S")
+
+    for X in range(2):
+        rare_path(E, X)
+
+    E.label(".Ldone_%=")
+    E.fresh()
+    E.nop(12)
+    E.raw("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    for i in range(128):
+        E.raw("v_accvgpr_read_b32 v%d, a%d" % (i, O_BASE + i))
+    for rb in range(2):
+        E.raw("v_mov_b32 %%[m%d], %s" % (rb, vr(M[rb])))
+        E.raw("v_mov_b32 %%[l%d], %s" % (rb, vr(L[rb])))
+    return E.out, loop_end
+
+
+def render():
+    lines, back = generate()
+    for _ in range(4):   # the loop head is reached from the set-up and from the loop end
+        lines2, back2 = generate(back)
+        if lines2 == lines:
+            break
+        lines, back = lines2, back2
+    else:
+        raise SystemExit("wait-state pass did not converge")
+    clob = ['"v%d"' % i for i in range(128, NV)] + ['"a%d"' % i for i in range(NA)] + \
+           ['"s%d"' % i for i in range(NS_LO, NS_HI + 1)] + ['"vcc"', '"m0"', '"scc"', '"memory"']
+    outs = ['[o%d%d] "=&{v[%d:%d]}"(o[%d][%d])' % (db, rb, oblk(db, rb), oblk(db, rb) + 15, db, rb)
+            for db in range(4) for rb in range(2)]
+    outs += ['[m0] "=v"(mref[0])', '[m1] "=v"(mref[1])', '[l0] "=v"(lsum[0])', '[l1] "=v"(lsum[1])']
+    ins = ['[rk%d] "s"(rk[%d])' % (i, i) for i in range(4)] + ['[rv%d] "s"(rv[%d])' % (i, i) for i in range(4)]
+    ins += ['[ka%d] "v"(ka[%d])' % (i, i) for i in range(8)] + ['[va%d] "v"(va[%d])' % (i, i) for i in range(8)]
+    ins += ['[ko%d] "v"(ko[%d])' % (i, i) for i in range(4)] + ['[vo%d] "v"(vo[%d])' % (i, i) for i in range(4)]
+    ins += ['[qa0] "v"(qa[0])', '[qa1] "v"(qa[1])', '[ldsw] "s"(ldsw)', '[tb] "s"(tb)', '[T] "s"(ntile)',
+            '[c] "s"(c)', '[klim] "v"(klim)', '[bperm] "v"(bperm)']
+    n_ins = sum(1 for l in lines if l.startswith("\t"))
+    n_nop = sum(1 for l in lines if l.strip().startswith("s_nop"))
+    text = ["// Written by gen_key_loop.py (do not edit): the key loop of attn_rows() for gfx950.",
+            "// %d instructions, %d of them s_nop." % (n_ins, n_nop),
+            "asm volatile("]
+    text += ['        "%s\\n"' % l.replace("\\", "\\\\").replace('"', '\\"') for l in lines]
+    text.append("        : " + ",\n          ".join(outs))
+    text.append("        : " + ",\n          ".join(ins))
+    text.append("        : " + ", ".join(clob) + ");")
+    return "\n".join(text) + "\n"
+
+
+OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "key_loop_gfx950.inc")
+
+if __name__ == "__main__":
+    path = sys.argv[1] if len(sys.argv) > 1 else OUT
+    with open(path, "w") as f:
+        f.write(render())
