@@ -74,6 +74,16 @@ V_BASE = 65536
 V_STAGE = 16384
 RESCALE_LIMIT_BITS = 0x43800000    # 256.0f
 
+# Schedule knobs (the values the kernel is built with).
+OPTS = {
+    "k_ahead": 2,        # K fragments read this many fragment pairs ahead of their MFMAs
+    "v_ahead": 2,        # V fragments likewise
+    "qk_valu_slots": 30, # QK phase: the exp work and the check spread over this many MFMAs
+    "pv_valu_slots": 29, # PV phase: the exp work spread over this many MFMAs
+    "barrier_after": 15, # PV phase: barrier and tile loads after this MFMA
+    "limit_bits": RESCALE_LIMIT_BITS,
+}
+
 
 def sblk(buf, rb, kb):
     return S_BASE[buf] + 16 * (2 * kb + rb)
@@ -339,8 +349,8 @@ def qk_phase(E, buf, stage, valu, valu_slots=None, extra=None):
         kb, s = f >> 3, f & 7
         for rb in range(2):
             mf.append(lambda E, rb=rb, kb=kb, s=s, f=f: mfma_qk(E, buf, rb, kb, s, f & 3))
-        if f + 2 < 16:
-            g = f + 2
+        g = f + OPTS["k_ahead"]
+        if g < 16:
             ex.setdefault(2 * f + 1, []).insert(0, lambda E, g=g: read_k(E, g & 3, g & 7, g >> 3, stage))
     distribute(E, mf, valu, ex, valu_slots)
 
@@ -354,19 +364,19 @@ def pv_phase(E, buf, stage, valu, valu_slots=None, extra=None):
         h, db = v >> 2, v & 3
         for rb in range(2):
             mf.append(lambda E, db=db, rb=rb, h=h, v=v: mfma_pv(E, buf, db, rb, h, v & 3))
-        if v + 2 < 16:
-            g = v + 2
+        g = v + OPTS["v_ahead"]
+        if g < 16:
             ex.setdefault(2 * v + 1, []).insert(0, lambda E, g=g: read_v(E, g & 3, g & 3, g >> 2, stage))
     distribute(E, mf, valu, ex, valu_slots)
 
 
 def prefetch_k(E, stage):
-    for g in range(2):
+    for g in range(OPTS["k_ahead"]):
         read_k(E, g, g, 0, stage)
 
 
 def prefetch_v(E, stage):
-    for g in range(2):
+    for g in range(OPTS["v_ahead"]):
         read_v(E, g, g, 0, stage)
 
 
@@ -501,7 +511,7 @@ def generate(backedge=None):
         E.salu("s_mov_b32 s%d, %%[rv%d]" % (SV + i, i))
     E.salu("s_mov_b32 s%d, 0" % S_T)
     E.salu("s_sub_u32 s%d, %%[T], 2" % S_TLAST)
-    E.salu("s_mov_b32 s%d, 0x%08x" % (S_LIM, RESCALE_LIMIT_BITS))
+    E.salu("s_mov_b32 s%d, 0x%08x" % (S_LIM, OPTS["limit_bits"]))
     for rb in range(2):
         E.valu("v_mov_b32 %s, 0xff800000" % vr(M[rb]), wr=vset(M[rb]))
         E.valu("v_mov_b32 %s, 0" % vr(L[rb]), wr=vset(L[rb]))
@@ -533,18 +543,19 @@ def generate(backedge=None):
     tail_state = {}
     for k in range(4):
         X, Y = k % 2, (k + 1) % 2
-        qk_phase(E, Y, (k + 1) % 4, softmax_half(X, 1, False, None, H2) + check_ops(), valu_slots=30,
+        qk_phase(E, Y, (k + 1) % 4, softmax_half(X, 1, False, None, H2) + check_ops(), valu_slots=OPTS["qk_valu_slots"],
                  extra={31: [lambda E, st=k: prefetch_v(E, st)]})
         rare_call(E, X, k, "A%d" % k)
         add_l(E)
         E.salu("s_cmp_eq_u32 s%d, s%d" % (S_T, S_TLAST))
         E.raw("s_cbranch_scc1 .Ltail%d_%%=" % k)
         tail_state[k] = E.state()
-        extra = {15: [lambda E: E.raw("s_waitcnt vmcnt(0)"), lambda E: E.raw("s_barrier")]}
+        bar = OPTS["barrier_after"]
+        extra = {bar: [lambda E: E.raw("s_waitcnt vmcnt(0)"), lambda E: E.raw("s_barrier")]}
         for i, f in enumerate(tile_loads((k + 3) % 4)):
-            extra.setdefault(16 + i, []).append(f)
+            extra.setdefault(bar + 1 + i, []).append(f)
         extra.setdefault(30, []).append(lambda E, st=(k + 2) % 4: prefetch_k(E, st))
-        pv_phase(E, X, k, softmax_half(Y, 0, False, None, H1), valu_slots=29, extra=extra)
+        pv_phase(E, X, k, softmax_half(Y, 0, False, None, H1), valu_slots=OPTS["pv_valu_slots"], extra=extra)
         E.salu("s_add_u32 s%d, s%d, 1" % (S_T, S_T))
     loop_end = [list(h) for h in E.hists]
     E.raw("s_branch .Lloop_%=")
@@ -616,6 +627,11 @@ def render():
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "key_loop_gfx950.inc")
 
 if __name__ == "__main__":
+    # gen_key_loop.py [out.inc [knob=value ...]]: the knobs select schedule variants
     path = sys.argv[1] if len(sys.argv) > 1 else OUT
+    for kv in sys.argv[2:]:
+        k, v = kv.split("=")
+        assert k in OPTS, k
+        OPTS[k] = int(v, 0)
     with open(path, "w") as f:
         f.write(render())
