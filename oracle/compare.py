@@ -41,3 +41,38 @@ def compare(o, o_ref, lse=None, lse_ref=None) -> dict:
     out["ok"] = bool(out["finite"] and out["rel_l2"] <= REL_L2_TOL and out["max_abs"] <= MAX_ABS_TOL
                      and out.get("lse_max_abs", 0.0) <= LSE_TOL)
     return out
+
+
+def bf16_round_f64(y) -> np.ndarray:
+    """The bfloat16 number nearest to each float64 value (ties to even), as float64.
+
+    bfloat16 keeps 8 significant bits: with y = m * 2^e and 0.5 <= |m| < 1, the nearest
+    bfloat16 is rint(m * 2^8) * 2^(e - 8) (numpy's rint breaks ties to even)."""
+    m, e = np.frexp(np.asarray(y, dtype=np.float64))
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def bf16_spacing(y) -> np.ndarray:
+    """Distance between consecutive bfloat16 numbers around |y| (normal range)."""
+    _, e = np.frexp(np.asarray(y, dtype=np.float64))
+    return np.ldexp(1.0, e - 8)
+
+
+def bf16_faithful(got, exact, abs_floor: float = 2.0 ** -18) -> dict:
+    """A BF16 result against exact values. 'ok' when every element is within one bfloat16
+    spacing of the exact value, or within abs_floor of it (values that come out of a
+    cancellation in FP32 carry an absolute error of a few FP32 ulps of the operands, which
+    is far more than a bfloat16 spacing of the tiny result). 'rne_frac' is the fraction of
+    elements equal to the nearest-even rounding of the exact value."""
+    got = np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    assert got.shape == exact.shape, (got.shape, exact.shape)
+    err = np.abs(got - exact)
+    lim = np.maximum(bf16_spacing(exact), abs_floor)
+    return {
+        "max_err_over_limit": float(np.max(err / lim)) if err.size else 0.0,
+        "rne_frac": float(np.mean(got == bf16_round_f64(exact))) if err.size else 1.0,
+        "finite": bool(np.all(np.isfinite(got))),
+        "n_elems": int(got.size),
+        "ok": bool(np.all(np.isfinite(got)) and np.all(err <= lim)),
+    }
