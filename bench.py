@@ -29,25 +29,41 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X published dense BF16 MFMA peak
 METRIC = "attention TFLOP/s (4·B·H·N²·d) and % of BF16 MFMA peak, 720p-like N"
-KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_dit_amd", "csrc", "attn_fwd_gfx950.hip")
+PEAK_HBM_GBS = 8000.0              # MI355X published HBM3E bandwidth
+CSRC = os.path.join(ROOT, "video_diffusion_dit_amd", "csrc")
+# sources whose hash a traffic record must match, per kind of call
+KERNEL_SOURCES = {
+    "dense": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
+    "varlen": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
+    "prologue": ("prologue_gfx950.hip",),
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_hash(kind: str = "dense") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-# Kernels one call of the hot path dispatches (the first is the dominant one).
+# Kernels one call dispatches (the first is the dominant one).
 CALL_KERNELS = {
     "dense": ("attn_fwd_dense_kernel", "attn_fwd_dense_split_kernel", "merge_kernel"),
     "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule"),
+    "prologue": ("qk_prologue_kernel",),
 }
 
 
-def measured_traffic(workload: str, kernel: str, split_kv: bool):
+def prologue_bytes(B: int, N: int, H: int, d: int = 128) -> float:
+    """Algorithmic HBM bytes of one prologue call: Q, K, V rows read once and written once."""
+    return float(B) * N * H * d * 2 * 6
+
+
+def measured_traffic(workload: str, kernel: str, split_kv: bool, kind: str = "dense"):
     """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source with the same split-KV setting; else None."""
+    the current kernel sources with the same split-KV setting; else None."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -56,7 +72,7 @@ def measured_traffic(workload: str, kernel: str, split_kv: bool):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(kind):
         return None
     if fields.get("split_kv", "false") != ("true" if split_kv else "false"):
         return None
@@ -83,7 +99,7 @@ def write_traffic_profile(args) -> int:
     """Scale FETCH_SIZE/WRITE_SIZE of one call's kernels by what the same counters read for a
     copy of known size, and record the result with the kernel-source hash."""
     fetch_csv, write_csv = args.write_traffic_profile
-    kind = "varlen" if "varlen" in args.workload else "dense"
+    kind = args.traffic_kind or ("varlen" if "varlen" in args.workload else "dense")
     names = CALL_KERNELS[kind]
     kernel = names[0]
     copy_bytes = float(args.calibrate_copy_mib << 20)
@@ -112,7 +128,10 @@ def write_traffic_profile(args) -> int:
     from workloads import WORKLOADS
     w = WORKLOADS[args.workload]
     tokens = w.B * w.N if w.kind == "dense" else w.total_tokens
-    algorithmic = tokens * w.H * (8.0 * w.d + 4.0)
+    if kind == "prologue":
+        algorithmic = prologue_bytes(w.B, w.N, w.H, w.d)
+    else:
+        algorithmic = tokens * w.H * (8.0 * w.d + 4.0)
     path = os.path.join(PROFILES, f"{kernel}_{args.workload}_hbm_traffic.txt")
     with open(path, "w") as f:
         f.write(f"# HBM traffic of one call ({', '.join(n for n in names)} as dispatched) on the "
@@ -121,7 +140,7 @@ def write_traffic_profile(args) -> int:
         for line in (args.profile_command or "").split(";"):
             if line.strip():
                 f.write(f"# command: {line.strip()}\n")
-        f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash(kind)}\n")
         f.write(f"copy_kernel: {copy_key}\n")
         f.write(f"copy_bytes: {copy_bytes:.0f}\n")
         f.write(f"copy_fetch_kib_per_dispatch: {f_copy / 1024.0:.1f}\n")
@@ -141,6 +160,63 @@ def write_traffic_profile(args) -> int:
         f.write(f"traffic_over_algorithmic: {(fetch_b + write_b) / algorithmic:.3f}\n")
     print(open(path).read())
     return 0
+
+
+def time_prologue(args, w, vd, dev) -> dict:
+    """Time the Q/K RMSNorm + 3-D RoPE prologue (with V re-laid) at the workload's token grid,
+    on seeded projected inputs resident in HBM; check seeded tokens against the oracle."""
+    import numpy as np
+    import torch
+
+    from workloads import make_projected
+    t0 = time.time()
+    xb = make_projected(w.B, w.grid, w.H, seed=0)
+    xs = [dev(b) for b in xb]
+    outs = tuple(torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda:0") for _ in range(3))
+    print(f"[bench] prologue inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def call():
+        vd.qk_prologue(xs[0], xs[1], xs[2], grid=w.grid, out=outs)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.prologue_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.prologue_steps)]
+    torch.cuda.synchronize()
+    for i in range(args.prologue_steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg = float(np.mean(ms))
+    nbytes = prologue_bytes(w.B, w.N, w.H, w.d)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    rec = {
+        "kernel": "qk_prologue_kernel",
+        "what": "per-head RMSNorm + interleaved 3-D RoPE of Q and K, V re-laid, [B,N,H,128] -> [B,H,N,128] BF16",
+        "bound": "hbm",
+        "achieved": round(gbs, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic(w.name, "qk_prologue_kernel", False, "prologue"),
+        "algorithmic_bytes": nbytes,
+        "ms": {"avg": round(avg, 4), "min": round(min(ms), 4), "max": round(max(ms), 4)},
+        "steps": args.prologue_steps,
+    }
+    print(f"[bench] prologue {args.prologue_steps} calls: {avg:.4f} ms -> {gbs:.0f} GB/s "
+          f"({100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f})", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        from oracle import bf16_bits_to_f64, bf16_faithful, qk_norm_rope
+        toks = np.random.default_rng(1).choice(w.N, 256, replace=False)
+        got = outs[0].view(torch.int16).cpu().numpy().view(np.uint16)[:, :, toks]
+        m = bf16_faithful(bf16_bits_to_f64(got), qk_norm_rope(xb[0], w.grid, tokens=toks))
+        rec["parity"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in m.items()}
+    del xs, outs
+    torch.cuda.empty_cache()
+    return rec
 
 
 def host_cores() -> int:
@@ -167,6 +243,10 @@ def main() -> int:
     ap.add_argument("--write-traffic-profile", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
                          "WRITE_SIZE) of a run with --calibrate-copy-mib into the profiles/ record; no GPU")
+    ap.add_argument("--traffic-kind", choices=sorted(CALL_KERNELS), default=None,
+                    help="with --write-traffic-profile: which call's kernels to record (default: the workload's)")
+    ap.add_argument("--prologue-steps", type=int, default=20,
+                    help="timed calls of the Q/K RMSNorm+RoPE prologue at the workload's grid (0: skip)")
     ap.add_argument("--profile-command", default="",
                     help="the command lines that produced the counter files (recorded in the profile)")
     args = ap.parse_args()
@@ -235,14 +315,6 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")   # contents irrelevant: bytes are counted
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     ms_per_step = wall_ms / args.steps
     avg_kernel_ms = float(np.mean(kernel_ms))
     flops = w.flops()
@@ -289,6 +361,17 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+
+    if w.grid is not None and args.prologue_steps > 0:
+        result["prologue"] = time_prologue(args, w, vd, dev)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")   # contents irrelevant: bytes are counted
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu_baseline:
         from oracle import attention_dense, attention_varlen, compare

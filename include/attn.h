@@ -118,6 +118,33 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
 /* Workspace bytes attn_fwd_varlen needs for these sizes (0 if the sizes are invalid). */
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens);
 
+/*
+ * Attention prologue: per-head RMSNorm and interleaved 3-D rotary embedding (RoPE) of the
+ * projected Q and K, rounded to BF16 once and written in the head-major layout attn_fwd
+ * reads; V is only re-laid. Page "PR #35728 report", key source excerpts (sana_video.py
+ * forward: RMSNorm on Q and K, [B, N, H, D] view, interleaved rotary embedding on Q and K
+ * only) and page "[sglang] SANA-Video 2.0 anchor attention ... FP32 upcast", introduction
+ * (Q/K/V reach attention in BF16 after RMSNorm and RoPE). Per token n and head h, in FP32:
+ *   y = x / sqrt(mean(x^2) + eps) * w                     (w = 1 when the weight is NULL)
+ *   pair i (channels 2i, 2i+1) turns by phi = pos_a(n) * theta^(-k/P_a), where the 64 pairs
+ *   split (22, 21, 21) over the axes a = (t, h, w), k is the pair's index within its axis,
+ *   and pos(n) = (n / (grid_h*grid_w), (n / grid_w) % grid_h, n % grid_w):
+ *   (y_2i, y_2i+1) -> (y_2i cos phi - y_2i+1 sin phi, y_2i sin phi + y_2i+1 cos phi).
+ *   xq, xk     : BF16 [B, N, H, d], contiguous (token-major, as the QKV projection writes them).
+ *   xv         : BF16 [B, N, H, d] or NULL; copied unchanged to v.
+ *   q, k       : BF16 [B, H, N, d] outputs (the layout of attn_fwd's q and k).
+ *   v          : BF16 [B, H, N, d] output, NULL exactly when xv is NULL.
+ *   weight_q/k : FP32 [d] RMSNorm weights or NULL (all ones). Device pointers.
+ *   B, N, H, d : sizes; d must be 128 (ATTN_ERR_UNSUPPORTED otherwise).
+ *   frames, grid_h, grid_w : the token grid, frames * grid_h * grid_w == N.
+ *   eps        : >= 0 (1e-6 in the workloads); theta: > 0 (10000 in the workloads).
+ * No output may overlap an input, a weight or another output (ATTN_ERR_INVALID_ARG).
+ * Asynchronous on `stream`; allocates nothing. Returns an attn_status_t.
+ */
+int attn_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, void* k, void* v,
+                     const float* weight_q, const float* weight_k, int B, int N, int H, int d,
+                     int frames, int grid_h, int grid_w, float eps, float theta, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

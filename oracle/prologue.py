@@ -59,19 +59,23 @@ def pair_frequencies(theta: float = 10000.0, axis_pairs=AXIS_PAIRS):
 
 
 def qk_norm_rope(x_bits, grid, weight=None, eps: float = 1e-6, theta: float = 10000.0,
-                 axis_pairs=AXIS_PAIRS) -> np.ndarray:
+                 axis_pairs=AXIS_PAIRS, tokens=None) -> np.ndarray:
     """RMSNorm over each head row, then interleaved 3-D RoPE; [B, N, H, d] uint16 ->
-    [B, H, N, d] float64."""
-    x = bf16_bits_to_f64(x_bits)
-    B, N, H, d = x.shape
+    [B, H, N, d] float64. With `tokens` (indices into N), only those tokens are evaluated
+    (each token depends on its own rows and position only) and the result is
+    [B, H, len(tokens), d]."""
+    x_bits = np.asarray(x_bits, np.uint16)
+    B, N, H, d = x_bits.shape
     assert d == 2 * sum(axis_pairs)
     assert N == int(np.prod(grid)), "the grid must cover the tokens"
+    toks = np.arange(N) if tokens is None else np.asarray(tokens, np.int64)
+    x = bf16_bits_to_f64(x_bits[:, toks])
     w = np.ones(d) if weight is None else np.asarray(weight, np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     y = x / np.sqrt(ms + float(np.float32(eps))) * w
     axis, freq = pair_frequencies(theta, axis_pairs)
-    pos = grid_positions(grid, N).astype(np.float64)          # [N, 3]
-    phi = pos[:, axis] * freq                                  # [N, 64]
+    pos = grid_positions(grid, N)[toks].astype(np.float64)    # [n, 3]
+    phi = pos[:, axis] * freq                                  # [n, 64]
     c = np.cos(phi)[None, :, None, :]
     s = np.sin(phi)[None, :, None, :]
     ye, yo = y[..., 0::2], y[..., 1::2]

@@ -36,6 +36,8 @@ def lib():
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_fwd_splitkv_workspace_bytes.restype = sz
+    lib.attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     f32, f32, vp]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.restype = ctypes.c_char_p
     return lib
@@ -44,7 +46,7 @@ def lib():
 def test_header_declares_the_expected_api():
     fns = header_functions()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_varlen_workspace_bytes",
-                 "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+                 "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_qk_prologue",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -183,3 +185,38 @@ def test_python_splitkv_workspace_matches_c(lib):
     from video_diffusion_dit_amd import splitkv_workspace_bytes
     assert splitkv_workspace_bytes(1, 16, 180320, slots=256) == 2 * 256 * PART_BYTES
     assert splitkv_workspace_bytes(1, 16, 32768, slots=256) == 0
+
+
+# ---------------------------------------------------------------- prologue
+XQ, XK, XV, PQ, PK, PV, WQ, WK = (0x200000000 * (i + 1) for i in range(8))
+
+
+def prologue(lib, xq=XQ, xk=XK, xv=XV, q=PQ, k=PK, v=PV, wq=None, wk=None, B=1, N=60, H=4, d=128,
+             F=3, gh=4, gw=5, eps=1e-6, theta=10000.0):
+    return lib.attn_qk_prologue(xq, xk, xv, q, k, v, wq, wk, B, N, H, d, F, gh, gw, eps, theta, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(xq=None), INVALID), (dict(k=None), INVALID), (dict(xv=None), INVALID), (dict(v=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(N=0), INVALID), (dict(d=0), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(gw=6), INVALID), (dict(F=0, N=0), INVALID), (dict(gh=-4, gw=-5), INVALID),
+    (dict(eps=-1e-6), INVALID), (dict(eps=math.nan), INVALID), (dict(theta=0.0), INVALID),
+    (dict(theta=math.inf), INVALID),
+    (dict(q=XK), INVALID), (dict(v=XQ + 256), INVALID),                  # an output over an input
+    (dict(k=PQ + 1024), INVALID),                                          # outputs overlap
+    (dict(wq=PV + 64), INVALID),                                           # weight inside an output
+    (dict(B=1 << 20, N=1 << 20, F=1 << 10, gh=1 << 10, gw=1), UNSUPPORTED),
+])
+def test_prologue_validation(lib, kw, code):
+    assert prologue(lib, **kw) == code
+    assert lib.attn_last_error().decode()
+
+
+def test_python_prologue_guards_without_gpu():
+    import torch
+    import video_diffusion_dit_amd as vd
+    x = torch.zeros((1, 6, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        vd.qk_prologue(x.float(), x, grid=(1, 2, 3))
+    with pytest.raises(ValueError):
+        vd.qk_prologue(x, x, grid=(1, 2, 3))          # CPU tensors

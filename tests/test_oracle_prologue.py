@@ -217,3 +217,10 @@ def test_v_is_only_relaid():
         for n in range(5):
             for h in range(3):
                 assert np.array_equal(out[b, h, n], vb[b, n, h])
+
+
+def test_selected_tokens_match_the_full_evaluation():
+    xb = rand_bits((2, 60, 3, 128), seed=11)
+    full = qk_norm_rope(xb, (3, 4, 5))
+    toks = [0, 7, 19, 20, 59]
+    assert np.array_equal(qk_norm_rope(xb, (3, 4, 5), tokens=toks), full[:, :, toks])

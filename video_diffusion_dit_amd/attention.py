@@ -73,6 +73,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_last_error.restype = ctypes.c_char_p
         lib.attn_tile_rows.restype = i32
         lib.attn_tile_keys.restype = i32
+        lib.attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                         f32, f32, vp]
+        lib.attn_qk_prologue.restype = i32
         _lib = lib
         return lib
 
@@ -265,3 +268,45 @@ def _launch_varlen(q, k, v, cu_seqlens, out, lse, scale: float, cu_seqlens_host=
         st = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
                                  nseg, H, T, d, scale, _ptr(ws), ws.numel(), _stream_handle(q.device))
     _raise_for(lib, st)
+
+
+def qk_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor | None = None, *, grid,
+                weight_q: torch.Tensor | None = None, weight_k: torch.Tensor | None = None,
+                eps: float = 1e-6, theta: float = 10000.0, out=None):
+    """Per-head RMSNorm + interleaved 3-D RoPE of the projected Q and K, BF16, into the
+    attention layout (``attn_qk_prologue`` in include/attn.h).
+
+    xq, xk (, xv): bfloat16 [B, N, H, 128] contiguous, token-major. grid = (frames, grid_h,
+    grid_w) with frames * grid_h * grid_w == N. weight_q/weight_k: float32 [128] or None.
+    Returns (q, k) or (q, k, v), bfloat16 [B, H, N, 128]; `out` may hold preallocated outputs.
+    """
+    tensors = [("xq", xq), ("xk", xk)] + ([("xv", xv)] if xv is not None else [])
+    for name, t in tensors:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor, got {tuple(t.shape)}")
+        if t.shape != xq.shape or t.device != xq.device:
+            raise ValueError("xq, xk and xv must have the same shape and device")
+    B, N, H, d = xq.shape
+    for name, w in (("weight_q", weight_q), ("weight_k", weight_k)):
+        if w is not None and (w.dtype != torch.float32 or w.device != xq.device or w.numel() != d
+                              or not w.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [{d}] tensor on {xq.device}")
+    F, gh, gw = (int(g) for g in grid)
+    if out is None:
+        out = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=xq.device)
+                    for _ in range(len(tensors)))
+    q, k = out[0], out[1]
+    v = out[2] if xv is not None else None
+    for t in out:
+        if t.shape != (B, H, N, d) or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != xq.device:
+            raise ValueError("out tensors must be contiguous bfloat16 [B, H, N, d] on the input device")
+    lib = load_library()
+    st = lib.attn_qk_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(weight_q), _ptr(weight_k), B, N, H, d, F, gh, gw,
+                              float(eps), float(theta), _stream_handle(xq.device))
+    _raise_for(lib, st)
+    return tuple(out)

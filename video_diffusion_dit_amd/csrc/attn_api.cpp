@@ -121,6 +121,38 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
                                                     static_cast<hipStream_t>(stream)));
 }
 
+int attn_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, void* k, void* v,
+                     const float* weight_q, const float* weight_k, int B, int N, int H, int d,
+                     int frames, int grid_h, int grid_w, float eps, float theta, void* stream) {
+    g_last_error[0] = '\0';
+    if (xq == nullptr || xk == nullptr || q == nullptr || k == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "xq, xk, q and k must be non-null device pointers");
+    if ((xv == nullptr) != (v == nullptr)) return fail(ATTN_ERR_INVALID_ARG, "xv and v must both be given or both be null");
+    if (B <= 0 || N <= 0 || H <= 0) return fail(ATTN_ERR_INVALID_ARG, "B, N and H must be >= 1");
+    if (d <= 0) return fail(ATTN_ERR_INVALID_ARG, "d must be >= 1");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
+    if (frames <= 0 || grid_h <= 0 || grid_w <= 0 || product(frames, grid_h, grid_w, 1) != N)
+        return fail(ATTN_ERR_INVALID_ARG, "frames * grid_h * grid_w must equal N (all >= 1)");
+    if (!isfinite(eps) || eps < 0.f) return fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!isfinite(theta) || theta <= 0.f) return fail(ATTN_ERR_INVALID_ARG, "theta must be finite and > 0");
+    const long long elems = product(B, N, H, d);
+    if (elems < 0 || product(B, N, 1, 1) > 4LL * INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const size_t bytes = (size_t)elems * 2;
+    const void* outs[3] = {q, k, v};
+    const void* ins[3] = {xq, xk, xv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (overlaps(outs[i], bytes, ins[j], bytes)) return fail(ATTN_ERR_INVALID_ARG, "an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], bytes, outs[j], bytes)) return fail(ATTN_ERR_INVALID_ARG, "q, k and v overlap");
+        if (overlaps(outs[i], bytes, weight_q, 512) || overlaps(outs[i], bytes, weight_k, 512))
+            return fail(ATTN_ERR_INVALID_ARG, "an output overlaps a weight");
+    }
+    return hip_status(attn_impl::launch_qk_prologue(xq, xk, xv, q, k, v, weight_q, weight_k, B, N, H,
+                                                    grid_h, grid_w, eps, theta,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
     if (nseg <= 0 || H <= 0 || total_tokens < 0) return 0;
     return attn_impl::varlen_workspace_bytes(nseg, total_tokens);

@@ -39,4 +39,10 @@ hipError_t launch_varlen(const void* q, const void* k, const void* v, void* out,
                          const int32_t* cu_seqlens, int nseg, int H, int total_tokens, float scale,
                          void* workspace, hipStream_t stream);
 
+// Prologue: per-head RMSNorm + interleaved 3-D RoPE on xq/xk (token-major [B,N,H,128] BF16)
+// into q/k ([B,H,N,128] BF16); xv -> v re-laid only (both may be null). N = F * Hp * Wp.
+hipError_t launch_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, void* k, void* v,
+                              const float* wq, const float* wk, int B, int N, int H, int Hp, int Wp,
+                              float eps, float theta, hipStream_t stream);
+
 }  // namespace attn_impl

@@ -33,6 +33,8 @@ Register map (per lane):
     v[128:143]           K fragment ring (4 x 4)       v[144:159]   V fragment ring (4 x 4)
     v160..v175           m, l, half sums, mask limit, -inf, tile sums
     v176..v199           temporaries (check, exact path)
+    s[40:61]             resource cursors, counters, masks, return address; s61 keeps the
+                         caller's M0 (the loads move it), which is restored at the end
     a[0:127]             O^T: block (db, rb) at 16*(2*db + rb)
     a[128:191]           Q fragments: (rb, s) at 128 + 4*(8*rb + s)
 The block hands O^T back in v[0:127] (same numbering), m and l in operands.
@@ -67,6 +69,7 @@ S_T, S_TLAST, S_LIM = 49, 50, 52   # tile counter, last loop tile, 256.0
 S_RA = 54                          # exact-path return address s[54:55]
 S_C1, S_C2 = 56, 58                # check masks
 S_STG = 60                         # K stage offset handed to the exact path
+S_M0 = 61                          # M0 of the caller, restored at the end
 NS_LO, NS_HI = 40, 61
 
 K_STAGE = 16384
@@ -506,6 +509,7 @@ def final_phase(E, Y, stage, uid):
 def generate(backedge=None):
     E = Emitter()
     # ---- set-up: cursors, statistics, Q (to AGPRs), O = 0, tiles 0..2
+    E.raw("s_mov_b32 s%d, m0" % S_M0)
     for i in range(4):
         E.salu("s_mov_b32 s%d, %%[rk%d]" % (SK + i, i))
         E.salu("s_mov_b32 s%d, %%[rv%d]" % (SV + i, i))
@@ -585,6 +589,7 @@ def generate(backedge=None):
     E.fresh()
     E.nop(12)
     E.raw("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    E.raw("s_mov_b32 m0, s%d" % S_M0)
     for i in range(128):
         E.raw("v_accvgpr_read_b32 v%d, a%d" % (i, O_BASE + i))
     for rb in range(2):
@@ -603,7 +608,7 @@ def render():
     else:
         raise SystemExit("wait-state pass did not converge")
     clob = ['"v%d"' % i for i in range(128, NV)] + ['"a%d"' % i for i in range(NA)] + \
-           ['"s%d"' % i for i in range(NS_LO, NS_HI + 1)] + ['"vcc"', '"m0"', '"scc"', '"memory"']
+           ['"s%d"' % i for i in range(NS_LO, NS_HI + 1)] + ['"vcc"', '"scc"', '"memory"']
     outs = ['[o%d%d] "=&{v[%d:%d]}"(o[%d][%d])' % (db, rb, oblk(db, rb), oblk(db, rb) + 15, db, rb)
             for db in range(4) for rb in range(2)]
     outs += ['[m0] "=v"(mref[0])', '[m1] "=v"(mref[1])', '[l0] "=v"(lsum[0])', '[l1] "=v"(lsum[1])']

@@ -115,8 +115,14 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     correctly rounds to infinity.
     """
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    out = t.astype(np.uint16)
+    if not np.isnan(u.view(np.float32)).any():
+        return out
     nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
     if nan.any():
         out[nan] = ((u[nan] >> np.uint32(16)) & np.uint32(0x8000)).astype(np.uint16) | np.uint16(0x7FC0)
@@ -247,6 +253,36 @@ def make_varlen(w: Workload, threads: int | None = None):
     cu = np.zeros(len(w.seqlens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(w.seqlens)
     return out[0], out[1], out[2], cu
+
+
+PROJ_ROOT = 7   # SeedSequence key of the projected-input streams (apart from the workload indices)
+
+
+def make_projected(B: int, grid: tuple, H: int, seed: int = 0, with_v: bool = True,
+                   threads: int | None = None, d: int = HEAD_DIM, chunk: int = 4096):
+    """Raw projected Q, K (and V) as the QKV projection hands them to the prologue: BF16 bit
+    patterns [B, N, H, d] (token-major), N = prod(grid). Every row is N(0, 1) times its own
+    log-normal scale (sigma 0.5), so rows differ in RMS the way projection outputs do; one
+    independent PCG64 stream per (tensor, batch, block of `chunk` tokens)."""
+    N = int(np.prod(grid))
+    roles = 3 if with_v else 2
+    nchunk = (N + chunk - 1) // chunk
+    kids = np.random.SeedSequence([ROOT_SEED, PROJ_ROOT, seed]).spawn(roles)
+    out = [np.empty((B, N, H, d), dtype=np.uint16) for _ in range(roles)]
+    jobs = [(r, i, ss) for r in range(roles) for i, ss in enumerate(kids[r].spawn(B * nchunk))]
+
+    def run(job):
+        r, i, ss = job
+        b, c = divmod(i, nchunk)
+        n0, n1 = c * chunk, min(N, (c + 1) * chunk)
+        rng = np.random.Generator(np.random.PCG64(ss))
+        x = rng.standard_normal((n1 - n0, H, d), dtype=np.float32)
+        x *= rng.lognormal(0.0, 0.5, size=(n1 - n0, H, 1)).astype(np.float32)
+        out[r][b, n0:n1] = f32_to_bf16_bits(x)
+
+    with ThreadPoolExecutor(threads or _threads()) as ex:
+        list(ex.map(run, jobs))
+    return tuple(out)
 
 
 def make_ragged(w: Workload, dense=None, threads: int | None = None):
