@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "dense": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
     "varlen": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
     "prologue": ("prologue_gfx950.hip",),
+    "linear": ("linear_gfx950.hip",),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -53,11 +54,18 @@ CALL_KERNELS = {
     "dense": ("attn_fwd_dense_kernel", "attn_fwd_dense_split_kernel", "merge_kernel"),
     "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule"),
     "prologue": ("qk_prologue_kernel",),
+    "linear": ("linear_out_kernel", "linear_kv_partial_kernel", "linear_kv_reduce_kernel"),
 }
 
 
 def prologue_bytes(B: int, N: int, H: int, d: int = 128) -> float:
     """Algorithmic HBM bytes of one prologue call: Q, K, V rows read once and written once."""
+    return float(B) * N * H * d * 2 * 6
+
+
+def linear_bytes(B: int, N: int, H: int, d: int = 128) -> float:
+    """Algorithmic HBM bytes of one linear-attention call: q, k, q_rot, k_rot, v read once, out
+    written once (the d x d state and the chunk partials are not counted)."""
     return float(B) * N * H * d * 2 * 6
 
 
@@ -130,6 +138,8 @@ def write_traffic_profile(args) -> int:
     tokens = w.B * w.N if w.kind == "dense" else w.total_tokens
     if kind == "prologue":
         algorithmic = prologue_bytes(w.B, w.N, w.H, w.d)
+    elif kind == "linear":
+        algorithmic = linear_bytes(w.B, w.N, w.H, w.d)
     else:
         algorithmic = tokens * w.H * (8.0 * w.d + 4.0)
     path = os.path.join(PROFILES, f"{kernel}_{args.workload}_hbm_traffic.txt")
@@ -219,6 +229,69 @@ def time_prologue(args, w, vd, dev) -> dict:
     return rec
 
 
+def time_linear(args, w, vd, dev) -> dict:
+    """Time the SANA-Video linear attention at the workload's token grid and heads, on seeded
+    ReLU'd/rotated inputs resident in HBM; check seeded tokens against the oracle."""
+    import numpy as np
+    import torch
+
+    from workloads import make_linear_inputs
+    t0 = time.time()
+    xb = make_linear_inputs(w.B, w.grid, w.H, seed=0)
+    xs = [dev(b) for b in xb]
+    out = torch.empty_like(xs[0])
+    print(f"[bench] linear-attention inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def call():
+        vd.linear_attention(*xs, out=out)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.linear_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.linear_steps)]
+    torch.cuda.synchronize()
+    for i in range(args.linear_steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg = float(np.mean(ms))
+    nbytes = linear_bytes(w.B, w.N, w.H, w.d)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    flops = 2 * 2.0 * w.B * w.H * w.N * w.d * w.d          # the two d x d products per token
+    rec = {
+        "kernel": "linear_out_kernel",
+        "what": "SANA-Video linear attention (V K_rot^T) Q_rot / (K.sum Q + 1e-15), BF16 [B,N,H,128]",
+        "timed": "whole call: linear_kv_partial_kernel, linear_kv_reduce_kernel, linear_out_kernel",
+        "bound": "hbm",
+        "achieved": round(gbs, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic(w.name, "linear_out_kernel", False, "linear"),
+        "algorithmic_bytes": nbytes,
+        "tflops": round(flops / (avg * 1e-3) / 1e12, 2),
+        "ms": {"avg": round(avg, 4), "min": round(min(ms), 4), "max": round(max(ms), 4)},
+        "steps": args.linear_steps,
+    }
+    print(f"[bench] linear attention {args.linear_steps} calls: {avg:.4f} ms -> {gbs:.0f} GB/s "
+          f"({100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f})", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        from oracle import bf16_bits_to_f64
+        from oracle.linear import linear_attention
+        toks = np.random.default_rng(2).choice(w.N, 256, replace=False)
+        heads = [0, w.H - 1]                         # the key-side sums run over every token
+        got = bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)[:, toks][:, :, heads])
+        ref = linear_attention(*[x[:, :, heads] for x in xb], tokens=toks)
+        rec["parity"] = {"rel_l2": round(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), 8),
+                         "n_elems": int(got.size), "ok": bool(np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref))}
+    del xs, out
+    torch.cuda.empty_cache()
+    return rec
+
+
 def host_cores() -> int:
     try:
         return len(os.sched_getaffinity(0))
@@ -247,6 +320,8 @@ def main() -> int:
                     help="with --write-traffic-profile: which call's kernels to record (default: the workload's)")
     ap.add_argument("--prologue-steps", type=int, default=20,
                     help="timed calls of the Q/K RMSNorm+RoPE prologue at the workload's grid (0: skip)")
+    ap.add_argument("--linear-steps", type=int, default=10,
+                    help="timed calls of the SANA-Video linear attention at the workload's grid (0: skip)")
     ap.add_argument("--profile-command", default="",
                     help="the command lines that produced the counter files (recorded in the profile)")
     args = ap.parse_args()
@@ -364,6 +439,8 @@ def main() -> int:
 
     if w.grid is not None and args.prologue_steps > 0:
         result["prologue"] = time_prologue(args, w, vd, dev)
+    if w.grid is not None and args.linear_steps > 0:
+        result["linear_attention"] = time_linear(args, w, vd, dev)
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0")   # contents irrelevant: bytes are counted

@@ -145,6 +145,37 @@ int attn_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, vo
                      const float* weight_q, const float* weight_k, int B, int N, int H, int d,
                      int frames, int grid_h, int grid_w, float eps, float theta, void* stream);
 
+/*
+ * SANA-Video linear attention (ReLU feature map, rotated Q/K in the numerator, un-rotated Q/K
+ * in the normaliser), per batch b and head h over the N tokens:
+ *   ksum = sum_m k_m;  den_n = q_n . ksum + eps;  kv = sum_m v_m k_rot_m^T (d x d);
+ *   out_n = (kv q_rot_n) / den_n.
+ * Page "PR #35728 report", key source excerpts (sana_video.py forward: normaliser
+ * 1 / (K.sum(-1)^T Q + 1e-15) from the un-rotated ReLU'd K and Q, then (V K_rot^T) Q_rot times
+ * it, flattened back to [B, N, H*D]; try_sana_video_linear_attention: the first product with
+ * BF16 inputs and FP32 accumulation, the second in FP32). Here kv and ksum accumulate in FP32
+ * (BF16 MFMA for kv), the second product runs on FP32 values (kv split exactly into three
+ * BF16 terms on the matrix cores), den and the division in FP32; out is rounded to BF16.
+ *   q, k        : BF16 [B, N, H, d], the ReLU-activated (un-rotated) rows, token-major.
+ *   q_rot, k_rot: BF16 [B, N, H, d], the same rows after the rotary embedding.
+ *   v           : BF16 [B, N, H, d].
+ *   out         : BF16 [B, N, H, d] (the page's [B, N, H*D] after its transpose).
+ *   B, N, H, d  : sizes, d must be 128 (ATTN_ERR_UNSUPPORTED otherwise).
+ *   eps         : finite, >= 0 (the page's 1e-15).
+ *   workspace   : DEVICE scratch of at least attn_linear_workspace_bytes(B, N, H, d) bytes,
+ *                 256-byte aligned (per-chunk partial sums, then kv and ksum); no
+ *                 initialisation needed; not to be shared by calls that may run concurrently.
+ * out may not overlap an input, nor the workspace any tensor (ATTN_ERR_INVALID_ARG).
+ * Asynchronous on `stream`; allocates nothing. Deterministic for the same inputs.
+ * Returns an attn_status_t.
+ */
+int attn_linear_fwd(const void* q, const void* k, const void* q_rot, const void* k_rot, const void* v,
+                    void* out, int B, int N, int H, int d, float eps, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_linear_fwd needs (0 if the sizes are invalid). */
+size_t attn_linear_workspace_bytes(int B, int N, int H, int d);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

@@ -38,6 +38,9 @@ def lib():
     lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      f32, f32, vp]
+    lib.attn_linear_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.attn_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_linear_workspace_bytes.restype = sz
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.restype = ctypes.c_char_p
     return lib
@@ -47,6 +50,7 @@ def test_header_declares_the_expected_api():
     fns = header_functions()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_varlen_workspace_bytes",
                  "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_qk_prologue",
+                 "attn_linear_fwd", "attn_linear_workspace_bytes",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -220,3 +224,37 @@ def test_python_prologue_guards_without_gpu():
         vd.qk_prologue(x.float(), x, grid=(1, 2, 3))
     with pytest.raises(ValueError):
         vd.qk_prologue(x, x, grid=(1, 2, 3))          # CPU tensors
+
+
+# ---------------------------------------------------------------- linear attention
+LQ, LK, LQR, LKR, LV, LO, LWS = (0x4000000000 * (i + 1) for i in range(7))
+
+
+def linear(lib, q=LQ, k=LK, qr=LQR, kr=LKR, v=LV, o=LO, B=1, N=300, H=2, d=128, eps=1e-15, ws=LWS, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_linear_workspace_bytes(B, N, H, 128)
+    return lib.attn_linear_fwd(q, k, qr, kr, v, o, B, N, H, d, eps, ws, wsb, None)
+
+
+def test_linear_workspace_query(lib):
+    f = lib.attn_linear_workspace_bytes
+    # per head: one chunk partial (128*128 + 128 floats) per 2048 tokens, then kv as three
+    # BF16 terms and ksum (FP32), each region 256-byte aligned
+    a = lambda x: (x + 255) // 256 * 256
+    one, terms, ks = (128 * 128 + 128) * 4, 3 * 128 * 128 * 2, 128 * 4
+    assert f(1, 300, 2, 128) == a(2 * one) + a(2 * terms) + a(2 * ks)
+    assert f(1, 180320, 16, 128) == a(16 * 89 * one) + a(16 * terms) + a(16 * ks)
+    assert f(0, 300, 2, 128) == 0 and f(1, 300, 2, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(kr=None), INVALID), (dict(o=None), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID), (dict(d=0), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(eps=-1.0), INVALID), (dict(eps=math.inf), INVALID),
+    (dict(o=LV + 128), INVALID),                                     # out overlaps v
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=LWS + 8), WORKSPACE),
+    (dict(ws=LO), INVALID),                                          # workspace over out
+])
+def test_linear_validation(lib, kw, code):
+    assert linear(lib, **kw) == code
+    assert lib.attn_last_error().decode()

@@ -76,6 +76,10 @@ def load_library() -> ctypes.CDLL:
         lib.attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          f32, f32, vp]
         lib.attn_qk_prologue.restype = i32
+        lib.attn_linear_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+        lib.attn_linear_fwd.restype = i32
+        lib.attn_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.attn_linear_workspace_bytes.restype = sz
         _lib = lib
         return lib
 
@@ -310,3 +314,29 @@ def qk_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor | None = No
                               float(eps), float(theta), _stream_handle(xq.device))
     _raise_for(lib, st)
     return tuple(out)
+
+
+def linear_attention(q: torch.Tensor, k: torch.Tensor, q_rot: torch.Tensor, k_rot: torch.Tensor,
+                     v: torch.Tensor, eps: float = 1e-15, out: torch.Tensor | None = None) -> torch.Tensor:
+    """SANA-Video linear attention (``attn_linear_fwd`` in include/attn.h): inputs bfloat16
+    [B, N, H, 128] token-major (q, k ReLU'd; q_rot, k_rot rotated); returns bfloat16
+    [B, N, H, 128]. The workspace is cached per device."""
+    for name, t in (("q", q), ("k", k), ("q_rot", q_rot), ("k_rot", k_rot), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor, got {tuple(t.shape)}")
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k, q_rot, k_rot and v must have the same shape and device")
+    B, N, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    lib = load_library()
+    need = int(lib.attn_linear_workspace_bytes(B, N, H, d))
+    ws = _workspace(q.device, need) if need else None
+    st = lib.attn_linear_fwd(_ptr(q), _ptr(k), _ptr(q_rot), _ptr(k_rot), _ptr(v), _ptr(out), B, N, H, d,
+                             float(eps), _ptr(ws), need, _stream_handle(q.device))
+    _raise_for(lib, st)
+    return out

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattn.so")
-SOURCES = ["attn_fwd_gfx950.hip", "prologue_gfx950.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_gfx950.hip", "prologue_gfx950.hip", "linear_gfx950.hip", "attn_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.

@@ -153,6 +153,40 @@ int attn_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, vo
                                                     static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_linear_workspace_bytes(int B, int N, int H, int d) {
+    if (B <= 0 || N <= 0 || H <= 0 || d != 128 || product(B, N, H, d) < 0) return 0;
+    return attn_impl::linear_workspace_bytes(B, N, H);
+}
+
+int attn_linear_fwd(const void* q, const void* k, const void* q_rot, const void* k_rot, const void* v, void* out,
+                    int B, int N, int H, int d, float eps, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    g_last_error[0] = '\0';
+    if (q == nullptr || k == nullptr || q_rot == nullptr || k_rot == nullptr || v == nullptr || out == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, q_rot, k_rot, v and out must be non-null device pointers");
+    if (B <= 0 || N <= 0 || H <= 0) return fail(ATTN_ERR_INVALID_ARG, "B, N and H must be >= 1");
+    if (d <= 0) return fail(ATTN_ERR_INVALID_ARG, "d must be >= 1");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
+    if (!isfinite(eps) || eps < 0.f) return fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const long long elems = product(B, N, H, d);
+    if (elems < 0 || product(B, H, (N + 255) / 256, 1) > INT_MAX / 2) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const size_t bytes = (size_t)elems * 2;
+    const void* ins[5] = {q, k, q_rot, k_rot, v};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(out, bytes, ins[i], bytes)) return fail(ATTN_ERR_INVALID_ARG, "out overlaps an input");
+    const size_t need = attn_impl::linear_workspace_bytes(B, N, H);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_linear_workspace_bytes()");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (overlaps(workspace, need, out, bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps out");
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(workspace, need, ins[i], bytes)) return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps an input");
+    return hip_status(attn_impl::launch_linear(q, k, q_rot, k_rot, v, out, B, N, H, eps, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
     if (nseg <= 0 || H <= 0 || total_tokens < 0) return 0;
     return attn_impl::varlen_workspace_bytes(nseg, total_tokens);

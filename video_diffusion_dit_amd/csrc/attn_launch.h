@@ -45,4 +45,10 @@ hipError_t launch_qk_prologue(const void* xq, const void* xk, const void* xv, vo
                               const float* wq, const float* wk, int B, int N, int H, int Hp, int Wp,
                               float eps, float theta, hipStream_t stream);
 
+// Linear attention: q, k (ReLU'd), q_rot, k_rot, v, out BF16 [B,N,H,128] token-major;
+// workspace >= linear_workspace_bytes(B, N, H), 256-byte aligned.
+size_t linear_workspace_bytes(int B, int N, int H);
+hipError_t launch_linear(const void* q, const void* k, const void* qr, const void* kr, const void* v, void* out,
+                         int B, int N, int H, float eps, void* workspace, hipStream_t stream);
+
 }  // namespace attn_impl

@@ -285,6 +285,35 @@ def make_projected(B: int, grid: tuple, H: int, seed: int = 0, with_v: bool = Tr
     return tuple(out)
 
 
+def make_linear_inputs(B: int, grid: tuple, H: int, seed: int = 0, threads: int | None = None,
+                       d: int = HEAD_DIM, chunk: int = 4096):
+    """Inputs of the SANA-Video linear attention: q, k = ReLU(RMSNorm(x)) rounded to BF16, and
+    q_rot, k_rot = the interleaved 3-D RoPE of those BF16 rows (FP32, rounded once); v plain.
+    x are the projected rows of make_projected. All BF16 bit patterns [B, N, H, d] (token-major)."""
+    xq, xk, xv = make_projected(B, grid, H, seed=seed, threads=threads, d=d)
+    N = int(np.prod(grid))
+    cos, sin = rope_tables(grid, N, d)                        # [N, d/2]
+    out = [np.empty_like(xq) for _ in range(4)]
+
+    def run(job):
+        which, b, n0 = job
+        n1 = min(N, n0 + chunk)
+        x = xq if which == 0 else xk
+        f = ((x[b, n0:n1].astype(np.uint32) << 16).view(np.float32))       # [n, H, d]
+        act = np.maximum(rmsnorm_rows(f), np.float32(0.0))
+        act_bits = f32_to_bf16_bits(act)
+        act_r = (act_bits.astype(np.uint32) << 16).view(np.float32)
+        rot = rope_interleaved(act_r, cos[n0:n1, None, :], sin[n0:n1, None, :])
+        out[2 * which][b, n0:n1] = act_bits
+        out[2 * which + 1][b, n0:n1] = f32_to_bf16_bits(rot)
+
+    jobs = [(which, b, n0) for which in (0, 1) for b in range(B) for n0 in range(0, N, chunk)]
+    with ThreadPoolExecutor(threads or _threads()) as ex:
+        list(ex.map(run, jobs))
+    q, q_rot, k, k_rot = out
+    return q, k, q_rot, k_rot, xv
+
+
 def make_ragged(w: Workload, dense=None, threads: int | None = None):
     """Varlen call of the stress recipe: segments w.ragged, THD [T, H, d].
 
