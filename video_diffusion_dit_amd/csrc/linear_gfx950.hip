@@ -232,10 +232,22 @@ __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
     OutFrags cur, nxt;
     load_out_frags(a, base, row_stride, n0 + 64 * w, col, g, cur);
     // kv terms -> LDS (row i of term t at t*D*KVROW + i*KVROW), 16 bytes per thread and step
+    // (straight-line batches of 8 loads, so the waits count the loads in flight instead of
+    // draining the queue after each one)
     const u32x4* src = reinterpret_cast<const u32x4*>(a.terms + (long)bh * KV_TERMS * D * D);
-    for (int cidx = tid; cidx < KV_TERMS * D * (D / 8); cidx += NT) {
-        const int row = cidx >> 4, ch = cidx & 15;          // row = term * D + i
-        *reinterpret_cast<u32x4*>(kvs + row * KVROW + 16 * ch) = src[cidx];
+    constexpr int PER = KV_TERMS * D * (D / 8) / NT;      // 24 chunks of 16 bytes per thread
+    static_assert(PER % 8 == 0, "copy batches");
+#pragma unroll
+    for (int bt = 0; bt < PER; bt += 8) {
+        u32x4 tmp[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tmp[u] = src[tid + (bt + u) * NT];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int cidx = tid + (bt + u) * NT;
+            const int row = cidx >> 4, ch = cidx & 15;      // row = term * D + i
+            *reinterpret_cast<u32x4*>(kvs + row * KVROW + 16 * ch) = tmp[u];
+        }
     }
     if (tid < D) ksum_s[tid] = a.ksum[(long)bh * D + tid];
     __syncthreads();
