@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "varlen": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
     "prologue": ("prologue_gfx950.hip",),
     "linear": ("linear_gfx950.hip",),
+    "block_sparse": ("attn_fwd_gfx950.hip", "key_loop_idx_gfx950.inc", "block_route_gfx950.hip"),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -55,6 +56,7 @@ CALL_KERNELS = {
     "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule"),
     "prologue": ("qk_prologue_kernel",),
     "linear": ("linear_out_kernel", "linear_kv_partial_kernel", "linear_kv_reduce_kernel"),
+    "block_sparse": ("attn_fwd_block_sparse_kernel", "route_kernel", "pool_kernel"),
 }
 
 
@@ -292,6 +294,86 @@ def time_linear(args, w, vd, dev) -> dict:
     return rec
 
 
+def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict:
+    """Time block-skip attention (routing, then the block-sparse pass) on the workload's
+    resident Q/K/V at threshold --block-skip-tau; FLOP counts only the (query, key) pairs the
+    kept tiles cover. Checks seeded rows against the oracle over the kept tiles."""
+    import numpy as np
+    import torch
+
+    tau = args.block_skip_tau
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        res = None
+        for i in range(n):
+            starts[i].record(stream)
+            res = fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in zip(starts, ends)], res
+
+    route_ms, (kv_idx, kv_cnt) = timed(lambda: vd.block_route(q, k, tau=tau, scale=w.scale), args.block_skip_steps)
+    sparse_ms, _ = timed(lambda: vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out),
+                         args.block_skip_steps)
+    ntq, ntk = -(-w.N // 256), -(-w.N // 64)
+    cnt = kv_cnt.cpu().numpy().astype(np.int64)
+    idx = kv_idx.cpu().numpy()
+    last_kept = np.take_along_axis(idx, np.maximum(cnt - 1, 0)[..., None], -1)[..., 0] == ntk - 1
+    keys = cnt * 64 - last_kept * (64 * ntk - w.N)
+    rows = np.minimum(256, w.N - 256 * np.arange(ntq))
+    pairs = float((keys * rows).sum())
+    density = pairs / (float(w.B) * w.H * w.N * w.N)
+    avg_s, avg_r = float(np.mean(sparse_ms)), float(np.mean(route_ms))
+    flops = 4.0 * w.d * pairs
+    tf = flops / (avg_s * 1e-3) / 1e12
+    rec = {
+        "kernel": "attn_fwd_block_sparse_kernel",
+        "what": "block-skip attention: pooled-proxy routing of 64-key tiles per 256-row query tile "
+                "(keep z >= max z - tau), then exact softmax attention over the kept tiles",
+        "tau": tau,
+        "density": round(density, 4),
+        "bound": "mfma",
+        "achieved": round(tf, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+        "flops_per_call": flops,
+        "traffic": measured_traffic(w.name, "attn_fwd_block_sparse_kernel", False, "block_sparse"),
+        "ms": {"sparse": round(avg_s, 4), "sparse_min": round(min(sparse_ms), 4),
+               "sparse_max": round(max(sparse_ms), 4), "route": round(avg_r, 4)},
+        "speedup_vs_dense_call": round(dense_ms / (avg_s + avg_r), 3),
+        "steps": args.block_skip_steps,
+    }
+    print(f"[bench] block-skip tau={tau}: density {density:.4f}, route {avg_r:.3f} ms, sparse {avg_s:.3f} ms "
+          f"-> {tf:.1f} TFLOP/s on kept pairs ({100 * tf / PEAK_BF16_TFLOPS:.1f} % of peak), "
+          f"{dense_ms / (avg_s + avg_r):.2f}x the dense call", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        from oracle import compare
+        from oracle.block_sparse import attention_kept
+        keep = np.zeros((w.B, w.H, ntq, ntk), bool)
+        b_, h_, i_ = np.nonzero(cnt > 0)
+        for b, h, i in zip(b_, h_, i_):
+            keep[b, h, i, idx[b, h, i, :cnt[b, h, i]]] = True
+        rows_s = np.random.default_rng(3).choice(w.B * w.H * w.N, 128, replace=False)
+        o_ref, _ = attention_kept(qb, kb, vb, w.scale, keep, rows=rows_s)
+        vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, w.d)[rows_s]
+        from oracle import bf16_bits_to_f64
+        m = compare(bf16_bits_to_f64(got), o_ref)
+        rec["parity"] = {"rel_l2": round(float(m["rel_l2"]), 8), "n_elems": int(m["n_elems"]), "ok": bool(m["ok"])}
+    del out, lse, kv_idx, kv_cnt
+    torch.cuda.empty_cache()
+    return rec
+
+
 def host_cores() -> int:
     try:
         return len(os.sched_getaffinity(0))
@@ -322,6 +404,10 @@ def main() -> int:
                     help="timed calls of the Q/K RMSNorm+RoPE prologue at the workload's grid (0: skip)")
     ap.add_argument("--linear-steps", type=int, default=10,
                     help="timed calls of the SANA-Video linear attention at the workload's grid (0: skip)")
+    ap.add_argument("--block-skip-steps", type=int, default=5,
+                    help="dense workloads: timed calls of block-skip attention on the same inputs (0: skip)")
+    ap.add_argument("--block-skip-tau", type=float, default=0.02,
+                    help="routing threshold of the timed block-skip calls")
     ap.add_argument("--profile-command", default="",
                     help="the command lines that produced the counter files (recorded in the profile)")
     args = ap.parse_args()
@@ -437,6 +523,8 @@ def main() -> int:
         "cpu_baseline": None,
     }
 
+    if w.kind == "dense" and args.block_skip_steps > 0:
+        result["block_skip"] = time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, avg_kernel_ms)
     if w.grid is not None and args.prologue_steps > 0:
         result["prologue"] = time_prologue(args, w, vd, dev)
     if w.grid is not None and args.linear_steps > 0:

@@ -176,6 +176,73 @@ int attn_linear_fwd(const void* q, const void* k, const void* q_rot, const void*
 /* Workspace bytes attn_linear_fwd needs (0 if the sizes are invalid). */
 size_t attn_linear_workspace_bytes(int B, int N, int H, int d);
 
+/*
+ * Block-skip attention (a block-sparse hook in the key loop). Page "PR #33702 report" (the
+ * Sol-Attn backend for MiniMax-H3), motivation and breakdown: inside the online-softmax pass,
+ * KV blocks are routed by a threshold (knob tau) and the rest skipped, without a full proxy
+ * score map; sink tokens stay in; a dense guard keeps the first dense_steps denoising steps and
+ * the dense_layers layers dense; head size 128 and BF16 only. The page gives no routing
+ * formula; the one implemented here is stated at attn_block_route.
+ *
+ * Key-tile lists (the hook's interface): for dense [B, H, N, 128] inputs, query tile I =
+ * rows 256*I .. 256*I+255 of one (b, h) (ntq = ceil(N/256) tiles), key tile J = keys
+ * 64*J .. 64*J+63 (ntk = ceil(N/64) tiles). Item = (b*H + h)*ntq + I.
+ *   kv_idx : int32 [B*H*ntq][attn_block_list_stride(N)]; row `item` holds kv_cnt[item]
+ *            strictly ascending key-tile indices in [0, ntk); the entries after them are read
+ *            (up to 8) but never attended to.
+ *   kv_cnt : int32 [B*H*ntq].
+ * A list that breaks these rules is processed memory-safely (each index is clamped to
+ * [previous index, ntk], the count to [0, ntk]) with an unspecified result.
+ */
+
+/* Row stride of kv_idx in entries: ceil(N/64) + 8 (0 if N <= 0). */
+int attn_block_list_stride(int N);
+
+/*
+ * Block-skip attention forward over given key-tile lists: the rows of query tile I attend
+ * to the keys of the tiles kv_idx[item][0 .. kv_cnt[item]-1] only (exact softmax over them,
+ * the numerics of attn_fwd). With every tile listed the result equals attn_fwd bit for bit.
+ * A tile with kv_cnt <= 0 gets O = 0 and LSE = -inf.
+ *   q, k, v, out, lse, B, H, N, d, scale, stream : as attn_fwd.
+ *   kv_idx, kv_cnt : DEVICE lists as above (read only); out and lse must not overlap them.
+ * Returns an attn_status_t.
+ */
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N, int d,
+                          float scale, void* stream);
+
+/*
+ * Key-tile routing of block-skip attention: writes kv_idx and kv_cnt for dense [B, H, N, 128]
+ * BF16 q and k. Rule (a reading of the page, which names the knobs only): with qbar_I the
+ * mean of the valid query rows of tile I and kbar_J that of the valid keys of tile J (FP32),
+ *     z_IJ = scale * qbar_I . kbar_J,   J is kept for I  iff  z_IJ >= max_J' z_IJ' - tau
+ *                                                       or  64*J < sink_tokens.
+ * The tile with the largest z is always kept, so kv_cnt >= 1. The z values are evaluated in
+ * FP32; a tile within FP32 rounding of the threshold may go either way.
+ *   tau         : >= 0; +inf keeps every tile (dense attention). NaN is rejected.
+ *   sink_tokens : >= 0; the key tiles holding keys 0 .. sink_tokens-1 are always kept.
+ *   kv_idx, kv_cnt : DEVICE outputs (sizes above); entries after each count up to 8 are set
+ *                 to ntk.
+ *   workspace   : DEVICE scratch of attn_block_route_workspace_bytes(B, H, N, d) bytes,
+ *                 256-byte aligned (the pooled tiles); no initialisation needed.
+ * Sequences of more than 15360 key tiles (N > 983040) return ATTN_ERR_UNSUPPORTED.
+ * Returns an attn_status_t.
+ */
+int attn_block_route(const void* q, const void* k, int B, int H, int N, int d, float scale, float tau,
+                     int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_block_route needs (0 if the sizes are invalid). */
+size_t attn_block_route_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * The dense guard of block-skip attention (host only): 1 if denoising step `step` of layer
+ * `layer` should run dense attention -- step < dense_steps, or layer listed in dense_layers
+ * ("a" or "a-b" inclusive items separated by commas, blanks allowed; NULL or "" lists none)
+ * -- else 0; ATTN_ERR_INVALID_ARG for negative arguments or a malformed list.
+ */
+int attn_block_skip_use_dense(int step, int layer, int dense_steps, const char* dense_layers);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

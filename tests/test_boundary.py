@@ -41,6 +41,12 @@ def lib():
     lib.attn_linear_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_linear_workspace_bytes.restype = sz
+    lib.attn_block_list_stride.argtypes = [i32]
+    lib.attn_block_route_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_block_route_workspace_bytes.restype = sz
+    lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+    lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+    lib.attn_block_skip_use_dense.argtypes = [i32, i32, i32, ctypes.c_char_p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.restype = ctypes.c_char_p
     return lib
@@ -50,7 +56,9 @@ def test_header_declares_the_expected_api():
     fns = header_functions()
     for name in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_varlen_workspace_bytes",
                  "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_qk_prologue",
-                 "attn_linear_fwd", "attn_linear_workspace_bytes",
+                 "attn_linear_fwd", "attn_linear_workspace_bytes", "attn_block_list_stride",
+                 "attn_block_route", "attn_block_route_workspace_bytes", "attn_fwd_block_sparse",
+                 "attn_block_skip_use_dense",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -258,3 +266,90 @@ def test_linear_workspace_query(lib):
 def test_linear_validation(lib, kw, code):
     assert linear(lib, **kw) == code
     assert lib.attn_last_error().decode()
+
+
+# ---------------------------------------------------------------- block-skip attention
+SQ, SK, SV, SO, SL, SI, SC, SW = (0x8000000000 * (i + 1) for i in range(8))
+
+
+def route(lib, q=SQ, k=SK, B=1, H=2, N=1000, d=128, scale=0.088, tau=0.1, sink=0, idx=SI, cnt=SC, ws=SW,
+          wsb=None):
+    if wsb is None:
+        wsb = lib.attn_block_route_workspace_bytes(B, H, N, 128)
+    return lib.attn_block_route(q, k, B, H, N, d, scale, tau, sink, idx, cnt, ws, wsb, None)
+
+
+def sparse(lib, q=SQ, k=SK, v=SV, o=SO, lse=SL, idx=SI, cnt=SC, B=1, H=2, N=1000, d=128, scale=0.088):
+    return lib.attn_fwd_block_sparse(q, k, v, o, lse, idx, cnt, B, H, N, d, scale, None)
+
+
+def test_block_list_stride_and_route_workspace(lib):
+    assert lib.attn_block_list_stride(1) == 1 + 8
+    assert lib.attn_block_list_stride(64) == 1 + 8 and lib.attn_block_list_stride(65) == 2 + 8
+    assert lib.attn_block_list_stride(180320) == 2818 + 8
+    assert lib.attn_block_list_stride(0) == 0
+    # pooled query tiles (FP32 [B*H][ceil(N/256)][128], 256-byte aligned), then pooled key tiles
+    a = lambda x: (x + 255) // 256 * 256
+    assert lib.attn_block_route_workspace_bytes(2, 3, 1000, 128) == a(6 * 4 * 512) + 6 * 16 * 512
+    assert lib.attn_block_route_workspace_bytes(1, 2, 1000, 64) == 0
+    assert lib.attn_block_route_workspace_bytes(0, 2, 1000, 128) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(cnt=None), INVALID), (dict(idx=None), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(scale=math.inf), INVALID), (dict(tau=-0.5), INVALID), (dict(tau=math.nan), INVALID),
+    (dict(sink=-1), INVALID),
+    (dict(N=983041), UNSUPPORTED),                                   # more key tiles than routing holds
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(ws=SW + 4), WORKSPACE),
+    (dict(idx=SQ + 64), INVALID),                                    # list over q
+    (dict(cnt=SI + 64), INVALID),                                    # counts inside the lists
+    (dict(ws=SC), INVALID),                                          # workspace over the counts
+])
+def test_route_validation(lib, kw, code):
+    assert route(lib, **kw) == code
+    assert lib.attn_last_error().decode()
+
+
+def test_route_accepts_infinite_tau_on_the_host(lib):
+    # tau = +inf is valid (keeps every tile); with a null stream and fake pointers the call
+    # would launch, so only the validation order is checked: a later error still wins
+    assert route(lib, tau=math.inf, ws=None) == WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(idx=None), INVALID), (dict(cnt=None), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(scale=math.nan), INVALID), (dict(o=SV + 256), INVALID),   # out over v
+    (dict(o=SI), INVALID), (dict(lse=SC), INVALID),                  # outputs over the lists
+])
+def test_block_sparse_validation(lib, kw, code):
+    assert sparse(lib, **kw) == code
+    assert lib.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("step,layer,steps,layers,want", [
+    (0, 7, 2, None, 1), (1, 7, 2, b"", 1), (2, 7, 2, b"", 0), (5, 3, 0, b"3", 1),
+    (5, 3, 0, b"0-2,4", 0), (5, 4, 0, b"0-2,4", 1), (5, 12, 1, b" 0 - 2 , 9-12 ", 1),
+    (5, 13, 1, b"0-2,9-12", 0),
+    (5, 1, 0, b"2-1", INVALID), (5, 1, 0, b"1,", INVALID), (5, 1, 0, b"a", INVALID),
+    (5, 1, 0, b"1;2", INVALID), (5, 1, 0, b"-1", INVALID), (-1, 1, 0, b"", INVALID),
+    (1, -1, 0, b"", INVALID), (1, 1, -2, b"", INVALID), (5, 1, 0, b"99999999999", INVALID),
+])
+def test_dense_guard(lib, step, layer, steps, layers, want):
+    assert lib.attn_block_skip_use_dense(step, layer, steps, layers) == want
+
+
+def test_python_block_skip_guards_without_gpu():
+    import torch
+    import video_diffusion_dit_amd as vd
+    x = torch.zeros((1, 2, 300, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        vd.block_route(x.float(), x, tau=0.1)
+    with pytest.raises(ValueError):
+        vd.block_route(x, x, tau=0.1)                 # CPU tensors
+    with pytest.raises(ValueError):
+        vd.attn_fwd_block_sparse(x, x, x, torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+    assert vd.block_skip_use_dense(0, 0, 1, "") and not vd.block_skip_use_dense(1, 3, 1, "0-2")
+    with pytest.raises(ValueError):
+        vd.block_skip_use_dense(1, 3, 1, "3-")

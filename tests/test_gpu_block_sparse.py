@@ -1,0 +1,198 @@
+"""GPU parity of block-skip attention (attn_block_route + attn_fwd_block_sparse) against the
+FP64 oracle of oracle/block_sparse.py.
+
+Routing: the kept tiles must equal the oracle's except where the oracle's z lies within the
+FP32 decision band around the threshold (oracle.block_sparse.decision_margin), and the lists
+must be well formed (ascending, counted, padded). Attention: the oracle's exact softmax over
+the tiles the GPU kept, with the dense bar (rel-L2 <= 5e-3, max-abs <= 2e-2, |dLSE| <= 1e-3).
+With every tile listed the output must equal the dense kernel's bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.block_sparse import attention_kept, decision_margin, route_blocks
+from workloads import WORKLOADS, make_dense, random_dense
+
+from gpu_util import bits_of, check, dev, dev_i32, f64_of
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def vd():
+    import video_diffusion_dit_amd as m
+    m.load_library()
+    return m
+
+
+def lists_to_keep(kv_idx, kv_cnt, ntk):
+    """[B,H,ntq,stride] / [B,H,ntq] int32 (host) -> keep [B,H,ntq,ntk], after checking that
+    every list is strictly ascending inside [0, ntk) and padded with ntk."""
+    B, H, ntq, stride = kv_idx.shape
+    keep = np.zeros((B, H, ntq, ntk), bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(ntq):
+                c = int(kv_cnt[b, h, i])
+                assert 1 <= c <= ntk
+                row = kv_idx[b, h, i]
+                ids = row[:c]
+                assert np.all(np.diff(ids) > 0) and ids[0] >= 0 and ids[-1] < ntk, (b, h, i, ids)
+                assert np.all(row[c:c + 8] == ntk)
+                keep[b, h, i, ids] = True
+    return keep
+
+
+def check_route(keep_gpu, q, k, tau, sink):
+    keep, z, zmax = route_blocks(q, k, SCALE, tau, sink_tokens=sink)
+    diff = keep_gpu != keep
+    if diff.any():
+        band = np.abs(z - (zmax[..., None] - tau)) <= decision_margin(q, k, SCALE, tau)
+        assert not (diff & ~band).any(), f"{int((diff & ~band).sum())} tiles routed differently outside the band"
+    print(f"[route] tau={tau} sink={sink}: density {keep_gpu.mean():.4f}, "
+          f"{int(diff.sum())} tiles inside the FP32 band differ", flush=True)
+    return keep
+
+
+def route(vd, q, k, tau, sink=0):
+    kv_idx, kv_cnt = vd.block_route(dev(q), dev(k), tau=tau, sink_tokens=sink, scale=SCALE)
+    torch.cuda.synchronize()
+    return kv_idx, kv_cnt
+
+
+@pytest.mark.parametrize("B,H,N,tau,sink", [
+    (2, 3, 1000, 0.0, 0),        # ragged query and key tiles; only the best tile
+    (2, 3, 1000, 0.008, 0),      # z spreads about 0.008 on these inputs
+    (1, 2, 1000, 0.005, 100),    # sink tiles 0 and 1
+    (1, 2, 4096, 0.01, 64),      # whole tiles only
+    (1, 1, 65, 0.01, 0),         # a 1-key last tile
+    (1, 1, 1, 0.0, 0),           # one token
+    (1, 2, 700, math.inf, 0),    # everything kept
+])
+def test_route_and_attention_small(vd, B, H, N, tau, sink):
+    q, k, v = random_dense(B, H, N, seed=N + H)
+    kv_idx, kv_cnt = route(vd, q, k, tau, sink)
+    ntk = -(-N // 64)
+    keep_gpu = lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ntk)
+    check_route(keep_gpu, q, k, tau, sink)
+    if sink:
+        assert keep_gpu[..., :-(-sink // 64)].all()
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_kept(q, k, v, SCALE, keep_gpu)
+    check(f64_of(out), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref,
+          label=f"block-sparse B{B} H{H} N{N} tau={tau} sink={sink}")
+
+
+@pytest.mark.parametrize("B,H,N", [(1, 2, 1000), (2, 1, 4096), (1, 1, 1), (1, 3, 257)])
+def test_every_tile_listed_equals_dense_bits(vd, B, H, N):
+    """tau = inf lists every tile in order: the tile-list loop must then do exactly what the
+    range loop does (the dense kernel without split-KV)."""
+    q, k, v = random_dense(B, H, N, seed=7 * N)
+    kv_idx, kv_cnt = route(vd, q, k, math.inf)
+    assert (kv_cnt.cpu().numpy() == -(-N // 64)).all()
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    ref, lse_ref = vd.attn_fwd(dev(q), dev(k), dev(v), scale=SCALE, return_lse=True, split_kv=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), bits_of(ref))
+    assert np.array_equal(lse.cpu().numpy(), lse_ref.cpu().numpy())
+
+
+def custom_lists(B, H, N, rows_of):
+    """kv_idx/kv_cnt from a function (b, h, query tile) -> list of tile indices; padding ntk."""
+    ntq, ntk = -(-N // 256), -(-N // 64)
+    stride = ntk + 8
+    idx = np.full((B, H, ntq, stride), ntk, np.int32)
+    cnt = np.zeros((B, H, ntq), np.int32)
+    keep = np.zeros((B, H, ntq, ntk), bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(ntq):
+                ids = rows_of(b, h, i, ntk)
+                cnt[b, h, i] = len(ids)
+                idx[b, h, i, :len(ids)] = ids
+                keep[b, h, i, [j for j in ids if 0 <= j < ntk]] = True
+    return idx, cnt, keep
+
+
+@pytest.mark.parametrize("name,rows_of", [
+    ("last tile only", lambda b, h, i, ntk: [ntk - 1]),
+    ("first and last", lambda b, h, i, ntk: [0, ntk - 1]),
+    ("every third", lambda b, h, i, ntk: list(range(i % 3, ntk, 3))),
+    ("two runs", lambda b, h, i, ntk: [0, 1, 2] + list(range(ntk // 2, ntk // 2 + 5))),
+    ("per-head pattern", lambda b, h, i, ntk: list(range(h, ntk, 2 + h))),
+])
+def test_hook_with_caller_lists(vd, name, rows_of):
+    B, H, N = 1, 3, 1500
+    q, k, v = random_dense(B, H, N, seed=31)
+    idx, cnt, keep = custom_lists(B, H, N, rows_of)
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), dev_i32(idx), dev_i32(cnt), scale=SCALE,
+                                        return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_kept(q, k, v, SCALE, keep)
+    check(f64_of(out), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref, label=f"hook: {name}")
+
+
+def test_hook_empty_tile_and_clamped_counts(vd):
+    """kv_cnt <= 0 gives O = 0 and LSE = -inf for that query tile; a count above ntk is read
+    as ntk; other tiles are unaffected."""
+    B, H, N = 1, 2, 600
+    q, k, v = random_dense(B, H, N, seed=41)
+    ntk = -(-N // 64)
+    idx, cnt, keep = custom_lists(B, H, N, lambda b, h, i, n: list(range(n)))
+    cnt[0, 0, 1] = 0
+    cnt[0, 1, 0] = -3
+    cnt[0, 1, 2] = 10 * ntk               # clamped to ntk: all tiles, which the list holds
+    keep[0, 0, 1] = False
+    keep[0, 1, 0] = False
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), dev_i32(idx), dev_i32(cnt), scale=SCALE,
+                                        return_lse=True)
+    torch.cuda.synchronize()
+    o = f64_of(out)
+    l = lse.cpu().numpy()
+    assert np.all(o[0, 0, 256:512] == 0) and np.all(np.isneginf(l[0, 0, 256:512]))
+    assert np.all(o[0, 1, 0:256] == 0) and np.all(np.isneginf(l[0, 1, 0:256]))
+    o_ref, lse_ref = attention_kept(q, k, v, SCALE, keep)
+    live = np.ones((B, H, N), bool)
+    live[0, 0, 256:512] = False
+    live[0, 1, 0:256] = False
+    check(o[live], o_ref[live], l[live].astype(np.float64), lse_ref[live], label="hook with empty tiles")
+
+
+def test_deterministic(vd):
+    q, k, v = random_dense(1, 4, 3000, seed=51)
+    a = vd.block_skip_attention(dev(q), dev(k), dev(v), tau=0.01, sink_tokens=64, scale=SCALE)
+    b = vd.block_skip_attention(dev(q), dev(k), dev(v), tau=0.01, sink_tokens=64, scale=SCALE)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(a), bits_of(b))
+
+
+@pytest.fixture(scope="module")
+def video_720p():
+    return make_dense(WORKLOADS["video_720p"])
+
+
+def test_video_720p_routing_and_sampled_rows(vd, video_720p):
+    """The 720p grid (B=1, H=16, N=180320) at the timed setting tau = 0.02: routing against
+    the oracle over every (head, query tile, key tile), attention on 384 seeded rows plus the
+    last 64 rows of head 15."""
+    q, k, v = video_720p
+    tau = 0.02
+    kv_idx, kv_cnt = route(vd, q, k, tau)
+    N = q.shape[2]
+    ntk = -(-N // 64)
+    keep_gpu = lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ntk)
+    check_route(keep_gpu, q, k, tau, 0)
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(720)
+    rows = np.unique(np.concatenate([rng.choice(16 * N, 384, replace=False), 15 * N + np.arange(N - 64, N)]))
+    o_ref, lse_ref = attention_kept(q, k, v, SCALE, keep_gpu, rows=rows)
+    o = f64_of(out).reshape(-1, 128)[rows]
+    l = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    check(o, o_ref, l, lse_ref, label="block-sparse video_720p tau=0.02 sampled rows")

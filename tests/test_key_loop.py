@@ -1,4 +1,5 @@
-"""CPU checks of the hand-scheduled key loop (csrc/key_loop_gfx950.inc).
+"""CPU checks of the hand-scheduled key loop (csrc/key_loop_gfx950.inc, and its tile-list
+variant csrc/key_loop_idx_gfx950.inc for block-skip attention).
 
 The loop is written by csrc/gen_key_loop.py, which inserts the s_waitcnt and s_nop the
 hardware needs. These tests re-derive those requirements with a separate, simpler scan of the
@@ -31,9 +32,11 @@ def gen():
     return load_gen()
 
 
-@pytest.fixture(scope="module")
-def asm_lines():
-    text = open(os.path.join(CSRC, "key_loop_gfx950.inc")).read()
+FILES = {"range": "key_loop_gfx950.inc", "list": "key_loop_idx_gfx950.inc"}
+
+
+def read_asm(name):
+    text = open(os.path.join(CSRC, name)).read()
     out = []
     for line in text.splitlines():
         m = re.match(r'\s*"(.*)\\n"\s*$', line)
@@ -42,8 +45,14 @@ def asm_lines():
     return out
 
 
-def test_committed_file_is_generated(gen):
+@pytest.fixture(scope="module", params=sorted(FILES))
+def asm_lines(request):
+    return read_asm(FILES[request.param])
+
+
+def test_committed_files_are_generated(gen):
     assert open(gen.OUT).read() == gen.render()
+    assert open(gen.OUT_IDX).read() == gen.render(True)
 
 
 def regs(tok):
@@ -169,12 +178,14 @@ def test_control_flow_and_registers(gen, asm_lines):
             assert m.group(2) in labels, line
     # one barrier in the set-up and one per tile of the four-tile loop body; none elsewhere
     assert sum(1 for l in asm_lines if l == "s_barrier") == 5
-    # registers named stay inside what the asm statement declares (v0..v199, a0..a191)
+    # registers named stay inside what the asm statement declares (v0..v199, a0..a191; the
+    # tile-list variant also v200, v201)
+    nv = gen.V_ZERO + 1 if any(l.startswith("global_load_dword v200") for l in asm_lines) else gen.NV
     for line in asm_lines:
         _, ops = parse(line)
         for t in ops:
             for kind, i in regs(t):
-                assert (kind == "v" and i < gen.NV) or (kind == "a" and i < gen.NA), line
+                assert (kind == "v" and i < nv) or (kind == "a" and i < gen.NA), line
     # every return address points at a label that follows its call
     calls = [l for l in asm_lines if l.startswith("s_add_u32 s54")]
     assert len(calls) == 9 and all(re.search(r"\.Lok\w+_%=-\.Lpc\w+_%=", c) for c in calls)
@@ -192,3 +203,58 @@ def test_loop_schedule_shape(gen):
     assert sum(l.startswith("buffer_load_dwordx4") for l in body) == 4 * 8
     nops = sum(int(l.split()[1]) + 1 for l in body if l.startswith("s_nop"))
     assert nops < 64, nops   # the schedule keeps hazards apart by itself
+
+
+def test_tile_list_index_flow(gen):
+    """Tile-list variant: every index read (v_readfirstlane of v200) follows an s_waitcnt
+    vmcnt(0) issued after the load that wrote v200; the set-up's scalar list load is waited
+    for before its registers are read; every index is clamped to [current, ntk] before the
+    cursors move by it; per loop tile exactly one index read and one index load."""
+    lines = read_asm(FILES["list"])
+    loaded = False
+    smem = False
+    for line in lines:
+        if line.startswith("global_load_dword v200"):
+            loaded = True
+        if line.startswith("s_waitcnt") and "vmcnt(0)" in line:
+            loaded = False
+        if line.startswith("v_readfirstlane_b32 s69, v200"):
+            assert not loaded, "index read before its load completed"
+        if line.startswith("s_load_dwordx4 s[64:67]"):
+            smem = True
+        if line.startswith("s_waitcnt") and "lgkmcnt(0)" in line:
+            smem = False
+        if smem:
+            _, ops = parse(line)
+            assert not any(re.fullmatch(r"s6[4-7]", o) for o in ops), line
+    # the byte step is computed from a clamped index: s_max, s_min, s_sub, s_mul in a row
+    for i, line in enumerate(lines):
+        if line.startswith("s_sub_i32 s70"):
+            nxt = parse(line)[1][1]
+            assert lines[i - 2] == "s_max_i32 %s, %s, s68" % (nxt, nxt), lines[i - 2]
+            assert lines[i - 1] == "s_min_i32 %s, %s, s71" % (nxt, nxt), lines[i - 1]
+            assert lines[i + 1] == "s_mul_i32 s70, s70, %[tb]" and lines[i + 2] == "s_mov_b32 s68, %s" % nxt
+    start = lines.index(".Lloop_%=:")
+    end = lines.index("s_branch .Lloop_%=")
+    body = lines[start:end]
+    assert sum(l.startswith("v_readfirstlane_b32 s69, v200") for l in body) == 4
+    assert sum(l.startswith("global_load_dword v200") for l in body) == 4
+    assert sum(l.startswith("s_sub_i32 s70") for l in lines) == 3 + 4   # set-up tiles 1..3, loop tiles
+    # cursor moves use the clamped step only
+    assert not any("%[tb]" in l and l.startswith(("s_add_u32 s40", "s_add_u32 s44")) for l in lines)
+
+
+def test_tile_list_variant_differs_only_in_tile_movement():
+    """Apart from the index bookkeeping, the two loops hold the same instructions (the extra
+    index read shifts where the loads fall between MFMAs) with the MFMAs in the same order."""
+    rng, lst = read_asm(FILES["range"]), read_asm(FILES["list"])
+    book = re.compile(r"^(s_max_i32 s6[4-9]|s_min_i32 s6[4-9]|s_sub_i32 s70|s_mul_i32 s70|s_mov_b32 s6[2389]|"
+                      r"s_mov_b32 s71|s_load_dwordx4|s_add_u32 s62|s_addc_u32 s63|global_load_dword v200|"
+                      r"v_readfirstlane_b32 s69|v_mov_b32 v201|s_waitcnt lgkmcnt\(0\)$|s_nop)")
+    norm = lambda xs: [re.sub(r"s70|%\[tb\]", "STEP", l) for l in xs if not book.match(l)]
+    a = [l for l in norm(rng) if not l.startswith("s_waitcnt lgkmcnt(0)")]
+    b = [l for l in norm(lst) if not l.startswith("s_waitcnt lgkmcnt(0)")]
+    assert sorted(a) == sorted(b)
+    assert [l for l in a if l.startswith("v_mfma")] == [l for l in b if l.startswith("v_mfma")]
+    labels = lambda xs: [l for l in xs if l.endswith(":") or l.startswith(("s_branch", "s_cbranch", "s_barrier"))]
+    assert labels(a) == labels(b)

@@ -80,6 +80,16 @@ def load_library() -> ctypes.CDLL:
         lib.attn_linear_fwd.restype = i32
         lib.attn_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.attn_linear_workspace_bytes.restype = sz
+        lib.attn_block_list_stride.argtypes = [i32]
+        lib.attn_block_list_stride.restype = i32
+        lib.attn_block_route_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.attn_block_route_workspace_bytes.restype = sz
+        lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+        lib.attn_block_route.restype = i32
+        lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        lib.attn_fwd_block_sparse.restype = i32
+        lib.attn_block_skip_use_dense.argtypes = [i32, i32, i32, ctypes.c_char_p]
+        lib.attn_block_skip_use_dense.restype = i32
         _lib = lib
         return lib
 
@@ -340,3 +350,90 @@ def linear_attention(q: torch.Tensor, k: torch.Tensor, q_rot: torch.Tensor, k_ro
                              float(eps), _ptr(ws), need, _stream_handle(q.device))
     _raise_for(lib, st)
     return out
+
+
+# ---------------------------------------------------------------- block-skip attention
+# Page "PR #33702 report" (the Sol-Attn backend): KV blocks routed by a threshold tau, sink
+# tokens kept, a dense guard over denoising steps and layers. Query tiles are 256 rows, key
+# tiles 64 keys; the routing rule is stated in include/attn.h (attn_block_route).
+
+def block_list_stride(N: int) -> int:
+    """Row stride (entries) of the kv_idx lists for N tokens: ceil(N/64) + 8."""
+    return int(load_library().attn_block_list_stride(N))
+
+
+def _list_shapes(B: int, H: int, N: int):
+    ntq = -(-N // 256)
+    return (B, H, ntq, block_list_stride(N)), (B, H, ntq)
+
+
+def block_route(q: torch.Tensor, k: torch.Tensor, *, tau: float, sink_tokens: int = 0,
+                scale: float | None = None):
+    """Key-tile lists of block-skip attention for dense BF16 [B, H, N, 128] q and k.
+
+    Returns (kv_idx int32 [B, H, ntq, stride], kv_cnt int32 [B, H, ntq]) on q's device,
+    written on the current stream (see attn_block_route for the rule)."""
+    _check_tensors(q, k, k, 4)
+    B, H, N, d = q.shape
+    if d != 128:
+        raise ValueError(f"head dimension {d} is not supported (only 128)")
+    lib = load_library()
+    idx_shape, cnt_shape = _list_shapes(B, H, N)
+    kv_idx = torch.empty(idx_shape, dtype=torch.int32, device=q.device)
+    kv_cnt = torch.empty(cnt_shape, dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        nbytes = int(lib.attn_block_route_workspace_bytes(B, H, N, d))
+        ws = _workspace(q.device, nbytes)
+        st = lib.attn_block_route(_ptr(q), _ptr(k), B, H, N, d, _default_scale(d, scale), float(tau),
+                                  int(sink_tokens), _ptr(kv_idx), _ptr(kv_cnt), _ptr(ws), ws.numel(),
+                                  _stream_handle(q.device))
+    _raise_for(lib, st)
+    return kv_idx, kv_cnt
+
+
+def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
+                          kv_cnt: torch.Tensor, scale: float | None = None, return_lse: bool = False,
+                          out: torch.Tensor | None = None):
+    """Attention of dense BF16 [B, H, N, 128] q, k, v where query tile I of (b, h) sees only
+    the key tiles kv_idx[b, h, I, :kv_cnt[b, h, I]] (int32 device tensors shaped as
+    block_route returns them; the caller's own lists are accepted: this is the hook)."""
+    _check_tensors(q, k, v, 4)
+    B, H, N, d = q.shape
+    if d != 128:
+        raise ValueError(f"head dimension {d} is not supported (only 128)")
+    idx_shape, cnt_shape = _list_shapes(B, H, N)
+    for name, t, shape in (("kv_idx", kv_idx, idx_shape), ("kv_cnt", kv_cnt, cnt_shape)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be an int32 tensor of shape {shape}")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on q's device")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(kv_idx),
+                                       _ptr(kv_cnt), B, H, N, d, _default_scale(d, scale),
+                                       _stream_handle(q.device))
+    _raise_for(lib, st)
+    return (out, lse) if return_lse else out
+
+
+def block_skip_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tau: float,
+                         sink_tokens: int = 0, scale: float | None = None, return_lse: bool = False):
+    """block_route, then attn_fwd_block_sparse over its lists."""
+    kv_idx, kv_cnt = block_route(q, k, tau=tau, sink_tokens=sink_tokens, scale=scale)
+    return attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=scale, return_lse=return_lse)
+
+
+def block_skip_use_dense(step: int, layer: int, dense_steps: int = 0, dense_layers: str | None = None) -> bool:
+    """The dense guard: True when denoising step `step` of layer `layer` runs dense
+    attention (step < dense_steps, or layer in the "a-b,c" list dense_layers)."""
+    lib = load_library()
+    text = None if dense_layers is None else str(dense_layers).encode()
+    st = lib.attn_block_skip_use_dense(int(step), int(layer), int(dense_steps), text)
+    if st < 0:
+        _raise_for(lib, st)
+    return bool(st)

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattn.so")
-SOURCES = ["attn_fwd_gfx950.hip", "prologue_gfx950.hip", "linear_gfx950.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_gfx950.hip", "block_route_gfx950.hip", "prologue_gfx950.hip", "linear_gfx950.hip",
+           "attn_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
@@ -33,18 +34,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def write_key_loop() -> str:
-    """Regenerate csrc/key_loop_gfx950.inc (the hand-scheduled key loop) from its generator."""
+def write_key_loop() -> list:
+    """Regenerate csrc/key_loop_gfx950.inc and csrc/key_loop_idx_gfx950.inc (the
+    hand-scheduled key loop over a tile range and over a tile list) from their generator."""
     import importlib.util
     spec = importlib.util.spec_from_file_location("gen_key_loop", os.path.join(CSRC, "gen_key_loop.py"))
     gen = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(gen)
-    text = gen.render()
-    old = open(gen.OUT).read() if os.path.exists(gen.OUT) else None
-    if text != old:
-        with open(gen.OUT, "w") as f:
-            f.write(text)
-    return gen.OUT
+    for path, indexed in ((gen.OUT, False), (gen.OUT_IDX, True)):
+        text = gen.render(indexed)
+        old = open(path).read() if os.path.exists(path) else None
+        if text != old:
+            with open(path, "w") as f:
+                f.write(text)
+    return [gen.OUT, gen.OUT_IDX]
 
 
 def build(verbose: bool = False) -> str:

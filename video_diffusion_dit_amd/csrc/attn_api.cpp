@@ -187,6 +187,119 @@ int attn_linear_fwd(const void* q, const void* k, const void* q_rot, const void*
                                                static_cast<hipStream_t>(stream)));
 }
 
+int attn_block_list_stride(int N) { return N > 0 ? attn_impl::block_list_stride(N) : 0; }
+
+size_t attn_block_route_workspace_bytes(int B, int H, int N, int d) {
+    if (B <= 0 || H <= 0 || N <= 0 || d != 128) return 0;
+    if (product(B, H, N, d) < 0) return 0;
+    return attn_impl::route_workspace_bytes(B, H, N);
+}
+
+int attn_block_route(const void* q, const void* k, int B, int H, int N, int d, float scale, float tau,
+                     int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (q == nullptr || k == nullptr || kv_idx == nullptr || kv_cnt == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, kv_idx and kv_cnt must be non-null device pointers");
+    if (B <= 0 || H <= 0 || N <= 0) return fail(ATTN_ERR_INVALID_ARG, "B, H and N must be >= 1");
+    if (d <= 0) return fail(ATTN_ERR_INVALID_ARG, "d must be >= 1");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (isnan(tau) || tau < 0.f) return fail(ATTN_ERR_INVALID_ARG, "tau must be >= 0 (+inf keeps every key tile)");
+    if (sink_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "sink_tokens must be >= 0");
+    const long long elems = product(B, H, N, d);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const int ntk = (N + attn_impl::tile_keys() - 1) / attn_impl::tile_keys();
+    if (ntk > attn_impl::route_max_tiles())
+        return fail(ATTN_ERR_UNSUPPORTED, "sequence longer than the routing supports (route_max_tiles key tiles)");
+    const long long items = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
+    if (items < 0 || items > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    const size_t need = attn_impl::route_workspace_bytes(B, H, N);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_block_route_workspace_bytes()");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const size_t tb = (size_t)elems * 2;
+    const size_t idx_bytes = (size_t)items * attn_impl::block_list_stride(N) * 4, cnt_bytes = (size_t)items * 4;
+    const void* outs[3] = {kv_idx, kv_cnt, workspace};
+    const size_t outb[3] = {idx_bytes, cnt_bytes, need};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], outb[i], q, tb) || overlaps(outs[i], outb[i], k, tb))
+            return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt or workspace overlaps q or k");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outb[i], outs[j], outb[j]))
+                return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt and workspace must not overlap");
+    }
+    return hip_status(attn_impl::launch_block_route(q, k, B, H, N, scale, tau, sink_tokens, kv_idx, kv_cnt,
+                                                    workspace, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N, int d,
+                          float scale, void* stream) {
+    g_last_error[0] = '\0';
+    int st = check_common(q, k, v, out, H, d, scale);
+    if (st != ATTN_OK) return st;
+    if (kv_idx == nullptr || kv_cnt == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "kv_idx and kv_cnt must be non-null device pointers");
+    if (B <= 0 || N <= 0) return fail(ATTN_ERR_INVALID_ARG, "B and N must be >= 1");
+    const long long elems = product(B, H, N, d);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    const long long items = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
+    if (items < 0 || items > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    const size_t tb = (size_t)elems * 2, lb = (size_t)product(B, H, N, 1) * 4;
+    st = check_aliasing(q, k, v, out, lse, tb, lb);
+    if (st != ATTN_OK) return st;
+    const size_t idx_bytes = (size_t)items * attn_impl::block_list_stride(N) * 4, cnt_bytes = (size_t)items * 4;
+    if (overlaps(out, tb, kv_idx, idx_bytes) || overlaps(out, tb, kv_cnt, cnt_bytes) ||
+        overlaps(lse, lb, kv_idx, idx_bytes) || overlaps(lse, lb, kv_cnt, cnt_bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx or kv_cnt");
+    return hip_status(attn_impl::launch_block_sparse(q, k, v, out, lse, kv_idx, kv_cnt, B, H, N, scale,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+int attn_block_skip_use_dense(int step, int layer, int dense_steps, const char* dense_layers) {
+    g_last_error[0] = '\0';
+    if (step < 0 || layer < 0 || dense_steps < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "step, layer and dense_steps must be >= 0");
+    bool dense = step < dense_steps;
+    // dense_layers: comma-separated items "a" or "a-b" (inclusive, a <= b), blanks allowed
+    const char* p = dense_layers != nullptr ? dense_layers : "";
+    auto blank = [](char c) { return c == ' ' || c == '\t'; };
+    auto number = [&](long& out) {
+        while (blank(*p)) ++p;
+        if (*p < '0' || *p > '9') return false;
+        long v = 0;
+        while (*p >= '0' && *p <= '9') {
+            v = v * 10 + (*p - '0');
+            if (v > INT_MAX) return false;
+            ++p;
+        }
+        while (blank(*p)) ++p;
+        out = v;
+        return true;
+    };
+    while (blank(*p)) ++p;
+    while (*p != '\0') {
+        long a, b;
+        if (!number(a)) return fail(ATTN_ERR_INVALID_ARG, "dense_layers: expected a layer number");
+        b = a;
+        if (*p == '-') {
+            ++p;
+            if (!number(b) || b < a) return fail(ATTN_ERR_INVALID_ARG, "dense_layers: bad range");
+        }
+        if (layer >= a && layer <= b) dense = true;
+        if (*p == ',') {
+            ++p;
+            while (blank(*p)) ++p;
+            if (*p == '\0') return fail(ATTN_ERR_INVALID_ARG, "dense_layers: trailing comma");
+        } else if (*p != '\0') {
+            return fail(ATTN_ERR_INVALID_ARG, "dense_layers: unexpected character");
+        }
+    }
+    return dense ? 1 : 0;
+}
+
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
     if (nseg <= 0 || H <= 0 || total_tokens < 0) return 0;
     return attn_impl::varlen_workspace_bytes(nseg, total_tokens);

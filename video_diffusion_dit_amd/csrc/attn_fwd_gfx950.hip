@@ -98,10 +98,15 @@ constexpr size_t PART_BYTES = sizeof(float) * PART_STRIDE * BM;   // one workgro
 // LSE) get the final rows; otherwise the workgroup's unnormalised O, m_ref and l go to part
 // (PART_STRIDE floats per row) for a later merge. Rows past n are computed on row n-1 and
 // not written. Every thread of the workgroup must call this (the key loop has barriers).
+// LIST: the key tiles are the kt1 entries of klist (ascending tile indices, readable 8
+// entries past kt1; kt0 is unused); the tile-list key loop clamps every entry to
+// [previous entry, ntk], so loads stay inside the sequence whatever the list holds.
+template <bool LIST>
 __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                           const bf16* __restrict__ V, bf16* __restrict__ O,
                                           float* __restrict__ LSE, long rs, int n, int q0, float c,
-                                          int kt0, int kt1, float* __restrict__ part) {
+                                          int kt0, int kt1, float* __restrict__ part,
+                                          const int32_t* __restrict__ klist = nullptr) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -138,9 +143,17 @@ __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16
     }
     const unsigned ldsw = sbase + 4096u * w;
     const int tb = (int)(BN * rs_bytes);
-    const int ntile = kt1 - kt0;
-    // Buffer resources start at tile kt0 and end at the sequence end.
-    const long skip = (long)kt0 * BN * rs_bytes;
+    const int ntile = LIST ? kt1 : kt1 - kt0;
+    [[maybe_unused]] const int ntk = (n + BN - 1) / BN;
+    int first = kt0, last = kt1 - 1;
+    if constexpr (LIST) {
+        first = min(max(klist[0], 0), ntk - 1);
+        last = min(max(klist[kt1 - 1], first), ntk - 1);
+    }
+    [[maybe_unused]] const int idx0 = first;
+    [[maybe_unused]] const unsigned lp[2] = {(unsigned)(uintptr_t)klist, (unsigned)((uint64_t)(uintptr_t)klist >> 32)};
+    // Buffer resources start at the first tile and end at the sequence end.
+    const long skip = (long)first * BN * rs_bytes;
     const long left = (long)n * rs_bytes - skip;
     const int nbytes = left > 0x7fffffffL ? 0x7fffffff : (left < 0 ? 0 : (int)left);
     const uint64_t kbase = (uint64_t)(uintptr_t)K + skip, vbase = (uint64_t)(uintptr_t)V + skip;
@@ -148,7 +161,7 @@ __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16
     const unsigned rv[4] = {(unsigned)vbase, (unsigned)(vbase >> 32) & 0xffffu, (unsigned)nbytes, (unsigned)BUF_FLAGS};
     // Keys of the last tile of the range at or past n are masked: key 32kb + 16(r/8) + 8g + r%8
     // of S register r is valid while 32kb + 16(r/8) + r%8 < klim.
-    const int valid = min(BN, n - (kt1 - 1) * BN);
+    const int valid = min(BN, n - last * BN);
     const int klim = valid - 8 * g;
     int qrow[2];
     uint64_t qa[2];
@@ -161,7 +174,11 @@ __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16
     const int bperm = (lane ^ 32) << 2;
     f32x16 o[4][2];
     float mref[2], lsum[2];
+    if constexpr (LIST) {
+#include "key_loop_idx_gfx950.inc"
+    } else {
 #include "key_loop_gfx950.inc"
+    }
 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -215,8 +232,42 @@ struct DenseArgs {
 __global__ __launch_bounds__(NT, 1) void attn_fwd_dense_kernel(DenseArgs a) {
     const int bh = blockIdx.x / a.ntq, qt = blockIdx.x - bh * a.ntq;
     const long base = (long)bh * a.N * D;
-    attn_rows(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)bh * a.N : nullptr,
-              D, a.N, qt * BM, a.c, 0, (a.N + BN - 1) / BN, nullptr);
+    attn_rows<false>(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)bh * a.N : nullptr,
+                     D, a.N, qt * BM, a.c, 0, (a.N + BN - 1) / BN, nullptr);
+}
+
+// Block-skip attention over caller-given key-tile lists: workgroup = (b*H + h) * ntq + query
+// tile, its kv_cnt entry gives how many tiles of its kv_idx row (stride entries) it attends
+// to. A tile with no keys gets O = 0 and LSE = -inf (softmax over an empty set).
+struct SparseArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    bf16* o;
+    float* lse;
+    const int32_t* kidx;
+    const int32_t* kcnt;
+    int N, ntq, ntk, stride;
+    float c;
+};
+
+__global__ __launch_bounds__(NT, 1) void attn_fwd_block_sparse_kernel(SparseArgs a) {
+    const int item = blockIdx.x;
+    const int bh = item / a.ntq, qt = item - bh * a.ntq;
+    const long base = (long)bh * a.N * D;
+    const int cnt = min(a.kcnt[item], a.ntk);
+    if (cnt <= 0) {
+        const int row = qt * BM + (int)threadIdx.x;
+        if (row < a.N) {
+            uint4* orow = reinterpret_cast<uint4*>(a.o + base + (long)row * D);
+#pragma unroll
+            for (int i = 0; i < D / 8; ++i) orow[i] = make_uint4(0, 0, 0, 0);
+            if (a.lse != nullptr) a.lse[(long)bh * a.N + row] = -INFINITY;
+        }
+        return;
+    }
+    attn_rows<true>(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)bh * a.N : nullptr,
+                    D, a.N, qt * BM, a.c, 0, cnt, nullptr, a.kidx + (long)item * a.stride);
 }
 
 // Split-KV launch (see attn_impl::split_plan): the plain kernel takes whole query tiles
@@ -249,8 +300,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_dense_split_kernel(DenseArgs a
         float* part = nullptr;
         if (t0 != 0 || t1 != sp.ntk) part = sp.part + (size_t)(2 * g + (i == i0 ? 0 : 1)) * (PART_BYTES / sizeof(float));
         if (i != i0) __syncthreads();   // the previous piece's waves are done with LDS
-        attn_rows(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)bh * a.N : nullptr,
-                  D, a.N, qt * BM, a.c, (int)t0, (int)t1, part);
+        attn_rows<false>(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)bh * a.N : nullptr,
+                         D, a.N, qt * BM, a.c, (int)t0, (int)t1, part);
     }
 }
 
@@ -387,8 +438,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_varlen_kernel(VarlenArgs a) {
     const int n = seg_len(a.cu, t.x, a.T);
     if (t.y * BM >= n) return;
     const long base = ((long)start * a.H + h) * D;
-    attn_rows(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)h * a.T + start : nullptr,
-              (long)a.H * D, n, t.y * BM, a.c, 0, (n + BN - 1) / BN, nullptr);
+    attn_rows<false>(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)h * a.T + start : nullptr,
+                     (long)a.H * D, n, t.y * BM, a.c, 0, (n + BN - 1) / BN, nullptr);
 }
 
 inline float log2e_scale(float scale) { return (float)((double)scale * 1.4426950408889634074); }
@@ -478,6 +529,29 @@ hipError_t launch_dense_split(const void* q, const void* k, const void* v, void*
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(p.R * 16)), dim3(256), 0, stream, a, sp);
+    return hipGetLastError();
+}
+
+int block_list_stride(int N) { return (N + BN - 1) / BN + 8; }
+
+hipError_t launch_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                               const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N,
+                               float scale, hipStream_t stream) {
+    SparseArgs a;
+    a.q = static_cast<const bf16*>(q);
+    a.k = static_cast<const bf16*>(k);
+    a.v = static_cast<const bf16*>(v);
+    a.o = static_cast<bf16*>(out);
+    a.lse = lse;
+    a.kidx = kv_idx;
+    a.kcnt = kv_cnt;
+    a.N = N;
+    a.ntq = (N + BM - 1) / BM;
+    a.ntk = (N + BN - 1) / BN;
+    a.stride = block_list_stride(N);
+    a.c = log2e_scale(scale);
+    const long grid = (long)B * H * a.ntq;
+    hipLaunchKernelGGL(attn_fwd_block_sparse_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -31,6 +31,21 @@ hipError_t launch_dense_split(const void* q, const void* k, const void* v, void*
                               int B, int H, int N, float scale, const SplitPlan& p, void* workspace,
                               hipStream_t stream);
 
+// Block-skip attention. Key-tile lists: kv_idx [B*H*ntq][block_list_stride(N)] int32,
+// kv_cnt [B*H*ntq]; item (b*H + h)*ntq + query tile.
+int block_list_stride(int N);
+hipError_t launch_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                               const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N,
+                               float scale, hipStream_t stream);
+// Routing of block-skip attention into those lists (block_route_gfx950.hip); workspace holds
+// the pooled query and key tiles (route_workspace_bytes, 256-byte aligned); at most
+// route_max_tiles() key tiles per sequence.
+size_t route_workspace_bytes(int B, int H, int N);
+int route_max_tiles();
+hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N, float scale, float tau,
+                              int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                              hipStream_t stream);
+
 // Workspace layout of the varlen schedule (bytes).
 size_t varlen_workspace_bytes(int nseg, int total_tokens);
 

@@ -1,0 +1,219 @@
+// Key-block routing of block-skip attention for gfx950: for every query tile of 256 rows,
+// the list of the 64-key tiles its rows attend to.
+//
+// Method: page "PR #33702 report" (the Sol-Attn backend for MiniMax-H3), motivation and
+// breakdown: KV blocks are routed by a threshold (knob tau) so that the attention skips most
+// of them, without building a full proxy score map; sink tokens stay in. The page gives no
+// formula; the rule taken here:
+//   qbar_I = mean of the valid query rows of tile I, kbar_J = mean of the valid keys of tile J
+//   z_IJ   = scale * qbar_I . kbar_J
+//   keep J for I  iff  z_IJ >= max_J' z_IJ' - tau  or  J*64 < sink_tokens
+// Only the per-tile lists leave the chip (the z of a tile row live in LDS), in the layout the
+// block-sparse attention kernel reads: kv_idx[item][stride] ascending tile indices and
+// kv_cnt[item], item = (b*H + h)*ntq + I, stride = ntk + 8; the 8 entries after the count
+// hold ntk.
+//
+// Kernels (HBM-bound pooling, then L2-resident routing):
+//   pool_kernel<RB>: one workgroup per 256 rows of one (b, h); thread (row lane rl, 16-byte
+//     chunk ch) sums rows rl, rl+16, ... of each RB-row block in FP32, the 16 row lanes are
+//     added in order through LDS, and the sum is divided by the block's valid rows.
+//   route_kernel<QPW>: one workgroup per QPW query tiles of one (b, h); thread J computes the
+//     QPW proxies of key tile J (128-term FP32 dot products) into LDS; then per query tile a
+//     block-wide max, the threshold, and an ordered compaction (each thread owns a contiguous
+//     run of tiles; a wave-level scan of the run counts gives the write offsets).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace {
+
+typedef __bf16 bf16;
+
+constexpr int D = 128;
+constexpr int BMQ = 256;   // query rows per tile (the attention kernel's workgroup rows)
+constexpr int BNK = 64;    // keys per tile (the attention kernel's key tile)
+constexpr int LIST_PAD = 8;
+constexpr int ROUTE_LDS_LIMIT = 61440;   // bytes of proxies a workgroup keeps in LDS
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int RB>
+__global__ __launch_bounds__(256) void pool_kernel(const bf16* __restrict__ x, float* __restrict__ out, int N,
+                                                   int nblk) {
+    constexpr int NB = 256 / RB;    // pooled blocks per workgroup
+    constexpr int PER = RB / 16;    // rows per thread and block
+    __shared__ float red[16][NB][D];
+    const int wpb = (N + 255) / 256;
+    const int bh = blockIdx.x / wpb, w = blockIdx.x - bh * wpb;
+    const int tid = threadIdx.x, ch = tid & 15, rl = tid >> 4;
+    const bf16* xb = x + (long)bh * N * D;
+    for (int b = 0; b < NB; ++b) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int i = 0; i < PER; ++i) {
+            const int r = w * 256 + b * RB + rl + 16 * i;
+            if (r < N) {
+                const uint4 u = *reinterpret_cast<const uint4*>(xb + (long)r * D + 8 * ch);
+                acc[0] += bf16_lo(u.x);
+                acc[1] += bf16_hi(u.x);
+                acc[2] += bf16_lo(u.y);
+                acc[3] += bf16_hi(u.y);
+                acc[4] += bf16_lo(u.z);
+                acc[5] += bf16_hi(u.z);
+                acc[6] += bf16_lo(u.w);
+                acc[7] += bf16_hi(u.w);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[rl][b][8 * ch + e] = acc[e];
+    }
+    __syncthreads();
+    for (int t = tid; t < NB * D; t += 256) {
+        const int b = t / D, c = t - b * D;
+        const int blk = w * NB + b;
+        const int rows = min(RB, N - blk * RB);
+        if (rows <= 0) continue;
+        float s = 0.f;
+        for (int j = 0; j < 16; ++j) s += red[j][b][c];
+        out[((long)bh * nblk + blk) * D + c] = s / (float)rows;
+    }
+}
+
+struct RouteArgs {
+    const float* qbar;   // [BH][ntq][128]
+    const float* kbar;   // [BH][ntk][128]
+    int32_t* kidx;
+    int32_t* kcnt;
+    int ntq, ntk, stride, nsink;
+    float scale, tau;
+};
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    const int tid = threadIdx.x;
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <int QPW>
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+    extern __shared__ float zs[];   // [QPW][ntk]
+    __shared__ float qs[QPW][D];
+    __shared__ float red[4];
+    __shared__ int wsum[4];
+    const int gpb = (a.ntq + QPW - 1) / QPW;
+    const int bh = blockIdx.x / gpb, g = blockIdx.x - bh * gpb;
+    const int qt0 = g * QPW, nq = min(QPW, a.ntq - qt0);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int t = tid; t < QPW * D; t += 256) {
+        const int qi = t / D;
+        qs[qi][t - qi * D] = qi < nq ? a.qbar[((long)bh * a.ntq + qt0 + qi) * D + (t - qi * D)] : 0.f;
+    }
+    __syncthreads();
+    const float* kb = a.kbar + (long)bh * a.ntk * D;
+    for (int J = tid; J < a.ntk; J += 256) {
+        float z[QPW];
+#pragma unroll
+        for (int qi = 0; qi < QPW; ++qi) z[qi] = 0.f;
+        const float4* kr = reinterpret_cast<const float4*>(kb + (long)J * D);
+#pragma unroll 4
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+            const float4 kv = kr[c4];
+#pragma unroll
+            for (int qi = 0; qi < QPW; ++qi) {
+                z[qi] = fmaf(qs[qi][4 * c4 + 0], kv.x, z[qi]);
+                z[qi] = fmaf(qs[qi][4 * c4 + 1], kv.y, z[qi]);
+                z[qi] = fmaf(qs[qi][4 * c4 + 2], kv.z, z[qi]);
+                z[qi] = fmaf(qs[qi][4 * c4 + 3], kv.w, z[qi]);
+            }
+        }
+#pragma unroll
+        for (int qi = 0; qi < QPW; ++qi) zs[qi * a.ntk + J] = z[qi] * a.scale;
+    }
+    __syncthreads();
+    const int run = (a.ntk + 255) / 256;
+    const int j0 = min(tid * run, a.ntk), j1 = min(j0 + run, a.ntk);
+    for (int qi = 0; qi < nq; ++qi) {
+        const float* z = zs + qi * a.ntk;
+        float m = -INFINITY;
+        for (int J = tid; J < a.ntk; J += 256) m = fmaxf(m, z[J]);
+        const float thr = block_max(m, red) - a.tau;
+        int cnt = 0;
+        for (int J = j0; J < j1; ++J) cnt += (z[J] >= thr || J < a.nsink) ? 1 : 0;
+        // exclusive prefix of the run counts: within the wave, then across the 4 waves
+        int incl = cnt;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        int off = incl - cnt;
+        for (int k = 0; k < wv; ++k) off += wsum[k];
+        const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        const long item = (long)bh * a.ntq + qt0 + qi;
+        int32_t* dst = a.kidx + item * a.stride;
+        for (int J = j0; J < j1; ++J)
+            if (z[J] >= thr || J < a.nsink) dst[off++] = J;
+        if (tid < LIST_PAD) dst[total + tid] = a.ntk;
+        if (tid == 0) a.kcnt[item] = total;
+        __syncthreads();   // wsum and red are reused by the next query tile
+    }
+}
+
+}  // namespace
+
+namespace attn_impl {
+
+size_t route_workspace_bytes(int B, int H, int N) {
+    const size_t bh = (size_t)B * H;
+    const size_t ntq = (size_t)(N + BMQ - 1) / BMQ, ntk = (size_t)(N + BNK - 1) / BNK;
+    const size_t qb = (bh * ntq * D * sizeof(float) + 255) & ~size_t(255);
+    return qb + bh * ntk * D * sizeof(float);
+}
+
+int route_max_tiles() { return ROUTE_LDS_LIMIT / (int)sizeof(float); }
+
+hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N, float scale, float tau,
+                              int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                              hipStream_t stream) {
+    const long bh = (long)B * H;
+    const int ntq = (N + BMQ - 1) / BMQ, ntk = (N + BNK - 1) / BNK;
+    float* qbar = static_cast<float*>(workspace);
+    const size_t qb = ((size_t)bh * ntq * D * sizeof(float) + 255) & ~size_t(255);
+    float* kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + qb);
+    const unsigned pool_grid = (unsigned)(bh * ((N + 255) / 256));
+    hipLaunchKernelGGL(pool_kernel<BMQ>, dim3(pool_grid), dim3(256), 0, stream, static_cast<const bf16*>(q), qbar,
+                       N, ntq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pool_kernel<BNK>, dim3(pool_grid), dim3(256), 0, stream, static_cast<const bf16*>(k), kbar,
+                       N, ntk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    RouteArgs a;
+    a.qbar = qbar;
+    a.kbar = kbar;
+    a.kidx = kv_idx;
+    a.kcnt = kv_cnt;
+    a.ntq = ntq;
+    a.ntk = ntk;
+    a.stride = ntk + LIST_PAD;
+    a.nsink = sink_tokens > 0 ? (int)(((long)sink_tokens + BNK - 1) / BNK) : 0;
+    a.scale = scale;
+    a.tau = tau;
+    if (4 * ntk * (int)sizeof(float) <= ROUTE_LDS_LIMIT) {
+        const size_t lds = (size_t)4 * ntk * sizeof(float);
+        hipLaunchKernelGGL(route_kernel<4>, dim3((unsigned)(bh * ((ntq + 3) / 4))), dim3(256), lds, stream, a);
+    } else {
+        const size_t lds = (size_t)ntk * sizeof(float);
+        hipLaunchKernelGGL(route_kernel<1>, dim3((unsigned)(bh * ntq)), dim3(256), lds, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace attn_impl

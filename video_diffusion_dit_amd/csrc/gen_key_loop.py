@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
-"""Writes key_loop_gfx950.inc: the key loop of the attention forward kernel for gfx950, as one
-inline-asm block with fixed registers. attn_fwd_gfx950.hip includes the file inside
+"""Writes key_loop_gfx950.inc and key_loop_idx_gfx950.inc: the key loop of the attention
+forward kernel for gfx950, as one inline-asm block with fixed registers, over a contiguous
+range of key tiles or over a list of key tiles. attn_fwd_gfx950.hip includes the files inside
 attn_rows(); build.py runs this script before every compile, and a CPU test checks that the
-committed file is what this script writes.
+committed files are what this script writes.
 
 Method (online softmax with BF16 probabilities and FP32 accumulation): page "[sglang]
 SANA-Video 2.0 anchor attention ... FP32 upcast" (blog on sglang PR #49219), "lessons" list
@@ -39,6 +40,17 @@ Register map (per lane):
     a[128:191]           Q fragments: (rb, s) at 128 + 4*(8*rb + s)
 The block hands O^T back in v[0:127] (same numbering), m and l in operands.
 
+Tile-list variant (block-skip attention, page "PR #33702 report", motivation: KV blocks
+routed by a threshold are skipped): the tiles walked are the entries of an int32 list in
+global memory (ascending tile indices; the list is readable at least 8 entries past its
+count). The cursors move by (next - current) tiles instead of one; each index is clamped to
+[current, ntk] first, so whatever the list holds, loads stay inside the sequence (an index of
+ntk reads zeros, as loads past the end do). Entries 1..3 come by one scalar load in the
+set-up; entry t+5 is fetched by a vector load in tile t, which the next tile's vmcnt(0) before
+its barrier completes, and moved to an SGPR with v_readfirstlane when the cursors advance.
+Extra registers: v200 (the fetched index), v201 (zero offset), s[62:63] list cursor,
+s[64:67] set-up entries, s68 current tile, s69 next tile, s70 byte step, s71 ntk.
+
 The script tracks the LDS reads in flight (inserting s_waitcnt lgkmcnt) and inserts s_nop
 for the gfx950 wait states that hand-written code must provide itself:
     VALU write -> MFMA read of the register                            2
@@ -71,6 +83,10 @@ S_C1, S_C2 = 56, 58                # check masks
 S_STG = 60                         # K stage offset handed to the exact path
 S_M0 = 61                          # M0 of the caller, restored at the end
 NS_LO, NS_HI = 40, 61
+# tile-list variant
+V_IDX, V_ZERO = 200, 201
+S_LP, S_I, S_PREV, S_NEXT, S_D, S_NTK = 62, 64, 68, 69, 70, 71
+INDEXED = False                    # set by render()
 
 K_STAGE = 16384
 V_BASE = 65536
@@ -383,11 +399,16 @@ def prefetch_v(E, stage):
         read_v(E, g, g, 0, stage)
 
 
-def tile_loads(stage):
+def tile_loads(stage, src=None):
     """Buffer->LDS loads of one tile (this wave's quarter of K and of V) into a stage; then
     both resource cursors move one tile on (records clamped at zero, so loads past the
-    sequence end read zeros)."""
+    sequence end read zeros). Tile-list variant: the cursors move to the tile whose index is
+    in SGPR src (set-up), or in v200 (loop: fetched one tile earlier, complete after the
+    tile's vmcnt(0)), which then fetches the index after it."""
     ops = []
+    if INDEXED and src is None:
+        ops.append(lambda E: (E.emit(Ins("v_readfirstlane_b32 s%d, %s" % (S_NEXT, vr(V_IDX)), "valu", rd=vset(V_IDX))),
+                              E.nop(4)))
     for i in range(4):
         for base, cur, name in ((K_STAGE * stage, SK, "ko"), (V_BASE + V_STAGE * stage, SV, "vo")):
             ops.append(lambda E, i=i, base=base, cur=cur, name=name: (
@@ -395,13 +416,32 @@ def tile_loads(stage):
                 E.emit(Ins("buffer_load_dwordx4 %%[%s%d], s[%d:%d], 0 offen lds" % (name, i, cur, cur + 3), "vmem", m0r=True))))
 
     def advance(E):
+        step = "%[tb]"
+        if INDEXED:
+            nxt = S_NEXT if src is None else src
+            E.salu("s_max_i32 s%d, s%d, s%d" % (nxt, nxt, S_PREV))
+            E.salu("s_min_i32 s%d, s%d, s%d" % (nxt, nxt, S_NTK))
+            E.salu("s_sub_i32 s%d, s%d, s%d" % (S_D, nxt, S_PREV))
+            E.salu("s_mul_i32 s%d, s%d, %%[tb]" % (S_D, S_D))
+            E.salu("s_mov_b32 s%d, s%d" % (S_PREV, nxt))
+            step = "s%d" % S_D
         for cur in (SK, SV):
-            E.salu("s_add_u32 s%d, s%d, %%[tb]" % (cur, cur))
+            E.salu("s_add_u32 s%d, s%d, %s" % (cur, cur, step))
             E.salu("s_addc_u32 s%d, s%d, 0" % (cur + 1, cur + 1))
-            E.salu("s_sub_i32 s%d, s%d, %%[tb]" % (cur + 2, cur + 2))
+            E.salu("s_sub_i32 s%d, s%d, %s" % (cur + 2, cur + 2, step))
             E.salu("s_max_i32 s%d, s%d, 0" % (cur + 2, cur + 2))
+        if INDEXED and src is None:
+            fetch_index(E)
     ops.append(advance)
     return ops
+
+
+def fetch_index(E):
+    """v200 = the list entry at s[62:63], which then moves on one entry."""
+    E.salu("s_add_u32 s%d, s%d, 4" % (S_LP, S_LP))
+    E.salu("s_addc_u32 s%d, s%d, 0" % (S_LP + 1, S_LP + 1))
+    E.emit(Ins("global_load_dword %s, %s, s[%d:%d] offset:-4" % (vr(V_IDX), vr(V_ZERO), S_LP, S_LP + 1), "vmem",
+               rd=vset(V_ZERO), wr=vset(V_IDX)))
 
 
 def rare_call(E, X, stage, uid):
@@ -513,6 +553,18 @@ def generate(backedge=None):
     for i in range(4):
         E.salu("s_mov_b32 s%d, %%[rk%d]" % (SK + i, i))
         E.salu("s_mov_b32 s%d, %%[rv%d]" % (SV + i, i))
+    if INDEXED:
+        # list cursor at entry 1; entries 1..3 (and 4) by one scalar load; entry 4 to v200
+        E.salu("s_mov_b32 s%d, %%[lp0]" % S_LP)
+        E.salu("s_mov_b32 s%d, %%[lp1]" % (S_LP + 1))
+        E.raw("s_load_dwordx4 s[%d:%d], s[%d:%d], 0x4" % (S_I, S_I + 3, S_LP, S_LP + 1))
+        E.salu("s_mov_b32 s%d, %%[i0]" % S_PREV)
+        E.salu("s_mov_b32 s%d, %%[ntk]" % S_NTK)
+        E.raw("s_waitcnt lgkmcnt(0)")
+        E.valu("v_mov_b32 %s, 0" % vr(V_ZERO), wr=vset(V_ZERO))
+        E.salu("s_add_u32 s%d, s%d, 16" % (S_LP, S_LP))
+        E.salu("s_addc_u32 s%d, s%d, 0" % (S_LP + 1, S_LP + 1))
+        fetch_index(E)
     E.salu("s_mov_b32 s%d, 0" % S_T)
     E.salu("s_sub_u32 s%d, %%[T], 2" % S_TLAST)
     E.salu("s_mov_b32 s%d, 0x%08x" % (S_LIM, OPTS["limit_bits"]))
@@ -528,7 +580,7 @@ def generate(backedge=None):
     for i in range(128):
         E.valu("v_accvgpr_write_b32 %s, 0" % ar(O_BASE + i), wr=aset(O_BASE + i))
     for u in range(3):
-        for f in tile_loads(u):
+        for f in tile_loads(u, S_I + u if INDEXED else None):
             f(E)
     E.raw("s_waitcnt vmcnt(0)")
     E.raw("s_barrier")
@@ -598,7 +650,17 @@ def generate(backedge=None):
     return E.out, loop_end
 
 
-def render():
+def render(indexed=False):
+    global INDEXED
+    INDEXED = indexed
+    try:
+        return _render()
+    finally:
+        INDEXED = False
+
+
+def _render():
+    nv, ns_hi = (V_ZERO + 1, S_NTK) if INDEXED else (NV, NS_HI)
     lines, back = generate()
     for _ in range(4):   # the loop head is reached from the set-up and from the loop end
         lines2, back2 = generate(back)
@@ -607,8 +669,8 @@ def render():
         lines, back = lines2, back2
     else:
         raise SystemExit("wait-state pass did not converge")
-    clob = ['"v%d"' % i for i in range(128, NV)] + ['"a%d"' % i for i in range(NA)] + \
-           ['"s%d"' % i for i in range(NS_LO, NS_HI + 1)] + ['"vcc"', '"scc"', '"memory"']
+    clob = ['"v%d"' % i for i in range(128, nv)] + ['"a%d"' % i for i in range(NA)] + \
+           ['"s%d"' % i for i in range(NS_LO, ns_hi + 1)] + ['"vcc"', '"scc"', '"memory"']
     outs = ['[o%d%d] "=&{v[%d:%d]}"(o[%d][%d])' % (db, rb, oblk(db, rb), oblk(db, rb) + 15, db, rb)
             for db in range(4) for rb in range(2)]
     outs += ['[m0] "=v"(mref[0])', '[m1] "=v"(mref[1])', '[l0] "=v"(lsum[0])', '[l1] "=v"(lsum[1])']
@@ -617,9 +679,12 @@ def render():
     ins += ['[ko%d] "v"(ko[%d])' % (i, i) for i in range(4)] + ['[vo%d] "v"(vo[%d])' % (i, i) for i in range(4)]
     ins += ['[qa0] "v"(qa[0])', '[qa1] "v"(qa[1])', '[ldsw] "s"(ldsw)', '[tb] "s"(tb)', '[T] "s"(ntile)',
             '[c] "s"(c)', '[klim] "v"(klim)', '[bperm] "v"(bperm)']
+    if INDEXED:
+        ins += ['[lp0] "s"(lp[0])', '[lp1] "s"(lp[1])', '[i0] "s"(idx0)', '[ntk] "s"(ntk)']
     n_ins = sum(1 for l in lines if l.startswith("\t"))
     n_nop = sum(1 for l in lines if l.strip().startswith("s_nop"))
-    text = ["// Written by gen_key_loop.py (do not edit): the key loop of attn_rows() for gfx950.",
+    what = ", over a list of key tiles" if INDEXED else ""
+    text = ["// Written by gen_key_loop.py (do not edit): the key loop of attn_rows() for gfx950%s." % what,
             "// %d instructions, %d of them s_nop." % (n_ins, n_nop),
             "asm volatile("]
     text += ['        "%s\\n"' % l.replace("\\", "\\\\").replace('"', '\\"') for l in lines]
@@ -630,13 +695,23 @@ def render():
 
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "key_loop_gfx950.inc")
+OUT_IDX = os.path.join(os.path.dirname(os.path.abspath(__file__)), "key_loop_idx_gfx950.inc")
 
 if __name__ == "__main__":
-    # gen_key_loop.py [out.inc [knob=value ...]]: the knobs select schedule variants
-    path = sys.argv[1] if len(sys.argv) > 1 else OUT
+    # gen_key_loop.py: both files; gen_key_loop.py out.inc [knob=value ...]: the range
+    # variant with schedule knobs changed (indexed=1 for the list variant)
+    if len(sys.argv) == 1:
+        for path, idx in ((OUT, False), (OUT_IDX, True)):
+            with open(path, "w") as f:
+                f.write(render(idx))
+        sys.exit(0)
+    indexed = False
     for kv in sys.argv[2:]:
         k, v = kv.split("=")
+        if k == "indexed":
+            indexed = bool(int(v))
+            continue
         assert k in OPTS, k
         OPTS[k] = int(v, 0)
-    with open(path, "w") as f:
-        f.write(render())
+    with open(sys.argv[1], "w") as f:
+        f.write(render(indexed))
