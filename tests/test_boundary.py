@@ -262,6 +262,7 @@ def test_linear_workspace_query(lib):
     (dict(o=LV + 128), INVALID),                                     # out overlaps v
     (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=LWS + 8), WORKSPACE),
     (dict(ws=LO), INVALID),                                          # workspace over out
+    (dict(N=1 << 20, H=1024), UNSUPPORTED),                          # a (b, h) slice past 2 GiB
 ])
 def test_linear_validation(lib, kw, code):
     assert linear(lib, **kw) == code

@@ -19,7 +19,8 @@
 //       operand layout for both A = V^T and B = K_rot.
 //   linear_kv_reduce_kernel   sums the chunk partials in chunk order (deterministic) and
 //       splits kv exactly into three BF16 terms.
-//   linear_out_kernel         one workgroup per (b, h, 1024 tokens): out = kv q_rot / den.
+//   linear_out_kernel         one workgroup per (b, h, 1024 tokens): out = kv q_rot / den;
+//       each wave keeps 32 rows of kv in registers, q_rot arrives in LDS by global->LDS DMA.
 //       The FP32 product runs on the BF16 matrix cores: kv = hi + mid + lo with three BF16
 //       terms (8 bits each, together every bit of the FP32 value), q_rot is BF16 exactly,
 //       so each of the three MFMA products is exact and the accumulation is FP32, the same
@@ -49,7 +50,6 @@ constexpr int KV_TERMS = 3;          // BF16 terms of the FP32 kv in the output 
 constexpr int OUT_SUB = 256;         // tokens per sub-block of the output pass (64 per wave)
 constexpr int OUT_SUBS = 4;          // sub-blocks per workgroup
 constexpr int OUT_TOK = OUT_SUB * OUT_SUBS;
-constexpr int KVROW = D * 2 + 16;    // LDS row stride of a BF16 kv term
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -85,7 +85,10 @@ __global__ __launch_bounds__(NT) void linear_kv_partial_kernel(LinearArgs a) {
     float* red = reinterpret_cast<float*>(smem + 2 * TILE * ROW);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
-    const int bh = blockIdx.x / a.S, s = blockIdx.x - bh * a.S;
+    // heads fastest: the workgroups running together read the same token rows of every head
+    // (whole 4 KiB token rows of the [B, N, H, 128] tensors instead of one 256-byte slice each)
+    const int nbh = gridDim.x / a.S;
+    const int s = blockIdx.x / nbh, bh = blockIdx.x - s * nbh;
     const int b = bh / a.H, h = bh - b * a.H;
     const long row_stride = (long)a.H * D;                       // elements between tokens
     const long base = ((long)b * a.N * a.H + h) * D;             // (b, token 0, h)
@@ -192,124 +195,231 @@ __global__ __launch_bounds__(NT) void linear_kv_reduce_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------- out = kv q_rot / den
-// A workgroup takes OUT_TOK tokens of one (b, h) in OUT_SUBS sub-blocks; in each, wave w owns
-// 64 tokens (two 32-token column blocks) against all four 32-row blocks of kv. A fragments
-// (kv terms) come from LDS; the B fragments (q_rot) and the q rows of the normaliser are
-// loaded in the MFMA operand layout (lane: token column, 8 dims), the next sub-block's while
-// the current one computes.
-struct OutFrags {
-    bf16x8 qr[2][8];   // q_rot: [column block][16-dim step]
-    bf16x8 q[2][8];    // q (normaliser)
+// A workgroup takes OUT_TOK tokens of one (b, h) in sub-blocks of OUT_SUB tokens. Wave w owns
+// output dims 32w .. 32w+31: its A fragments (rows 32w.. of the three kv terms, all 128 dims)
+// stay in registers for the whole workgroup. q_rot of a sub-block goes from HBM straight into
+// LDS (global_load_lds: each instruction moves four whole token rows, 1 KiB, fully
+// coalesced), double-buffered and XOR-swizzled (row r, 16-byte chunk c at r*256 +
+// 16*(c ^ (r % 16))), and every wave reads the B fragments of all OUT_SUB tokens from it. The
+// normaliser of a token: 16 lanes load its q row (one 16-byte chunk each, coalesced), dot it
+// with ksum and add across the 16 lanes; wave w does tokens 64w .. 64w+63 of the next
+// sub-block into LDS while its MFMAs run.
+constexpr int QROW = D * 2;                  // LDS bytes per staged q_rot row (swizzled, no pad)
+constexpr int QBUF = OUT_SUB * QROW;         // one sub-block of q_rot
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima) as a builtin, which the compiler's
+// wait-count bookkeeping sees (an asm statement would be opaque to it)
+constexpr int WAIT_VMCNT0 = 0x0F70;
+
+constexpr unsigned BUF_FLAGS = 0x00020000;   // raw buffer, 32-bit data format
+
+// Buffer resource over tokens n .. N-1 of the (b, h) slice of a token-major [B, N, H, 128]
+// tensor (p points at token n; token n + r at byte r * row_stride * 2). Every load below puts
+// its whole offset in the VGPR (soffset 0), which the bounds check covers: rows past the last
+// token read zeros.
+__device__ __forceinline__ u32x4 rows_rsrc(const bf16* p, int rows, long row_stride) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, (unsigned)(((long)(rows - 1) * row_stride + D) * 2),
+                 BUF_FLAGS};
+}
+
+// Per-lane byte offsets of the q_rot staging: instruction i of wave w moves rows
+// 64w + 4i .. +3 (lane: row 4i + lane/16, LDS slot lane%16, global chunk slot ^ row%16).
+// The swizzle repeats every 4 instructions: offset = v[i % 4] + (i / 4) * 16 rows... written
+// as v[i % 4] + i' * step4 with the row step added in the asm.
+struct StageOffsets {
+    unsigned v[4];
 };
 
-__device__ __forceinline__ void load_out_frags(const LinearArgs& a, long base, long row_stride, int n_first,
-                                               int col, int g, OutFrags& f) {
+__device__ __forceinline__ StageOffsets stage_offsets(long row_stride, int w, int lane) {
+    StageOffsets o;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int nn = min(n_first + 32 * cb + col, a.N - 1);
-        const bf16* qr = a.qr + base + (long)nn * row_stride + 8 * g;
-        const bf16* q = a.q + base + (long)nn * row_stride + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            f.qr[cb][ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
-            f.q[cb][ks] = *reinterpret_cast<const bf16x8*>(q + 16 * ks);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4);           // row within a group of 16 (swizzle key)
+        const int c = (lane & 15) ^ (r & 15);
+        o.v[i] = (unsigned)((((long)(64 * w + 4 * i + (lane >> 4))) * row_stride + 8 * c) * 2);
     }
+    return o;
+}
+
+// q_rot rows of the resource (one sub-block) into LDS buffer dst. Instruction i = 4m + k uses
+// offset v[k] + m * step16 (16 rows), formed by one v_add in the asm. One asm block, so the
+// compiler puts no wait for these LDS writes in front of unrelated LDS reads: the caller waits
+// (vmcnt(0), then a barrier) before any wave reads dst. M0 (the LDS destination) is saved and
+// restored around it.
+__device__ __forceinline__ void stage_qrot(u32x4 rsrc, unsigned step16, const StageOffsets& o, char* dst, int w) {
+    const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(dst + 64 * w * QROW);
+    unsigned saved, st, t;
+#define STAGE_LOAD(k) "v_add_u32 %[t], %[st], %[o" #k "]\n" "buffer_load_dwordx4 %[t], %[rs], 0 offen lds\n" \
+                      "s_add_u32 m0, m0, 1024\n" "s_nop 0\n"
+#define STAGE_GROUP STAGE_LOAD(0) STAGE_LOAD(1) STAGE_LOAD(2) STAGE_LOAD(3) "s_add_u32 %[st], %[st], %[s16]\n"
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n"
+        "s_mov_b32 m0, %[l]\n"
+        "s_mov_b32 %[st], 0\n"
+        "s_nop 0\n"
+        STAGE_GROUP STAGE_GROUP STAGE_GROUP STAGE_GROUP
+        "s_mov_b32 m0, %[sv]\n"
+        : [sv] "=&s"(saved), [st] "=&s"(st), [t] "=&v"(t)
+        : [l] "s"(lds), [rs] "s"(rsrc), [s16] "s"(step16), [o0] "v"(o.v[0]), [o1] "v"(o.v[1]), [o2] "v"(o.v[2]),
+          [o3] "v"(o.v[3])
+        : "memory");
+#undef STAGE_LOAD
+#undef STAGE_GROUP
+}
+
+// q rows of tokens 64w .. 64w+63 of the resource: lane (row 4i + lane/16, chunk lane%16), 16
+// loads (zeros past the last token).
+struct QRows {
+    u32x4 v[16];
+};
+
+__device__ __forceinline__ void load_q_rows(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned step4, QRows& qrw) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        qrw.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + i * step4), 0, 0));
+}
+
+// Sum over the 16 lanes of a DPP row (each lane ends with the total): xor 1 and xor 2 within
+// quads, then the mirrored half-row and the mirrored row.
+__device__ __forceinline__ float row16_sum(float p) {
+    p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), 0xB1, 0xF, 0xF, false));
+    p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), 0x4E, 0xF, 0xF, false));
+    p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), 0x141, 0xF, 0xF, false));
+    p += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), 0x140, 0xF, 0xF, false));
+    return p;
+}
+
+// den of those 64 tokens -> den_s[64w + row]; lane (row group lane/16, chunk c) ends holding
+// the sums of rows 4i + lane/16 for every i and writes the one with i = c.
+__device__ __forceinline__ void write_den(const QRows& qrw, const float* ksum_s, float eps, float* den_s, int w,
+                                          int lane) {
+    const int c = lane & 15;
+    float ks8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ks8[e] = ksum_s[8 * c + e];
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p = fmaf(__uint_as_float(qrw.v[i][e] << 16), ks8[2 * e], p);
+            p = fmaf(__uint_as_float(qrw.v[i][e] & 0xffff0000u), ks8[2 * e + 1], p);
+        }
+        p = row16_sum(p);
+        mine = c == i ? p : mine;
+    }
+    den_s[64 * w + 4 * c + (lane >> 4)] = mine + eps;
 }
 
 __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
-    __shared__ __attribute__((aligned(16))) char kvs[KV_TERMS * D * KVROW];
+    __shared__ __attribute__((aligned(1024))) char qbuf[2][QBUF];
+    __shared__ float den_s[2][OUT_SUB];
     __shared__ float ksum_s[D];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ntb = (a.N + OUT_TOK - 1) / OUT_TOK;
-    const int bh = blockIdx.x / ntb, tb = blockIdx.x - bh * ntb;
+    const int nbh = gridDim.x / ntb;   // heads fastest, as in the kv pass
+    const int tb = blockIdx.x / nbh, bh = blockIdx.x - tb * nbh;
     const int b = bh / a.H, h = bh - b * a.H;
     const long row_stride = (long)a.H * D;
     const long base = ((long)b * a.N * a.H + h) * D;
     const int n0 = tb * OUT_TOK;
+    const int nsub = min(OUT_SUBS, (a.N - n0 + OUT_SUB - 1) / OUT_SUB);
     const int g = lane >> 5, col = lane & 31;
 
-    OutFrags cur, nxt;
-    load_out_frags(a, base, row_stride, n0 + 64 * w, col, g, cur);
-    // kv terms -> LDS (row i of term t at t*D*KVROW + i*KVROW), 16 bytes per thread and step
-    // (straight-line batches of 8 loads, so the waits count the loads in flight instead of
-    // draining the queue after each one)
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.terms + (long)bh * KV_TERMS * D * D);
-    constexpr int PER = KV_TERMS * D * (D / 8) / NT;      // 24 chunks of 16 bytes per thread
-    static_assert(PER % 8 == 0, "copy batches");
+    // resources per sub-block (from its first token); per-lane offsets fixed for the kernel
+    auto q_rsrc = [&](int n) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + base + (long)n * row_stride), (short)0,
+                                                 (int)(((long)(a.N - n - 1) * row_stride + D) * 2), (int)BUF_FLAGS);
+    };
+    const StageOffsets so = stage_offsets(row_stride, w, lane);
+    const unsigned qoff = (unsigned)((((long)(64 * w + (lane >> 4))) * row_stride + 8 * (lane & 15)) * 2);
+    const unsigned step4 = (unsigned)(4 * row_stride * 2), step16 = 4 * step4;
+    stage_qrot(rows_rsrc(a.qr + base + (long)n0 * row_stride, a.N - n0, row_stride), step16, so, qbuf[0], w);
+    QRows qrw;
+    load_q_rows(q_rsrc(n0), qoff, step4, qrw);
+    // A fragments: kv term rows 32w + col, dims 16ks + 8g .. +7
+    bf16x8 af[KV_TERMS][8];
+    const bf16* tm = a.terms + (long)bh * KV_TERMS * D * D + (long)(32 * w + col) * D + 8 * g;
 #pragma unroll
-    for (int bt = 0; bt < PER; bt += 8) {
-        u32x4 tmp[8];
+    for (int t = 0; t < KV_TERMS; ++t)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) tmp[u] = src[tid + (bt + u) * NT];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int cidx = tid + (bt + u) * NT;
-            const int row = cidx >> 4, ch = cidx & 15;      // row = term * D + i
-            *reinterpret_cast<u32x4*>(kvs + row * KVROW + 16 * ch) = tmp[u];
-        }
-    }
+        for (int ks = 0; ks < 8; ++ks) af[t][ks] = *reinterpret_cast<const bf16x8*>(tm + (long)t * D * D + 16 * ks);
     if (tid < D) ksum_s[tid] = a.ksum[(long)bh * D + tid];
     __syncthreads();
+    __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);   // this wave's q_rot rows are in LDS, af and q loaded
+    write_den(qrw, ksum_s, a.eps, den_s[0], w, lane);
 
-#pragma unroll
-    for (int sub = 0; sub < OUT_SUBS; ++sub) {
-        const int n_first = n0 + OUT_SUB * sub + 64 * w;
-        if (sub + 1 < OUT_SUBS) load_out_frags(a, base, row_stride, n_first + OUT_SUB, col, g, nxt);
-
-        // normaliser: lane (col, g) sums its 64 dims of q . ksum, the partner lane the other 64
-        float den[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            float p = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) p = fmaf((float)cur.q[cb][ks][t], ksum_s[16 * ks + 8 * g + t], p);
-            den[cb] = p + __shfl_xor(p, 32) + a.eps;
+    for (int sub = 0; sub < nsub; ++sub) {
+        const int cur = sub & 1;
+        const int n_first = n0 + OUT_SUB * sub;
+        // every wave waited for its q_rot rows of this sub-block and wrote its den before
+        // arriving; every wave is done reading the other buffer
+        __syncthreads();
+        const bool more = sub + 1 < nsub;
+        if (more) {
+            const int nn = n_first + OUT_SUB;
+            stage_qrot(rows_rsrc(a.qr + base + (long)nn * row_stride, a.N - nn, row_stride), step16, so, qbuf[cur ^ 1], w);
+            load_q_rows(q_rsrc(nn), qoff, step4, qrw);
         }
-
-        f32x16 acc[4][2];
+        const char* qb = qbuf[cur];
+        f32x16 acc[OUT_SUB / 32];
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
+        for (int cb = 0; cb < OUT_SUB / 32; ++cb) acc[cb] = f32x16{};
+        // B fragments of column block cb (row 32cb + col, chunks 2ks + g), read one block ahead
+        bf16x8 bq[2][8];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) acc[ib][cb] = f32x16{};
+        for (int ks = 0; ks < 8; ++ks)
+            bq[0][ks] = *reinterpret_cast<const bf16x8*>(qb + col * QROW + 16 * ((2 * ks + g) ^ (col & 15)));
 #pragma unroll
-        for (int term = 0; term < KV_TERMS; ++term)
+        for (int cb = 0; cb < OUT_SUB / 32; ++cb) {
+            if (cb + 1 < OUT_SUB / 32) {
+                const int r = 32 * (cb + 1) + col;
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks)
+                    bq[(cb + 1) & 1][ks] =
+                        *reinterpret_cast<const bf16x8*>(qb + r * QROW + 16 * ((2 * ks + g) ^ (r & 15)));
+            }
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    // A: kv term, rows 32ib + col, dims 16ks + 8g .. +7
-                    const bf16x8 fa = *reinterpret_cast<const bf16x8*>(
-                        kvs + (term * D + 32 * ib + col) * KVROW + 2 * (16 * ks + 8 * g));
+                for (int t = 0; t < KV_TERMS; ++t) acc[cb] = mfma(af[t][ks], bq[cb & 1][ks], acc[cb]);
+        }
+        if (more) {   // the next sub-block's loads had the MFMA phase to land
+            __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
+            write_den(qrw, ksum_s, a.eps, den_s[cur ^ 1], w, lane);
+        }
+        // Output through LDS, so that the global stores move whole rows: once every wave is done
+        // with this sub-block's q_rot, each writes its 32 dims of the 256 tokens (scaled by
+        // 1/den, BF16) into that buffer, laid out like q_rot (row t, 16-byte chunk c at
+        // t*256 + 16*(c ^ (t % 16))), then moves 64 whole rows to HBM, 4 per instruction.
+        // C layout: lane (token column col, g), register q -> dim 32w + 8(q/4) + 4g + q%4.
+        __syncthreads();
+        char* ob = qbuf[cur];
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) acc[ib][cb] = mfma(fa, cur.qr[cb][ks], acc[ib][cb]);
-                }
-
-        // C layout: lane (token column col, g), register q -> dim 32ib + 8(q/4) + 4g + q%4
+        for (int cb = 0; cb < OUT_SUB / 32; ++cb) {
+            const int t = 32 * cb + col;
+            const float inv = 1.0f / den_s[cur][t];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int n = n_first + 32 * cb + col;
-            if (n < a.N) {
-                const float inv = 1.0f / den[cb];
-                bf16* orow = a.out + base + (long)n * row_stride;
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const int d0 = 32 * ib + 8 * qq + 4 * g;
-                        const bf16 e0 = (bf16)(acc[ib][cb][4 * qq + 0] * inv), e1 = (bf16)(acc[ib][cb][4 * qq + 1] * inv);
-                        const bf16 e2 = (bf16)(acc[ib][cb][4 * qq + 2] * inv), e3 = (bf16)(acc[ib][cb][4 * qq + 3] * inv);
-                        const unsigned lo = (unsigned)__builtin_bit_cast(unsigned short, e0) |
-                                            ((unsigned)__builtin_bit_cast(unsigned short, e1) << 16);
-                        const unsigned hi = (unsigned)__builtin_bit_cast(unsigned short, e2) |
-                                            ((unsigned)__builtin_bit_cast(unsigned short, e3) << 16);
-                        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(lo, hi);
-                    }
+            for (int qq = 0; qq < 4; ++qq) {
+                const bf16 e0 = (bf16)(acc[cb][4 * qq + 0] * inv), e1 = (bf16)(acc[cb][4 * qq + 1] * inv);
+                const bf16 e2 = (bf16)(acc[cb][4 * qq + 2] * inv), e3 = (bf16)(acc[cb][4 * qq + 3] * inv);
+                const unsigned lo = (unsigned)__builtin_bit_cast(unsigned short, e0) |
+                                    ((unsigned)__builtin_bit_cast(unsigned short, e1) << 16);
+                const unsigned hi = (unsigned)__builtin_bit_cast(unsigned short, e2) |
+                                    ((unsigned)__builtin_bit_cast(unsigned short, e3) << 16);
+                const int chunk = (4 * w + qq) ^ (t & 15);     // dims 32w + 8qq .. +7
+                *reinterpret_cast<uint2*>(ob + t * QROW + 16 * chunk + 8 * g) = make_uint2(lo, hi);
             }
         }
-        if (sub + 1 < OUT_SUBS) cur = nxt;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 64 * w + 4 * i + (lane >> 4), c = lane & 15;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(ob + r * QROW + 16 * (c ^ (r & 15)));
+            if (n_first + r < a.N)
+                *reinterpret_cast<u32x4*>(a.out + base + (long)(n_first + r) * row_stride + 8 * c) = val;
+        }
     }
 }
 
