@@ -20,7 +20,7 @@
 //   linear_kv_reduce_kernel   sums the chunk partials in chunk order (deterministic) and
 //       splits kv exactly into three BF16 terms.
 //   linear_out_kernel         one workgroup per (b, h, 1024 tokens): out = kv q_rot / den;
-//       each wave keeps 32 rows of kv in registers, q_rot arrives in LDS by global->LDS DMA.
+//       each wave keeps 32 rows of kv in registers, q_rot arrives in LDS by buffer->LDS loads.
 //       The FP32 product runs on the BF16 matrix cores: kv = hi + mid + lo with three BF16
 //       terms (8 bits each, together every bit of the FP32 value), q_rot is BF16 exactly,
 //       so each of the three MFMA products is exact and the accumulation is FP32, the same
@@ -47,8 +47,11 @@ constexpr int TILE = 64;             // tokens per LDS tile in the kv pass
 constexpr int KV_CHUNK = 2048;       // tokens per workgroup in the kv pass (a multiple of TILE)
 constexpr int ROW = D * 2 + 32;      // LDS row stride in bytes (padded: 8-bank shift per row)
 constexpr int KV_TERMS = 3;          // BF16 terms of the FP32 kv in the output pass
-constexpr int OUT_SUB = 256;         // tokens per sub-block of the output pass (64 per wave)
-constexpr int OUT_SUBS = 4;          // sub-blocks per workgroup
+#define LIN_OUT_SUB 128              // tokens per sub-block of the output pass (a multiple of 64)
+constexpr int OUT_SUB = LIN_OUT_SUB;
+constexpr int OUT_SUBS = 1024 / OUT_SUB;   // sub-blocks per workgroup
+constexpr int RPW = OUT_SUB / 4;           // rows of a sub-block each wave stages, normalises, stores
+constexpr int NI = RPW / 4;                // instructions for them (four rows each)
 constexpr int OUT_TOK = OUT_SUB * OUT_SUBS;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -195,15 +198,18 @@ __global__ __launch_bounds__(NT) void linear_kv_reduce_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------- out = kv q_rot / den
-// A workgroup takes OUT_TOK tokens of one (b, h) in sub-blocks of OUT_SUB tokens. Wave w owns
-// output dims 32w .. 32w+31: its A fragments (rows 32w.. of the three kv terms, all 128 dims)
-// stay in registers for the whole workgroup. q_rot of a sub-block goes from HBM straight into
-// LDS (global_load_lds: each instruction moves four whole token rows, 1 KiB, fully
-// coalesced), double-buffered and XOR-swizzled (row r, 16-byte chunk c at r*256 +
-// 16*(c ^ (r % 16))), and every wave reads the B fragments of all OUT_SUB tokens from it. The
-// normaliser of a token: 16 lanes load its q row (one 16-byte chunk each, coalesced), dot it
-// with ksum and add across the 16 lanes; wave w does tokens 64w .. 64w+63 of the next
-// sub-block into LDS while its MFMAs run.
+// A workgroup takes OUT_TOK tokens of one (b, h) in sub-blocks of OUT_SUB tokens; two
+// workgroups share a compute unit (64 KiB of LDS and at most 256 registers per lane each), so
+// one computes while the other waits on memory. Wave w owns output dims 32w .. 32w+31: its A
+// fragments (rows 32w.. of the three kv terms, all 128 dims) stay in registers for the whole
+// workgroup. q_rot of a sub-block goes from HBM straight into LDS (buffer->LDS loads: each
+// instruction moves four whole token rows, 1 KiB, fully coalesced), double-buffered and
+// XOR-swizzled (row r, 16-byte chunk c at r*256 + 16*(c ^ (r % 16))), and every wave reads the
+// B fragments of all OUT_SUB tokens from it. The normaliser of a token: 16 lanes load its q row
+// (one 16-byte chunk each, coalesced), dot it with ksum and add across the 16 lanes; wave w
+// does tokens RPW*w .. RPW*w+RPW-1 of the next sub-block into LDS while its MFMAs run. The
+// grid runs heads fastest, so the workgroups in flight read whole 4 KiB token rows of the
+// token-major tensors together.
 constexpr int QROW = D * 2;                  // LDS bytes per staged q_rot row (swizzled, no pad)
 constexpr int QBUF = OUT_SUB * QROW;         // one sub-block of q_rot
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima) as a builtin, which the compiler's
@@ -223,7 +229,7 @@ __device__ __forceinline__ u32x4 rows_rsrc(const bf16* p, int rows, long row_str
 }
 
 // Per-lane byte offsets of the q_rot staging: instruction i of wave w moves rows
-// 64w + 4i .. +3 (lane: row 4i + lane/16, LDS slot lane%16, global chunk slot ^ row%16).
+// RPW*w + 4i .. +3 (lane: row 4i + lane/16, LDS slot lane%16, global chunk slot ^ row%16).
 // The swizzle repeats every 4 instructions: offset = v[i % 4] + (i / 4) * 16 rows... written
 // as v[i % 4] + i' * step4 with the row step added in the asm.
 struct StageOffsets {
@@ -236,7 +242,7 @@ __device__ __forceinline__ StageOffsets stage_offsets(long row_stride, int w, in
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * i + (lane >> 4);           // row within a group of 16 (swizzle key)
         const int c = (lane & 15) ^ (r & 15);
-        o.v[i] = (unsigned)((((long)(64 * w + 4 * i + (lane >> 4))) * row_stride + 8 * c) * 2);
+        o.v[i] = (unsigned)((((long)(RPW * w + 4 * i + (lane >> 4))) * row_stride + 8 * c) * 2);
     }
     return o;
 }
@@ -247,7 +253,7 @@ __device__ __forceinline__ StageOffsets stage_offsets(long row_stride, int w, in
 // (vmcnt(0), then a barrier) before any wave reads dst. M0 (the LDS destination) is saved and
 // restored around it.
 __device__ __forceinline__ void stage_qrot(u32x4 rsrc, unsigned step16, const StageOffsets& o, char* dst, int w) {
-    const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(dst + 64 * w * QROW);
+    const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(dst + RPW * w * QROW);
     unsigned saved, st, t;
 #define STAGE_LOAD(k) "v_add_u32 %[t], %[st], %[o" #k "]\n" "buffer_load_dwordx4 %[t], %[rs], 0 offen lds\n" \
                       "s_add_u32 m0, m0, 1024\n" "s_nop 0\n"
@@ -257,7 +263,10 @@ __device__ __forceinline__ void stage_qrot(u32x4 rsrc, unsigned step16, const St
         "s_mov_b32 m0, %[l]\n"
         "s_mov_b32 %[st], 0\n"
         "s_nop 0\n"
-        STAGE_GROUP STAGE_GROUP STAGE_GROUP STAGE_GROUP
+        STAGE_GROUP STAGE_GROUP
+#if LIN_OUT_SUB == 256
+        STAGE_GROUP STAGE_GROUP
+#endif
         "s_mov_b32 m0, %[sv]\n"
         : [sv] "=&s"(saved), [st] "=&s"(st), [t] "=&v"(t)
         : [l] "s"(lds), [rs] "s"(rsrc), [s16] "s"(step16), [o0] "v"(o.v[0]), [o1] "v"(o.v[1]), [o2] "v"(o.v[2]),
@@ -267,15 +276,15 @@ __device__ __forceinline__ void stage_qrot(u32x4 rsrc, unsigned step16, const St
 #undef STAGE_GROUP
 }
 
-// q rows of tokens 64w .. 64w+63 of the resource: lane (row 4i + lane/16, chunk lane%16), 16
+// q rows of tokens RPW*w .. +RPW-1 of the resource: lane (row 4i + lane/16, chunk lane%16), NI
 // loads (zeros past the last token).
 struct QRows {
-    u32x4 v[16];
+    u32x4 v[NI];
 };
 
 __device__ __forceinline__ void load_q_rows(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned step4, QRows& qrw) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NI; ++i)
         qrw.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + i * step4), 0, 0));
 }
 
@@ -289,7 +298,7 @@ __device__ __forceinline__ float row16_sum(float p) {
     return p;
 }
 
-// den of those 64 tokens -> den_s[64w + row]; lane (row group lane/16, chunk c) ends holding
+// den of those RPW tokens -> den_s[RPW*w + row]; lane (row group lane/16, chunk c) ends holding
 // the sums of rows 4i + lane/16 for every i and writes the one with i = c.
 __device__ __forceinline__ void write_den(const QRows& qrw, const float* ksum_s, float eps, float* den_s, int w,
                                           int lane) {
@@ -299,7 +308,7 @@ __device__ __forceinline__ void write_den(const QRows& qrw, const float* ksum_s,
     for (int e = 0; e < 8; ++e) ks8[e] = ksum_s[8 * c + e];
     float mine = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NI; ++i) {
         float p = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -309,10 +318,10 @@ __device__ __forceinline__ void write_den(const QRows& qrw, const float* ksum_s,
         p = row16_sum(p);
         mine = c == i ? p : mine;
     }
-    den_s[64 * w + 4 * c + (lane >> 4)] = mine + eps;
+    if (c < NI) den_s[RPW * w + 4 * c + (lane >> 4)] = mine + eps;
 }
 
-__global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
+__global__ __launch_bounds__(NT, LIN_OUT_SUB == 128 ? 2 : 1) void linear_out_kernel(LinearArgs a) {
     __shared__ __attribute__((aligned(1024))) char qbuf[2][QBUF];
     __shared__ float den_s[2][OUT_SUB];
     __shared__ float ksum_s[D];
@@ -332,12 +341,15 @@ __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
         return __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + base + (long)n * row_stride), (short)0,
                                                  (int)(((long)(a.N - n - 1) * row_stride + D) * 2), (int)BUF_FLAGS);
     };
-    const StageOffsets so = stage_offsets(row_stride, w, lane);
-    const unsigned qoff = (unsigned)((((long)(64 * w + (lane >> 4))) * row_stride + 8 * (lane & 15)) * 2);
+    // per-lane offsets (recomputed where used: a few VALU ops, cheaper than keeping them live)
+    auto qoff = [&]() {
+        return (unsigned)((((long)(RPW * w + (lane >> 4))) * row_stride + 8 * (lane & 15)) * 2);
+    };
     const unsigned step4 = (unsigned)(4 * row_stride * 2), step16 = 4 * step4;
-    stage_qrot(rows_rsrc(a.qr + base + (long)n0 * row_stride, a.N - n0, row_stride), step16, so, qbuf[0], w);
+    stage_qrot(rows_rsrc(a.qr + base + (long)n0 * row_stride, a.N - n0, row_stride), step16,
+               stage_offsets(row_stride, w, lane), qbuf[0], w);
     QRows qrw;
-    load_q_rows(q_rsrc(n0), qoff, step4, qrw);
+    load_q_rows(q_rsrc(n0), qoff(), step4, qrw);
     // A fragments: kv term rows 32w + col, dims 16ks + 8g .. +7
     bf16x8 af[KV_TERMS][8];
     const bf16* tm = a.terms + (long)bh * KV_TERMS * D * D + (long)(32 * w + col) * D + 8 * g;
@@ -359,13 +371,15 @@ __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
         const bool more = sub + 1 < nsub;
         if (more) {
             const int nn = n_first + OUT_SUB;
-            stage_qrot(rows_rsrc(a.qr + base + (long)nn * row_stride, a.N - nn, row_stride), step16, so, qbuf[cur ^ 1], w);
-            load_q_rows(q_rsrc(nn), qoff, step4, qrw);
+            stage_qrot(rows_rsrc(a.qr + base + (long)nn * row_stride, a.N - nn, row_stride), step16,
+                       stage_offsets(row_stride, w, lane), qbuf[cur ^ 1], w);
+            load_q_rows(q_rsrc(nn), qoff(), step4, qrw);
         }
         const char* qb = qbuf[cur];
         f32x16 acc[OUT_SUB / 32];
 #pragma unroll
         for (int cb = 0; cb < OUT_SUB / 32; ++cb) acc[cb] = f32x16{};
+#if LIN_OUT_SUB == 256
         // B fragments of column block cb (row 32cb + col, chunks 2ks + g), read one block ahead
         bf16x8 bq[2][8];
 #pragma unroll
@@ -385,6 +399,20 @@ __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
 #pragma unroll
                 for (int t = 0; t < KV_TERMS; ++t) acc[cb] = mfma(af[t][ks], bq[cb & 1][ks], acc[cb]);
         }
+#else
+        // B fragment (row 32cb + col, chunk 2ks + g) per step; the other wave of the SIMD
+        // covers the LDS latency
+#pragma unroll
+        for (int cb = 0; cb < OUT_SUB / 32; ++cb) {
+            const int r = 32 * cb + col;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 bq = *reinterpret_cast<const bf16x8*>(qb + r * QROW + 16 * ((2 * ks + g) ^ (r & 15)));
+#pragma unroll
+                for (int t = 0; t < KV_TERMS; ++t) acc[cb] = mfma(af[t][ks], bq, acc[cb]);
+            }
+        }
+#endif
         if (more) {   // the next sub-block's loads had the MFMA phase to land
             __builtin_amdgcn_s_waitcnt(WAIT_VMCNT0);
             write_den(qrw, ksum_s, a.eps, den_s[cur ^ 1], w, lane);
@@ -392,7 +420,7 @@ __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
         // Output through LDS, so that the global stores move whole rows: once every wave is done
         // with this sub-block's q_rot, each writes its 32 dims of the 256 tokens (scaled by
         // 1/den, BF16) into that buffer, laid out like q_rot (row t, 16-byte chunk c at
-        // t*256 + 16*(c ^ (t % 16))), then moves 64 whole rows to HBM, 4 per instruction.
+        // t*256 + 16*(c ^ (t % 16))), then moves RPW whole rows to HBM, 4 per instruction.
         // C layout: lane (token column col, g), register q -> dim 32w + 8(q/4) + 4g + q%4.
         __syncthreads();
         char* ob = qbuf[cur];
@@ -414,8 +442,8 @@ __global__ __launch_bounds__(NT, 1) void linear_out_kernel(LinearArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 64 * w + 4 * i + (lane >> 4), c = lane & 15;
+        for (int i = 0; i < NI; ++i) {
+            const int r = RPW * w + 4 * i + (lane >> 4), c = lane & 15;
             const u32x4 val = *reinterpret_cast<const u32x4*>(ob + r * QROW + 16 * (c ^ (r & 15)));
             if (n_first + r < a.N)
                 *reinterpret_cast<u32x4*>(a.out + base + (long)(n_first + r) * row_stride + 8 * c) = val;
