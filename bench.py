@@ -222,10 +222,38 @@ def time_prologue(args, w, vd, dev) -> dict:
           f"({100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f})", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         from oracle import bf16_bits_to_f64, bf16_faithful, qk_norm_rope
-        toks = np.random.default_rng(1).choice(w.N, 256, replace=False)
+        toks = np.random.default_rng(1).choice(w.N, 4096, replace=False)
         got = outs[0].view(torch.int16).cpu().numpy().view(np.uint16)[:, :, toks]
-        m = bf16_faithful(bf16_bits_to_f64(got), qk_norm_rope(xb[0], w.grid, tokens=toks))
+        t1 = time.perf_counter()
+        exact = qk_norm_rope(xb[0], w.grid, tokens=toks)
+        cpu_s = time.perf_counter() - t1
+        m = bf16_faithful(bf16_bits_to_f64(got), exact)
         rec["parity"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in m.items()}
+        sample_bytes = float(len(toks)) * w.B * w.H * w.d * 2 * 2      # Q rows read and written
+        rec["cpu_baseline"] = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
+                               "cores": oracle_cores(), "kind": "oracle",
+                               "sample": f"Q of {len(toks)} seeded tokens x {w.H} heads (the GPU call also does K and V), "
+                                         f"FP64 NumPy, {cpu_s:.2f} s"}
+    # a practical ceiling for this byte mix: plain device-to-device copies of the same three
+    # tensors (the same bytes read and written), timed the same way
+    def copies():
+        for x, o in zip(xs, outs):
+            o.view(torch.int16).copy_(x.view(torch.int16).view(o.shape[0], o.shape[2], o.shape[1], o.shape[3])
+                                      .reshape(o.shape))
+    copies()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(5):
+        copies()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 5
+    rec["copy_reference"] = {"what": "device-to-device copies of the same three tensors (same bytes read and written)",
+                             "achieved": round(nbytes / (copy_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                             "ms": round(copy_ms, 4)}
+    print(f"[bench] plain copy of the same bytes: {copy_ms:.4f} ms -> {nbytes / (copy_ms * 1e-3) / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
     del xs, outs
     torch.cuda.empty_cache()
     return rec
@@ -286,7 +314,16 @@ def time_linear(args, w, vd, dev) -> dict:
         toks = np.random.default_rng(2).choice(w.N, 256, replace=False)
         heads = [0, w.H - 1]                         # the key-side sums run over every token
         got = bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)[:, toks][:, :, heads])
+        t1 = time.perf_counter()
         ref = linear_attention(*[x[:, :, heads] for x in xb], tokens=toks)
+        cpu_s = time.perf_counter() - t1
+        # what the sample reads and writes: k, k_rot, v of every token and q, q_rot, out of
+        # the 256 tokens, for the two heads
+        sample_bytes = float(w.B) * len(heads) * w.d * 2 * (3.0 * w.N + 3.0 * len(toks))
+        rec["cpu_baseline"] = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
+                               "cores": oracle_cores(), "kind": "oracle",
+                               "sample": f"heads {heads} over all {w.N} tokens, outputs of 256 seeded tokens, "
+                                         f"FP64 NumPy, {cpu_s:.2f} s"}
         rec["parity"] = {"rel_l2": round(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), 8),
                          "n_elems": int(got.size), "ok": bool(np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref))}
     del xs, out
@@ -363,7 +400,16 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
         for b, h, i in zip(b_, h_, i_):
             keep[b, h, i, idx[b, h, i, :cnt[b, h, i]]] = True
         rows_s = np.random.default_rng(3).choice(w.B * w.H * w.N, 128, replace=False)
+        t1 = time.perf_counter()
         o_ref, _ = attention_kept(qb, kb, vb, w.scale, keep, rows=rows_s)
+        cpu_s = time.perf_counter() - t1
+        tile_keys = np.minimum(64, w.N - 64 * np.arange(ntk))
+        bh_r, n_r = rows_s // w.N, rows_s % w.N
+        kept_keys = (keep.reshape(-1, ntq, ntk)[bh_r, n_r // 256] * tile_keys).sum(axis=1)
+        cpu_flops = 4.0 * w.d * float(kept_keys.sum())
+        rec["cpu_baseline"] = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle_cores(), "kind": "oracle",
+                               "sample": f"128 seeded query rows over their kept keys, FP64 NumPy, {cpu_s:.2f} s"}
         vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out)
         got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, w.d)[rows_s]
         from oracle import bf16_bits_to_f64
@@ -372,6 +418,13 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
     del out, lse, kv_idx, kv_cnt
     torch.cuda.empty_cache()
     return rec
+
+
+def oracle_cores() -> int:
+    """Threads the FP64 oracle's BLAS calls use on this host."""
+    from threadpoolctl import threadpool_info
+    blas_threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    return min(blas_threads, host_cores())
 
 
 def host_cores() -> int:
