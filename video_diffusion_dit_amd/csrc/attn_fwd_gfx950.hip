@@ -43,11 +43,11 @@
 //
 // Row statistics: m_ref (per row, in log2 units of the scaled logit) and l (per-lane
 // partial). The common path computes P with the current m_ref and only checks that no
-// lane's tile sum exceeds 2^8 (then no probability exceeds 2^8 and FP32/BF16 stay exact in
-// relative terms); otherwise (always on a row's first tile, where m_ref = -inf) the wave
-// recomputes S from LDS and takes the exact path: true row max, rescale of O and l,
-// recompute of P. The result is the same softmax; only the reference the BF16
-// probabilities are relative to differs, which BF16 rounding (relative) does not see.
+// lane's tile sum exceeds 2^24 (then no probability exceeds 2^24, far from FP32 overflow);
+// otherwise (always on a row's first tile, where m_ref = -inf) the wave recomputes S from
+// LDS and takes the exact path: true row max, rescale of O and l, recompute of P. The result
+// is the same softmax; only the reference the BF16 probabilities are taken against differs,
+// and BF16 rounding is relative, so its error bound does not depend on it.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -24,7 +24,7 @@ holds four tiles.
 
 Softmax bookkeeping (per row block): m (the reference the probabilities are taken against,
 log2 units of the scaled logit) and l (the lane's partial row sum). The common path computes
-p = exp2(S*c - m) and checks that no lane's tile sum exceeds 2^8; when one does (always on the
+p = exp2(S*c - m) and checks that no lane's tile sum exceeds 2^24; when one does (always on the
 first tile, where m = -inf) the wave calls the exact path, which recomputes S of the tile
 from LDS, moves m to the running row maximum, rescales O and l, and recomputes P.
 
@@ -77,7 +77,7 @@ TMP0 = 176
 NV = 200
 O_BASE, Q_BASE, NA = 0, 128, 192
 SK, SV = 40, 44                    # buffer-resource cursors s[40:43] (K), s[44:47] (V)
-S_T, S_TLAST, S_LIM = 49, 50, 52   # tile counter, last loop tile, 256.0
+S_T, S_TLAST, S_LIM = 49, 50, 52   # tile counter, last loop tile, rescale limit
 S_RA = 54                          # exact-path return address s[54:55]
 S_C1, S_C2 = 56, 58                # check masks
 S_STG = 60                         # K stage offset handed to the exact path
@@ -91,7 +91,11 @@ INDEXED = False                    # set by render()
 K_STAGE = 16384
 V_BASE = 65536
 V_STAGE = 16384
-RESCALE_LIMIT_BITS = 0x43800000    # 256.0f
+# The largest tile sum accepted without moving the reference: 2^24 as an FP32 bit pattern.
+# Accepted probabilities stay below 2^24, so O sums at most N * 2^24 * max|v| (FP32 holds it
+# for max|v| < 2^86 at N = 2^17); a larger limit sends fewer tiles to the exact path when the
+# running maximum keeps climbing (outlier channels).
+RESCALE_LIMIT_BITS = 0x4B800000
 
 # Schedule knobs (the values the kernel is built with).
 OPTS = {
