@@ -151,3 +151,67 @@ def decision_margin(q_bits, k_bits, scale: float, tau: float, bm: int = QUERY_BL
             zmax = (scale_as_used(scale) * (qb @ kb.T)).max(axis=1)
             out[b, h] = e + e.max(axis=1, keepdims=True) + 2 * u * (np.abs(zmax)[:, None] + t)
     return out
+
+
+# ---------------------------------------------------------------- packed (varlen) batches
+# Page "PR #33702 report", motivation: the backend serves the packed varlen forward (THD
+# layout, attention confined to each segment). Routing and attention are the rule above
+# applied to each segment [cu[s], cu[s+1]) on its own: its query tiles are 256 of its rows,
+# its key tiles 64 of its keys, counted from the segment start.
+
+def segment_tiles(cu_seqlens, block: int) -> np.ndarray:
+    """Offsets of each segment's first tile in the numbering segment by segment, tile by
+    tile ([nseg + 1]; the last entry is the total number of tiles)."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    counts = -(-(cu[1:] - cu[:-1]) // block)
+    return np.concatenate([[0], np.cumsum(counts)])
+
+
+def route_blocks_varlen(q_bits, k_bits, cu_seqlens, scale: float, tau: float, sink_tokens: int = 0,
+                        bm: int = QUERY_BLOCK, bn: int = KEY_BLOCK):
+    """Per segment s (empty ones skipped): (keep [H, ntq_s, ntk_s], z, zmax [H, ntq_s]) for THD
+    [T, H, d] BF16 bits, as route_blocks on the segment seen as a [1, H, len, d] batch."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    out = []
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            out.append(None)
+            continue
+        qs = np.ascontiguousarray(np.asarray(q_bits)[a:e].transpose(1, 0, 2))[None]
+        ks = np.ascontiguousarray(np.asarray(k_bits)[a:e].transpose(1, 0, 2))[None]
+        keep, z, zmax = route_blocks(qs, ks, scale, tau, sink_tokens, bm, bn)
+        out.append((keep[0], z[0], zmax[0]))
+    return out
+
+
+def attention_kept_varlen(q_bits, k_bits, v_bits, cu_seqlens, scale: float, keeps, rows=None,
+                          bm: int = QUERY_BLOCK, bn: int = KEY_BLOCK):
+    """Attention of THD [T, H, d] BF16 inputs where query tile i of segment s sees only the key
+    tiles keeps[s][h, i] marks (keeps[s] bool [H, ntq_s, ntk_s], None for empty segments).
+
+    rows=None: o [T, H, d], lse [H, T]; rows = flat indices h*T + t: o [len, d], lse [len]."""
+    T, H, d = np.asarray(q_bits).shape
+    cu = np.asarray(cu_seqlens, np.int64)
+    flat = np.arange(H * T) if rows is None else np.asarray(rows, np.int64)
+    o = np.zeros((flat.size, d))
+    lse = np.full(flat.size, -np.inf)
+    h_of, t_of = flat // T, flat % T
+    seg_of = np.searchsorted(cu, t_of, side="right") - 1
+    for s in np.unique(seg_of):
+        a, e = int(cu[s]), int(cu[s + 1])
+        sel_s = np.nonzero(seg_of == s)[0]
+        for h in np.unique(h_of[sel_s]):
+            sel_h = sel_s[h_of[sel_s] == h]
+            qi = (t_of[sel_h] - a) // bm
+            for i in np.unique(qi):
+                sel = sel_h[qi == i]
+                keys = a + kept_keys(keeps[s][h, i], e - a, bn)
+                if keys.size == 0:
+                    continue
+                o[sel], lse[sel] = attention_rows(bf16_bits_to_f64(np.asarray(q_bits)[t_of[sel], h]),
+                                                  bf16_bits_to_f64(np.asarray(k_bits)[keys, h]),
+                                                  bf16_bits_to_f64(np.asarray(v_bits)[keys, h]), scale)
+    if rows is None:
+        return o.reshape(H, T, d).transpose(1, 0, 2), lse.reshape(H, T)
+    return o, lse

@@ -13,8 +13,10 @@ import pytest
 import torch
 
 from oracle import attention_dense
-from oracle.block_sparse import (KEY_BLOCK, QUERY_BLOCK, attention_kept, decision_margin,
-                                 kept_pairs, pooled_means, proxy_logits, route_blocks)
+from oracle import attention_varlen
+from oracle.block_sparse import (KEY_BLOCK, QUERY_BLOCK, attention_kept, attention_kept_varlen, decision_margin,
+                                 kept_pairs, pooled_means, proxy_logits, route_blocks, route_blocks_varlen,
+                                 segment_tiles)
 
 
 def bits(x):
@@ -194,3 +196,51 @@ def test_kept_pairs_and_margin():
 
 def test_default_blocks_are_the_kernel_tiles():
     assert (QUERY_BLOCK, KEY_BLOCK) == (256, 64)
+
+
+def test_segment_tile_numbering():
+    cu = [0, 300, 300, 301, 1000]
+    np.testing.assert_array_equal(segment_tiles(cu, 256), [0, 2, 2, 3, 6])
+    np.testing.assert_array_equal(segment_tiles(cu, 64), [0, 5, 5, 6, 17])
+
+
+def test_varlen_routing_is_per_segment_dense_routing():
+    """A packed batch of segments routes and attends exactly as each segment alone would: the
+    varlen oracle on [a | b] equals the dense oracle on a and on b."""
+    rng = np.random.default_rng(21)
+    lens = [300, 1, 0, 520]
+    T, H, d = sum(lens), 2, 128
+    q, k, v = (bits(rng.standard_normal((T, H, d))) for _ in range(3))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    routes = route_blocks_varlen(q, k, cu, 0.0883883, 0.01, sink_tokens=64)
+    assert routes[2] is None
+    keeps = [None if r is None else r[0] for r in routes]
+    o, lse = attention_kept_varlen(q, k, v, cu, 0.0883883, keeps)
+    for s, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
+        if e == a:
+            continue
+        dq, dk, dv = (np.ascontiguousarray(x[a:e].transpose(1, 0, 2))[None] for x in (q, k, v))
+        keep, z, zmax = route_blocks(dq, dk, 0.0883883, 0.01, sink_tokens=64)
+        np.testing.assert_array_equal(keeps[s], keep[0])
+        od, ld = attention_kept(dq, dk, dv, 0.0883883, keep)
+        np.testing.assert_allclose(o[a:e], od[0].transpose(1, 0, 2), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lse[:, a:e], ld[0], rtol=1e-13)
+    # a length-1 segment keeps its only tile and returns its own value
+    np.testing.assert_array_equal(o[300], widen(v[300]))
+
+
+def test_varlen_infinite_tau_is_varlen_attention():
+    rng = np.random.default_rng(22)
+    lens = [129, 64, 7]
+    T = sum(lens)
+    q, k, v = (bits(rng.standard_normal((T, 3, 128))) for _ in range(3))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    keeps = [r[0] for r in route_blocks_varlen(q, k, cu, 0.0883883, math.inf)]
+    assert all(kp.all() for kp in keeps)
+    o, lse = attention_kept_varlen(q, k, v, cu, 0.0883883, keeps)
+    o_ref, lse_ref = attention_varlen(q, k, v, cu, 0.0883883)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-13)
+    rows = np.array([0, 128, 129, 3 * T - 1])
+    o_r, lse_r = attention_kept_varlen(q, k, v, cu, 0.0883883, keeps, rows=rows)
+    np.testing.assert_allclose(o_r, o.transpose(1, 0, 2).reshape(-1, 128)[rows], rtol=1e-12, atol=1e-15)
