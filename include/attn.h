@@ -236,6 +236,53 @@ int attn_block_route(const void* q, const void* k, int B, int H, int N, int d, f
 size_t attn_block_route_workspace_bytes(int B, int H, int N, int d);
 
 /*
+ * Block-skip attention on packed (varlen) batches: segment s = rows cu_seqlens[s] ..
+ * cu_seqlens[s+1]-1 of THD [total_tokens, H, 128] tensors, attended to within the segment
+ * only (as attn_fwd_varlen). Query tiles (256 rows) and key tiles (64 keys) are counted per
+ * segment from its first row, and query tiles are numbered segment by segment: tile i of
+ * segment s is g = sum over s' < s of ceil(len_s' / 256), plus i. List row (g * H + h) of
+ * kv_idx holds that tile's key-tile indices (counted from the segment's first key, ascending,
+ * below ceil(len_s / 64)); kv_cnt[g * H + h] their number. The lists hold
+ * attn_block_varlen_tiles(nseg, total_tokens) * H rows of attn_block_list_stride(total_tokens)
+ * entries. The routing rule is attn_block_route's, applied to each segment on its own.
+ */
+
+/* Upper bound of the number of query tiles of a packed batch: total_tokens / 256 + nseg. */
+int attn_block_varlen_tiles(int nseg, int total_tokens);
+
+/*
+ * Key-tile routing of a packed batch into kv_idx / kv_cnt (layout above), q and k BF16 THD.
+ * cu_seqlens: DEVICE int32 [nseg + 1] as attn_fwd_varlen takes it (not checked by the
+ * kernels; offsets outside [0, total_tokens] are clamped). tau, sink_tokens: as
+ * attn_block_route (sinks counted from each segment's first key). workspace: DEVICE scratch of
+ * attn_block_route_varlen_workspace_bytes(nseg, H, total_tokens, d) bytes, 256-byte aligned.
+ * total_tokens = 0 is a no-op; more than 983040 tokens return ATTN_ERR_UNSUPPORTED.
+ * Returns an attn_status_t.
+ */
+int attn_block_route_varlen(const void* q, const void* k, const int32_t* cu_seqlens, int nseg, int H,
+                            int total_tokens, int d, float scale, float tau, int sink_tokens, int32_t* kv_idx,
+                            int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_block_route_varlen needs (0 if the sizes are invalid). */
+size_t attn_block_route_varlen_workspace_bytes(int nseg, int H, int total_tokens, int d);
+
+/*
+ * Block-skip attention forward of a packed batch over given key-tile lists (layout above):
+ * as attn_fwd_varlen, except that each query tile attends to its listed key tiles only. With
+ * every tile listed the result equals attn_fwd_varlen bit for bit; a tile with kv_cnt <= 0
+ * gets O = 0 and LSE = -inf. workspace: DEVICE scratch of
+ * attn_fwd_block_sparse_varlen_workspace_bytes(nseg, H, total_tokens) bytes, 256-byte aligned
+ * (the varlen schedule and the tile numbering). Returns an attn_status_t.
+ */
+int attn_fwd_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                 int nseg, int H, int total_tokens, int d, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_block_sparse_varlen needs (0 if the sizes are invalid). */
+size_t attn_fwd_block_sparse_varlen_workspace_bytes(int nseg, int H, int total_tokens);
+
+/*
  * The dense guard of block-skip attention (host only): 1 if denoising step `step` of layer
  * `layer` should run dense attention -- step < dense_steps, or layer listed in dense_layers
  * ("a" or "a-b" inclusive items separated by commas, blanks allowed; NULL or "" lists none)

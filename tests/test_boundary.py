@@ -47,6 +47,13 @@ def lib():
     lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
     lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
     lib.attn_block_skip_use_dense.argtypes = [i32, i32, i32, ctypes.c_char_p]
+    lib.attn_block_varlen_tiles.argtypes = [i32, i32]
+    lib.attn_block_route_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.attn_block_route_varlen_workspace_bytes.restype = sz
+    lib.attn_block_route_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+    lib.attn_fwd_block_sparse_varlen_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.attn_fwd_block_sparse_varlen_workspace_bytes.restype = sz
+    lib.attn_fwd_block_sparse_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.restype = ctypes.c_char_p
     return lib
@@ -58,7 +65,9 @@ def test_header_declares_the_expected_api():
                  "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_qk_prologue",
                  "attn_linear_fwd", "attn_linear_workspace_bytes", "attn_block_list_stride",
                  "attn_block_route", "attn_block_route_workspace_bytes", "attn_fwd_block_sparse",
-                 "attn_block_skip_use_dense",
+                 "attn_block_skip_use_dense", "attn_block_varlen_tiles", "attn_block_route_varlen",
+                 "attn_block_route_varlen_workspace_bytes", "attn_fwd_block_sparse_varlen",
+                 "attn_fwd_block_sparse_varlen_workspace_bytes",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -354,3 +363,62 @@ def test_python_block_skip_guards_without_gpu():
     assert vd.block_skip_use_dense(0, 0, 1, "") and not vd.block_skip_use_dense(1, 3, 1, "0-2")
     with pytest.raises(ValueError):
         vd.block_skip_use_dense(1, 3, 1, "3-")
+
+
+# ---------------------------------------------------------------- packed block-skip
+VQ, VK, VV, VO, VL, VI, VC, VW, VCU = (0x10000000000 * (i + 1) for i in range(9))
+
+
+def route_v(lib, q=VQ, k=VK, cu=VCU, nseg=3, H=2, T=1000, d=128, scale=0.088, tau=0.01, sink=0, idx=VI, cnt=VC,
+            ws=VW, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_block_route_varlen_workspace_bytes(nseg, H, T, 128)
+    return lib.attn_block_route_varlen(q, k, cu, nseg, H, T, d, scale, tau, sink, idx, cnt, ws, wsb, None)
+
+
+def sparse_v(lib, q=VQ, k=VK, v=VV, o=VO, lse=VL, cu=VCU, idx=VI, cnt=VC, nseg=3, H=2, T=1000, d=128, scale=0.088,
+             ws=VW, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_fwd_block_sparse_varlen_workspace_bytes(nseg, H, T)
+    return lib.attn_fwd_block_sparse_varlen(q, k, v, o, lse, cu, idx, cnt, nseg, H, T, d, scale, ws, wsb, None)
+
+
+def test_varlen_block_sizes(lib):
+    assert lib.attn_block_varlen_tiles(3, 38048) == 38048 // 256 + 3
+    assert lib.attn_block_varlen_tiles(0, 100) == 0
+    a = lambda x: (x + 255) // 256 * 256
+    # tile offsets (two int arrays of nseg + 1), pooled query tiles, pooled key tiles
+    assert lib.attn_block_route_varlen_workspace_bytes(3, 2, 1000, 128) == \
+        2 * a(4 * 4) + a((1000 // 256 + 3) * 2 * 512) + (1000 // 64 + 3) * 2 * 512
+    assert lib.attn_block_route_varlen_workspace_bytes(3, 2, 1000, 64) == 0
+    assert lib.attn_fwd_block_sparse_varlen_workspace_bytes(3, 2, 1000) == \
+        lib.attn_fwd_varlen_workspace_bytes(3, 2, 1000) + 2 * a(4 * 4)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nseg=0), INVALID), (dict(H=0), INVALID), (dict(T=-1), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(tau=-1.0), INVALID), (dict(sink=-2), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(q=None), INVALID), (dict(cu=None), INVALID), (dict(cnt=None), INVALID),
+    (dict(T=983041), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=8), WORKSPACE), (dict(ws=VW + 8), WORKSPACE),
+    (dict(idx=VQ + 256), INVALID), (dict(ws=VC), INVALID), (dict(cnt=VCU), INVALID),
+])
+def test_route_varlen_validation(lib, kw, code):
+    assert route_v(lib, **kw) == code
+    assert lib.attn_last_error().decode()
+
+
+def test_varlen_empty_batch_is_a_no_op(lib):
+    assert route_v(lib, T=0, q=None, k=None, cu=None, idx=None, cnt=None, ws=None) == OK
+    assert sparse_v(lib, T=0, q=None, k=None, v=None, o=None, cu=None, idx=None, cnt=None, ws=None) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nseg=0), INVALID), (dict(H=0), INVALID), (dict(d=64), UNSUPPORTED), (dict(scale=math.inf), INVALID),
+    (dict(v=None), INVALID), (dict(cu=None), INVALID), (dict(idx=None), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=64), WORKSPACE),
+    (dict(o=VQ), INVALID), (dict(o=VI), INVALID), (dict(lse=VC), INVALID), (dict(ws=VCU), INVALID),
+])
+def test_block_sparse_varlen_validation(lib, kw, code):
+    assert sparse_v(lib, **kw) == code
+    assert lib.attn_last_error().decode()

@@ -196,3 +196,141 @@ def test_video_720p_routing_and_sampled_rows(vd, video_720p):
     o = f64_of(out).reshape(-1, 128)[rows]
     l = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
     check(o, o_ref, l, lse_ref, label="block-sparse video_720p tau=0.02 sampled rows")
+
+
+# ---------------------------------------------------------------- packed (varlen) batches
+from oracle.block_sparse import attention_kept_varlen, route_blocks_varlen  # noqa: E402
+from workloads import make_varlen, random_varlen  # noqa: E402
+
+
+def varlen_keeps(vd, kv_idx, kv_cnt, cu, H):
+    """Host lists -> per-segment keep [H, ntq_s, ntk_s] (None for empty segments), after
+    checking every list is ascending inside the segment's key tiles and padded."""
+    offs = vd.varlen_tile_offsets(list(cu))
+    out = []
+    for s in range(len(cu) - 1):
+        n = int(cu[s + 1] - cu[s])
+        if n == 0:
+            out.append(None)
+            continue
+        ntq, ntk = -(-n // 256), -(-n // 64)
+        keep = np.zeros((H, ntq, ntk), bool)
+        for i in range(ntq):
+            for h in range(H):
+                c = int(kv_cnt[offs[s] + i, h])
+                ids = kv_idx[offs[s] + i, h, :c]
+                assert 1 <= c <= ntk and np.all(np.diff(ids) > 0) and ids[0] >= 0 and ids[-1] < ntk
+                assert np.all(kv_idx[offs[s] + i, h, c:c + 8] == ntk)
+                keep[h, i, ids] = True
+        out.append(keep)
+    return out
+
+
+def check_route_varlen(keeps, q, k, cu, tau, sink):
+    ref = route_blocks_varlen(q, k, cu, SCALE, tau, sink)
+    n_diff = 0
+    for s, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
+        if ref[s] is None:
+            assert keeps[s] is None
+            continue
+        keep, z, zmax = ref[s]
+        diff = keeps[s] != keep
+        if diff.any():
+            qs = np.ascontiguousarray(q[a:e].transpose(1, 0, 2))[None]
+            ks = np.ascontiguousarray(k[a:e].transpose(1, 0, 2))[None]
+            band = np.abs(z - (zmax[..., None] - tau)) <= decision_margin(qs, ks, SCALE, tau)[0]
+            assert not (diff & ~band).any()
+            n_diff += int(diff.sum())
+    print(f"[route varlen] tau={tau} sink={sink}: {n_diff} tiles inside the FP32 band differ", flush=True)
+
+
+def run_varlen_route(vd, q, k, cu, tau, sink=0):
+    cu_d = dev_i32(cu)
+    kv_idx, kv_cnt = vd.block_route_varlen(dev(q), dev(k), cu_d, tau=tau, sink_tokens=sink, scale=SCALE)
+    torch.cuda.synchronize()
+    return cu_d, kv_idx, kv_cnt
+
+
+@pytest.mark.parametrize("lens,H,tau,sink", [
+    ((300, 1, 0, 520, 64), 3, 0.0, 0),      # a length-1 and an empty segment
+    ((300, 1, 0, 520, 64), 3, 0.01, 100),
+    ((1000,), 2, 0.008, 0),                  # one segment: the dense case
+    ((256, 257, 511), 2, math.inf, 0),
+])
+def test_varlen_route_and_attention_small(vd, lens, H, tau, sink):
+    q, k, v, cu = random_varlen(lens, H, seed=sum(lens) + H)
+    cu_d, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, tau, sink)
+    keeps = varlen_keeps(vd, kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), cu, H)
+    check_route_varlen(keeps, q, k, cu, tau, sink)
+    out, lse = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), cu_d, kv_idx, kv_cnt, scale=SCALE,
+                                               return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_kept_varlen(q, k, v, cu, SCALE, keeps)
+    check(f64_of(out), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref,
+          label=f"block-sparse varlen {lens} H{H} tau={tau} sink={sink}")
+
+
+def test_varlen_every_tile_listed_equals_varlen_bits(vd):
+    q, k, v, cu = random_varlen((700, 1, 64, 300), 3, seed=77)
+    cu_d, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, math.inf)
+    out, lse = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), cu_d, kv_idx, kv_cnt, scale=SCALE,
+                                               return_lse=True)
+    ref, lse_ref = vd.attn_fwd_varlen(dev(q), dev(k), dev(v), cu_d, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), bits_of(ref))
+    assert np.array_equal(lse.cpu().numpy(), lse_ref.cpu().numpy())
+
+
+def test_varlen_hook_with_caller_lists(vd):
+    """Caller lists: each tile keeps its segment's last key tile and tile 0; one tile keeps
+    nothing (O = 0, LSE = -inf)."""
+    lens, H = (600, 70, 300), 2
+    q, k, v, cu = random_varlen(lens, H, seed=88)
+    T = int(cu[-1])
+    (G, _, stride), _ = vd.varlen_list_shapes(len(lens), T, H)
+    offs = vd.varlen_tile_offsets(list(cu))
+    idx = np.full((G, H, stride), 0, np.int32)
+    cnt = np.zeros((G, H), np.int32)
+    keeps = []
+    for s, n in enumerate(lens):
+        ntq, ntk = -(-n // 256), -(-n // 64)
+        keep = np.zeros((H, ntq, ntk), bool)
+        for i in range(ntq):
+            for h in range(H):
+                ids = sorted({0, ntk - 1})
+                idx[offs[s] + i, h, :len(ids)] = ids
+                idx[offs[s] + i, h, len(ids):] = ntk
+                cnt[offs[s] + i, h] = len(ids)
+                keep[h, i, ids] = True
+        keeps.append(keep)
+    cnt[offs[0] + 1, 1] = 0            # rows 256..511 of segment 0, head 1
+    keeps[0][1, 1] = False
+    out, lse = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), dev_i32(cu), dev_i32(idx), dev_i32(cnt),
+                                               scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    o, l = f64_of(out), lse.cpu().numpy()
+    assert np.all(o[256:512, 1] == 0) and np.all(np.isneginf(l[1, 256:512]))
+    o_ref, lse_ref = attention_kept_varlen(q, k, v, cu, SCALE, keeps)
+    live = np.ones((T, H), bool)
+    live[256:512, 1] = False
+    check(o[live], o_ref[live], l.T[live].astype(np.float64), lse_ref.T[live], label="varlen hook")
+
+
+def test_packed_varlen_workload_sampled(vd):
+    """The packed workload (segments 30000 / 6000 / 2048, H = 24) at tau = 0.02: routing of
+    every tile against the oracle, attention on 384 seeded rows plus the last 16 rows."""
+    w = WORKLOADS["packed_varlen"]
+    q, k, v, cu = make_varlen(w)
+    T, H = q.shape[0], q.shape[1]
+    cu_d, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, 0.02)
+    keeps = varlen_keeps(vd, kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), cu, H)
+    check_route_varlen(keeps, q, k, cu, 0.02, 0)
+    out, lse = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), cu_d, kv_idx, kv_cnt, scale=SCALE,
+                                               return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(38)
+    rows = np.unique(np.concatenate([rng.choice(H * T, 384, replace=False), (H - 1) * T + np.arange(T - 16, T)]))
+    o_ref, lse_ref = attention_kept_varlen(q, k, v, cu, SCALE, keeps, rows=rows)
+    o = f64_of(out).transpose(1, 0, 2).reshape(-1, 128)[rows]
+    check(o, o_ref, lse.cpu().numpy().reshape(-1)[rows].astype(np.float64), lse_ref,
+          label="block-sparse packed_varlen tau=0.02 sampled rows")

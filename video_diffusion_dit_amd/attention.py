@@ -88,6 +88,16 @@ def load_library() -> ctypes.CDLL:
         lib.attn_block_route.restype = i32
         lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         lib.attn_fwd_block_sparse.restype = i32
+        lib.attn_block_varlen_tiles.argtypes = [i32, i32]
+        lib.attn_block_varlen_tiles.restype = i32
+        lib.attn_block_route_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.attn_block_route_varlen_workspace_bytes.restype = sz
+        lib.attn_block_route_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+        lib.attn_block_route_varlen.restype = i32
+        lib.attn_fwd_block_sparse_varlen_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.attn_fwd_block_sparse_varlen_workspace_bytes.restype = sz
+        lib.attn_fwd_block_sparse_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+        lib.attn_fwd_block_sparse_varlen.restype = i32
         lib.attn_block_skip_use_dense.argtypes = [i32, i32, i32, ctypes.c_char_p]
         lib.attn_block_skip_use_dense.restype = i32
         _lib = lib
@@ -437,3 +447,89 @@ def block_skip_use_dense(step: int, layer: int, dense_steps: int = 0, dense_laye
     if st < 0:
         _raise_for(lib, st)
     return bool(st)
+
+
+def _check_cu(q, cu_seqlens, cu_seqlens_host):
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dtype == torch.int32
+            and cu_seqlens.device == q.device and cu_seqlens.dim() == 1 and cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on q's device")
+    host = cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens.cpu().tolist()
+    if len(host) != cu_seqlens.numel():
+        raise ValueError("cu_seqlens_host does not match cu_seqlens")
+    return check_cu_seqlens(host, q.shape[0])
+
+
+def varlen_list_shapes(nseg: int, T: int, H: int):
+    """(kv_idx, kv_cnt) shapes of the packed-batch lists: [tiles, H, stride], [tiles, H], with
+    tiles = T // 256 + nseg (an upper bound; tile g of the numbering segment by segment)."""
+    lib = load_library()
+    tiles = int(lib.attn_block_varlen_tiles(nseg, T))
+    return (tiles, H, block_list_stride(max(T, 1))), (tiles, H)
+
+
+def varlen_tile_offsets(cu_host) -> list:
+    """First query tile of each segment in the numbering segment by segment (host lists)."""
+    out, acc = [], 0
+    for a, e in zip(cu_host[:-1], cu_host[1:]):
+        out.append(acc)
+        acc += -(-(int(e) - int(a)) // 256)
+    return out + [acc]
+
+
+def block_route_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, *, tau: float,
+                       sink_tokens: int = 0, scale: float | None = None, cu_seqlens_host=None):
+    """Key-tile lists of block-skip attention for a packed batch (THD BF16 [T, H, 128] q, k):
+    (kv_idx int32 [tiles, H, stride], kv_cnt int32 [tiles, H]); row g of the lists is query
+    tile g of the numbering segment by segment (see varlen_tile_offsets)."""
+    _check_tensors(q, k, k, 3)
+    T, H, d = q.shape
+    if d != 128:
+        raise ValueError(f"head dimension {d} is not supported (only 128)")
+    _check_cu(q, cu_seqlens, cu_seqlens_host)
+    nseg = cu_seqlens.numel() - 1
+    lib = load_library()
+    idx_shape, cnt_shape = varlen_list_shapes(nseg, T, H)
+    kv_idx = torch.empty(idx_shape, dtype=torch.int32, device=q.device)
+    kv_cnt = torch.empty(cnt_shape, dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        nbytes = int(lib.attn_block_route_varlen_workspace_bytes(nseg, H, T, d))
+        ws = _workspace(q.device, nbytes)
+        st = lib.attn_block_route_varlen(_ptr(q), _ptr(k), _ptr(cu_seqlens), nseg, H, T, d, _default_scale(d, scale),
+                                         float(tau), int(sink_tokens), _ptr(kv_idx), _ptr(kv_cnt), _ptr(ws),
+                                         ws.numel(), _stream_handle(q.device))
+    _raise_for(lib, st)
+    return kv_idx, kv_cnt
+
+
+def attn_fwd_block_sparse_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                                 kv_idx: torch.Tensor, kv_cnt: torch.Tensor, scale: float | None = None,
+                                 return_lse: bool = False, out: torch.Tensor | None = None, cu_seqlens_host=None):
+    """Packed-batch attention where query tile g (numbered segment by segment) of head h sees
+    only the key tiles kv_idx[g, h, :kv_cnt[g, h]] of its segment (the caller's own lists are
+    accepted: this is the hook). Returns out (BF16 [T, H, 128]) or (out, lse FP32 [H, T])."""
+    _check_tensors(q, k, v, 3)
+    T, H, d = q.shape
+    if d != 128:
+        raise ValueError(f"head dimension {d} is not supported (only 128)")
+    _check_cu(q, cu_seqlens, cu_seqlens_host)
+    nseg = cu_seqlens.numel() - 1
+    idx_shape, cnt_shape = varlen_list_shapes(nseg, T, H)
+    for name, t, shape in (("kv_idx", kv_idx, idx_shape), ("kv_cnt", kv_cnt, cnt_shape)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be an int32 tensor of shape {shape}")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on q's device")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    with torch.cuda.device(q.device):
+        nbytes = int(lib.attn_fwd_block_sparse_varlen_workspace_bytes(nseg, H, T))
+        ws = _workspace(q.device, nbytes)
+        st = lib.attn_fwd_block_sparse_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                                              _ptr(kv_idx), _ptr(kv_cnt), nseg, H, T, d, _default_scale(d, scale),
+                                              _ptr(ws), ws.numel(), _stream_handle(q.device))
+    _raise_for(lib, st)
+    return (out, lse) if return_lse else out

@@ -62,6 +62,20 @@ int hip_status(hipError_t e) {
     return fail(ATTN_ERR_HIP, hipGetErrorString(e));
 }
 
+// Checks shared by the two packed block-skip entry points (total_tokens >= 1 here).
+int check_varlen_lists(const int32_t* cu, const int32_t* kv_idx, const int32_t* kv_cnt, int nseg, int H,
+                              int total_tokens, size_t& idx_bytes, size_t& cnt_bytes) {
+    if (cu == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens must be a non-null device pointer");
+    if (kv_idx == nullptr || kv_cnt == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "kv_idx and kv_cnt must be non-null device pointers");
+    const long long rows = product((long long)attn_impl::varlen_tiles_q(nseg, total_tokens), H, 1, 1);
+    const long long entries = product(rows, attn_impl::block_list_stride(total_tokens), 1, 1);
+    if (rows < 0 || rows > INT_MAX || entries < 0) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    idx_bytes = (size_t)entries * 4;
+    cnt_bytes = (size_t)rows * 4;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,6 +272,108 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out
         return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx or kv_cnt");
     return hip_status(attn_impl::launch_block_sparse(q, k, v, out, lse, kv_idx, kv_cnt, B, H, N, scale,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+int attn_block_varlen_tiles(int nseg, int total_tokens) {
+    if (nseg <= 0 || total_tokens < 0) return 0;
+    const size_t t = attn_impl::varlen_tiles_q(nseg, total_tokens);
+    return t > (size_t)INT_MAX ? 0 : (int)t;
+}
+
+size_t attn_block_route_varlen_workspace_bytes(int nseg, int H, int total_tokens, int d) {
+    if (nseg <= 0 || H <= 0 || total_tokens < 0 || d != 128) return 0;
+    return attn_impl::route_varlen_workspace_bytes(nseg, H, total_tokens);
+}
+
+int attn_block_route_varlen(const void* q, const void* k, const int32_t* cu_seqlens, int nseg, int H,
+                            int total_tokens, int d, float scale, float tau, int sink_tokens, int32_t* kv_idx,
+                            int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (nseg <= 0) return fail(ATTN_ERR_INVALID_ARG, "nseg must be >= 1");
+    if (H <= 0) return fail(ATTN_ERR_INVALID_ARG, "H must be >= 1");
+    if (d <= 0) return fail(ATTN_ERR_INVALID_ARG, "d must be >= 1");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
+    if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (isnan(tau) || tau < 0.f) return fail(ATTN_ERR_INVALID_ARG, "tau must be >= 0 (+inf keeps every key tile)");
+    if (sink_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "sink_tokens must be >= 0");
+    if (total_tokens == 0) return ATTN_OK;
+    if (q == nullptr || k == nullptr) return fail(ATTN_ERR_INVALID_ARG, "q and k must be non-null device pointers");
+    const long long elems = product(total_tokens, H, d, 1);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    if ((total_tokens + attn_impl::tile_keys() - 1) / attn_impl::tile_keys() > attn_impl::route_max_tiles())
+        return fail(ATTN_ERR_UNSUPPORTED, "packed batch longer than the routing supports (route_max_tiles key tiles)");
+    size_t idx_bytes = 0, cnt_bytes = 0;
+    int st = check_varlen_lists(cu_seqlens, kv_idx, kv_cnt, nseg, H, total_tokens, idx_bytes, cnt_bytes);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn_impl::route_varlen_workspace_bytes(nseg, H, total_tokens);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_block_route_varlen_workspace_bytes()");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const size_t tb = (size_t)elems * 2;
+    const void* outs[3] = {kv_idx, kv_cnt, workspace};
+    const size_t outb[3] = {idx_bytes, cnt_bytes, need};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], outb[i], q, tb) || overlaps(outs[i], outb[i], k, tb) ||
+            overlaps(outs[i], outb[i], cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)))
+            return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt or workspace overlaps q, k or cu_seqlens");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outb[i], outs[j], outb[j]))
+                return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt and workspace must not overlap");
+    }
+    return hip_status(attn_impl::launch_block_route_varlen(q, k, cu_seqlens, nseg, H, total_tokens, scale, tau,
+                                                           sink_tokens, kv_idx, kv_cnt, workspace,
+                                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_fwd_block_sparse_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
+    if (nseg <= 0 || H <= 0 || total_tokens < 0) return 0;
+    return attn_impl::block_sparse_varlen_workspace_bytes(nseg, total_tokens);
+}
+
+int attn_fwd_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                 int nseg, int H, int total_tokens, int d, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (nseg <= 0) return fail(ATTN_ERR_INVALID_ARG, "nseg must be >= 1");
+    if (total_tokens == 0) {
+        if (H <= 0) return fail(ATTN_ERR_INVALID_ARG, "H must be >= 1");
+        if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+        if (d != 128) return fail(d <= 0 ? ATTN_ERR_INVALID_ARG : ATTN_ERR_UNSUPPORTED,
+                                  "only head dimension 128 is supported");
+        return ATTN_OK;
+    }
+    int st = check_common(q, k, v, out, H, d, scale);
+    if (st != ATTN_OK) return st;
+    const long long elems = product(total_tokens, H, d, 1);
+    if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    size_t idx_bytes = 0, cnt_bytes = 0;
+    st = check_varlen_lists(cu_seqlens, kv_idx, kv_cnt, nseg, H, total_tokens, idx_bytes, cnt_bytes);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn_impl::block_sparse_varlen_workspace_bytes(nseg, total_tokens);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_fwd_block_sparse_varlen_workspace_bytes()");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const size_t tb = (size_t)elems * 2, lb = (size_t)product(H, total_tokens, 1, 1) * 4;
+    st = check_aliasing(q, k, v, out, lse, tb, lb);
+    if (st != ATTN_OK) return st;
+    if (overlaps(out, tb, kv_idx, idx_bytes) || overlaps(out, tb, kv_cnt, cnt_bytes) ||
+        overlaps(lse, lb, kv_idx, idx_bytes) || overlaps(lse, lb, kv_cnt, cnt_bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx or kv_cnt");
+    const void* ins[7] = {q, k, v, out, lse, kv_idx, kv_cnt};
+    const size_t inb[7] = {tb, tb, tb, tb, lb, idx_bytes, cnt_bytes};
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(workspace, need, ins[i], inb[i]))
+            return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor argument");
+    if (overlaps(workspace, need, cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)))
+        return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps cu_seqlens");
+    return hip_status(attn_impl::launch_block_sparse_varlen(q, k, v, out, lse, cu_seqlens, kv_idx, kv_cnt, nseg,
+                                                            H, total_tokens, scale, workspace,
+                                                            static_cast<hipStream_t>(stream)));
 }
 
 int attn_block_skip_use_dense(int step, int layer, int dense_steps, const char* dense_layers) {

@@ -442,6 +442,50 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_varlen_kernel(VarlenArgs a) {
                      (long)a.H * D, n, t.y * BM, a.c, 0, (n + BN - 1) / BN, nullptr);
 }
 
+// Block-skip attention over a packed batch: the varlen schedule's entry (segment s, query
+// tile i) and head h attend to the key tiles of list row (off_q[s] + i) * H + h, key-tile
+// indices counted from the segment's first key (off_q: first query tile of each segment,
+// numbered segment by segment, as the routing writes them).
+struct SparseVarlenArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    bf16* o;
+    float* lse;
+    const int32_t* cu;
+    const char* ws;       // varlen schedule
+    const int* off_q;
+    const int32_t* kidx;
+    const int32_t* kcnt;
+    int nseg, H, T, stride;
+    float c;
+};
+
+__global__ __launch_bounds__(NT, 1) void attn_fwd_block_sparse_varlen_kernel(SparseVarlenArgs a) {
+    const int e = blockIdx.x / a.H, h = blockIdx.x - e * a.H;
+    if (e >= *reinterpret_cast<const int*>(a.ws)) return;
+    const int2 t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
+    const int start = min(max(a.cu[t.x], 0), a.T);
+    const int n = seg_len(a.cu, t.x, a.T);
+    if (t.y * BM >= n) return;
+    const long base = ((long)start * a.H + h) * D;
+    const long row = ((long)a.off_q[t.x] + t.y) * a.H + h;
+    const int cnt = min(a.kcnt[row], (n + BN - 1) / BN);
+    float* lse = a.lse ? a.lse + (long)h * a.T + start : nullptr;
+    if (cnt <= 0) {
+        const int r = t.y * BM + (int)threadIdx.x;
+        if (r < n) {
+            uint4* orow = reinterpret_cast<uint4*>(a.o + base + (long)r * a.H * D);
+#pragma unroll
+            for (int i = 0; i < D / 8; ++i) orow[i] = make_uint4(0, 0, 0, 0);
+            if (lse != nullptr) lse[r] = -INFINITY;
+        }
+        return;
+    }
+    attn_rows<true>(a.q + base, a.k + base, a.v + base, a.o + base, lse, (long)a.H * D, n, t.y * BM, a.c, 0, cnt,
+                    nullptr, a.kidx + row * a.stride);
+}
+
 inline float log2e_scale(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
 }  // namespace
@@ -557,6 +601,42 @@ hipError_t launch_block_sparse(const void* q, const void* k, const void* v, void
 
 size_t varlen_workspace_bytes(int nseg, int total_tokens) {
     return ws_list_offset(nseg) + ws_align(sizeof(int2) * (size_t)max_entries(nseg, total_tokens));
+}
+
+size_t block_sparse_varlen_workspace_bytes(int nseg, int total_tokens) {
+    return varlen_workspace_bytes(nseg, total_tokens) + tile_offsets_bytes(nseg);
+}
+
+hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                                      const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                      int nseg, int H, int total_tokens, float scale, void* workspace,
+                                      hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    hipLaunchKernelGGL(build_varlen_schedule, dim3(1), dim3(1024), 0, stream, cu_seqlens, nseg, total_tokens, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    char* offs = ws + varlen_workspace_bytes(nseg, total_tokens);
+    e = launch_tile_offsets(cu_seqlens, nseg, total_tokens, offs, stream);
+    if (e != hipSuccess) return e;
+    SparseVarlenArgs a;
+    a.q = static_cast<const bf16*>(q);
+    a.k = static_cast<const bf16*>(k);
+    a.v = static_cast<const bf16*>(v);
+    a.o = static_cast<bf16*>(out);
+    a.lse = lse;
+    a.cu = cu_seqlens;
+    a.ws = ws;
+    a.off_q = reinterpret_cast<const int*>(offs);
+    a.kidx = kv_idx;
+    a.kcnt = kv_cnt;
+    a.nseg = nseg;
+    a.H = H;
+    a.T = total_tokens;
+    a.stride = block_list_stride(total_tokens);
+    a.c = log2e_scale(scale);
+    const long grid = max_entries(nseg, total_tokens) * H;
+    hipLaunchKernelGGL(attn_fwd_block_sparse_varlen_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_varlen(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -46,6 +46,23 @@ hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N,
                               int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
                               hipStream_t stream);
 
+// Packed (varlen) block-skip: query tiles (256 rows) and key tiles (64 keys) counted per
+// segment and numbered segment by segment; at most varlen_tiles_q(nseg, T) query tiles.
+// Lists: kv_idx [tiles_q * H][block_list_stride(T)], kv_cnt [tiles_q * H], row (tile * H + h).
+size_t varlen_tiles_q(int nseg, int T);
+size_t tile_offsets_bytes(int nseg);
+// first query and key tile of each segment ([nseg + 1] ints each, 256-byte aligned) into dst
+hipError_t launch_tile_offsets(const int32_t* cu, int nseg, int T, void* dst, hipStream_t stream);
+size_t route_varlen_workspace_bytes(int nseg, int H, int T);
+hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t* cu, int nseg, int H, int T,
+                                     float scale, float tau, int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt,
+                                     void* workspace, hipStream_t stream);
+size_t block_sparse_varlen_workspace_bytes(int nseg, int total_tokens);
+hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                                      const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                      int nseg, int H, int total_tokens, float scale, void* workspace,
+                                      hipStream_t stream);
+
 // Workspace layout of the varlen schedule (bytes).
 size_t varlen_workspace_bytes(int nseg, int total_tokens);
 

@@ -165,6 +165,163 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- packed (varlen) batches
+// Segment s = rows cu[s] .. cu[s+1]-1 of THD [T, H, 128] tensors (row stride H*128). Query
+// tiles (256 rows) and key tiles (64 keys) are counted per segment from its first row and
+// numbered segment by segment: tile i of segment s is tile off[s] + i.
+
+__device__ __forceinline__ int seg_bound(const int32_t* cu, int s, int T) { return min(max(cu[s], 0), T); }
+
+// off_q[s] / off_k[s]: first query / key tile of segment s ([nseg + 1], last = totals). One
+// workgroup: each thread sums a contiguous run of segments, a serial scan orders the runs.
+__global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t* __restrict__ cu, int nseg, int T,
+                                                            int* __restrict__ off_q, int* __restrict__ off_k) {
+    __shared__ int pq[1024], pk[1024];
+    const int tid = threadIdx.x;
+    const int per = (nseg + 1023) / 1024;
+    const int s0 = min(tid * per, nseg), s1 = min(s0 + per, nseg);
+    int sq = 0, sk = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int a = seg_bound(cu, s, T), e = max(seg_bound(cu, s + 1, T), a);
+        sq += (e - a + BMQ - 1) / BMQ;
+        sk += (e - a + BNK - 1) / BNK;
+    }
+    pq[tid] = sq;
+    pk[tid] = sk;
+    __syncthreads();
+    if (tid == 0) {
+        int aq = 0, ak = 0;
+        for (int i = 0; i < 1024; ++i) {
+            const int vq = pq[i], vk = pk[i];
+            pq[i] = aq;
+            pk[i] = ak;
+            aq += vq;
+            ak += vk;
+        }
+        off_q[nseg] = aq;
+        off_k[nseg] = ak;
+    }
+    __syncthreads();
+    int aq = pq[tid], ak = pk[tid];
+    for (int s = s0; s < s1; ++s) {
+        off_q[s] = aq;
+        off_k[s] = ak;
+        const int a = seg_bound(cu, s, T), e = max(seg_bound(cu, s + 1, T), a);
+        aq += (e - a + BMQ - 1) / BMQ;
+        ak += (e - a + BNK - 1) / BNK;
+    }
+}
+
+// segment holding tile g: the last s with off[s] <= g (off ascending, off[0] = 0)
+__device__ __forceinline__ int tile_segment(const int* off, int nseg, int g) {
+    int lo = 0, hi = nseg;   // off[lo] <= g < off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= g) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Mean of one RB-row tile of one head: workgroup (tile g, head h); thread (row lane rl, chunk
+// ch) sums rows rl, rl+16, ...; the 16 row lanes are added in order through LDS.
+template <int RB>
+__global__ __launch_bounds__(256) void pool_varlen_kernel(const bf16* __restrict__ x, float* __restrict__ out,
+                                                          const int32_t* __restrict__ cu, const int* __restrict__ off,
+                                                          int nseg, int H, int T) {
+    __shared__ float red[16][D];
+    const int g = blockIdx.x / H, h = blockIdx.x - g * H;
+    if (g >= off[nseg]) return;
+    const int s = tile_segment(off, nseg, g);
+    const int a = seg_bound(cu, s, T), e = max(seg_bound(cu, s + 1, T), a);
+    const int r0 = a + RB * (g - off[s]), rows = min(RB, e - r0);
+    const int tid = threadIdx.x, ch = tid & 15, rl = tid >> 4;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = rl; r < rows; r += 16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + ((long)(r0 + r) * H + h) * D + 8 * ch);
+        acc[0] += bf16_lo(u.x);
+        acc[1] += bf16_hi(u.x);
+        acc[2] += bf16_lo(u.y);
+        acc[3] += bf16_hi(u.y);
+        acc[4] += bf16_lo(u.z);
+        acc[5] += bf16_hi(u.z);
+        acc[6] += bf16_lo(u.w);
+        acc[7] += bf16_hi(u.w);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[rl][8 * ch + i] = acc[i];
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.f;
+        for (int j = 0; j < 16; ++j) sum += red[j][tid];
+        out[((long)g * H + h) * D + tid] = sum / (float)rows;
+    }
+}
+
+struct RouteVarlenArgs {
+    const float* qbar;   // [tiles_q][H][128]
+    const float* kbar;   // [tiles_k][H][128]
+    const int* off_q;
+    const int* off_k;
+    int32_t* kidx;       // [tiles_q * H][stride]
+    int32_t* kcnt;       // [tiles_q * H]
+    int nseg, H, stride, nsink;
+    float scale, tau;
+};
+
+// One workgroup per (query tile g, head h): the proxies of the segment's key tiles into LDS,
+// then the threshold and the ordered compaction as route_kernel does.
+__global__ __launch_bounds__(256) void route_varlen_kernel(RouteVarlenArgs a) {
+    extern __shared__ float zs[];
+    __shared__ float qs[D];
+    __shared__ float red[4];
+    __shared__ int wsum[4];
+    const int g = blockIdx.x / a.H, h = blockIdx.x - g * a.H;
+    if (g >= a.off_q[a.nseg]) return;
+    const int s = tile_segment(a.off_q, a.nseg, g);
+    const int k0 = a.off_k[s], ntk = a.off_k[s + 1] - k0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid < D) qs[tid] = a.qbar[((long)g * a.H + h) * D + tid];
+    __syncthreads();
+    for (int J = tid; J < ntk; J += 256) {
+        const float4* kr = reinterpret_cast<const float4*>(a.kbar + ((long)(k0 + J) * a.H + h) * D);
+        float z = 0.f;
+#pragma unroll 4
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+            const float4 kv = kr[c4];
+            z = fmaf(qs[4 * c4 + 0], kv.x, z);
+            z = fmaf(qs[4 * c4 + 1], kv.y, z);
+            z = fmaf(qs[4 * c4 + 2], kv.z, z);
+            z = fmaf(qs[4 * c4 + 3], kv.w, z);
+        }
+        zs[J] = z * a.scale;
+    }
+    __syncthreads();
+    float m = -INFINITY;
+    for (int J = tid; J < ntk; J += 256) m = fmaxf(m, zs[J]);
+    const float thr = block_max(m, red) - a.tau;
+    const int run = (ntk + 255) / 256;
+    const int j0 = min(tid * run, ntk), j1 = min(j0 + run, ntk);
+    int cnt = 0;
+    for (int J = j0; J < j1; ++J) cnt += (zs[J] >= thr || J < a.nsink) ? 1 : 0;
+    int incl = cnt;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int off = incl - cnt;
+    for (int k = 0; k < wv; ++k) off += wsum[k];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    const long item = (long)g * a.H + h;
+    int32_t* dst = a.kidx + item * a.stride;
+    for (int J = j0; J < j1; ++J)
+        if (zs[J] >= thr || J < a.nsink) dst[off++] = J;
+    if (tid < LIST_PAD) dst[total + tid] = ntk;
+    if (tid == 0) a.kcnt[item] = total;
+}
+
 }  // namespace
 
 namespace attn_impl {
@@ -177,6 +334,62 @@ size_t route_workspace_bytes(int B, int H, int N) {
 }
 
 int route_max_tiles() { return ROUTE_LDS_LIMIT / (int)sizeof(float); }
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t varlen_tiles_q(int nseg, int T) { return (size_t)T / BMQ + (size_t)nseg; }
+static size_t varlen_tiles_k(int nseg, int T) { return (size_t)T / BNK + (size_t)nseg; }
+
+size_t tile_offsets_bytes(int nseg) { return 2 * align256(sizeof(int) * ((size_t)nseg + 1)); }
+
+hipError_t launch_tile_offsets(const int32_t* cu, int nseg, int T, void* dst, hipStream_t stream) {
+    int* off_q = static_cast<int*>(dst);
+    int* off_k = reinterpret_cast<int*>(static_cast<char*>(dst) + align256(sizeof(int) * ((size_t)nseg + 1)));
+    hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(1024), 0, stream, cu, nseg, T, off_q, off_k);
+    return hipGetLastError();
+}
+
+size_t route_varlen_workspace_bytes(int nseg, int H, int T) {
+    return tile_offsets_bytes(nseg) + align256(varlen_tiles_q(nseg, T) * H * D * sizeof(float)) +
+           varlen_tiles_k(nseg, T) * H * D * sizeof(float);
+}
+
+hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t* cu, int nseg, int H, int T,
+                                     float scale, float tau, int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt,
+                                     void* workspace, hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e = launch_tile_offsets(cu, nseg, T, ws, stream);
+    if (e != hipSuccess) return e;
+    const int* off_q = reinterpret_cast<const int*>(ws);
+    const int* off_k = reinterpret_cast<const int*>(ws + align256(sizeof(int) * ((size_t)nseg + 1)));
+    const size_t tq = varlen_tiles_q(nseg, T), tk = varlen_tiles_k(nseg, T);
+    float* qbar = reinterpret_cast<float*>(ws + tile_offsets_bytes(nseg));
+    float* kbar = reinterpret_cast<float*>(ws + tile_offsets_bytes(nseg) + align256(tq * H * D * sizeof(float)));
+    hipLaunchKernelGGL(pool_varlen_kernel<BMQ>, dim3((unsigned)(tq * H)), dim3(256), 0, stream,
+                       static_cast<const bf16*>(q), qbar, cu, off_q, nseg, H, T);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pool_varlen_kernel<BNK>, dim3((unsigned)(tk * H)), dim3(256), 0, stream,
+                       static_cast<const bf16*>(k), kbar, cu, off_k, nseg, H, T);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    RouteVarlenArgs a;
+    a.qbar = qbar;
+    a.kbar = kbar;
+    a.off_q = off_q;
+    a.off_k = off_k;
+    a.kidx = kv_idx;
+    a.kcnt = kv_cnt;
+    a.nseg = nseg;
+    a.H = H;
+    a.stride = (T + BNK - 1) / BNK + LIST_PAD;
+    a.nsink = sink_tokens > 0 ? (int)(((long)sink_tokens + BNK - 1) / BNK) : 0;
+    a.scale = scale;
+    a.tau = tau;
+    const size_t lds = (size_t)((T + BNK - 1) / BNK) * sizeof(float);
+    hipLaunchKernelGGL(route_varlen_kernel, dim3((unsigned)(tq * H)), dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N, float scale, float tau,
                               int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
