@@ -420,6 +420,98 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
     return rec
 
 
+def time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, dense_ms: float) -> dict:
+    """Block-skip attention on the packed workload (routing per segment, then the block-sparse
+    varlen pass) at --block-skip-tau; FLOP counts the (query, key) pairs of the kept tiles."""
+    import numpy as np
+    import torch
+
+    tau = args.block_skip_tau
+    cu_d = torch.from_numpy(np.asarray(cu, np.int32)).to(q.device)
+    cu_h = [int(x) for x in cu]
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        res = None
+        for i in range(n):
+            starts[i].record(stream)
+            res = fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)], res
+
+    route_ms, (kv_idx, kv_cnt) = timed(lambda: vd.block_route_varlen(q, k, cu_d, tau=tau, scale=w.scale,
+                                                                     cu_seqlens_host=cu_h), args.block_skip_steps)
+    sparse_ms, _ = timed(lambda: vd.attn_fwd_block_sparse_varlen(q, k, v, cu_d, kv_idx, kv_cnt, scale=w.scale,
+                                                                 out=out, cu_seqlens_host=cu_h), args.block_skip_steps)
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    offs = vd.varlen_tile_offsets(cu_h)
+    pairs, full, keeps = 0.0, 0.0, []
+    for s_, (a, e) in enumerate(zip(cu_h[:-1], cu_h[1:])):
+        n = e - a
+        if n == 0:
+            keeps.append(None)
+            continue
+        ntq, ntk = -(-n // 256), -(-n // 64)
+        rows = np.minimum(256, n - 256 * np.arange(ntq))
+        tkeys = np.minimum(64, n - 64 * np.arange(ntk))
+        keep = np.zeros((w.H, ntq, ntk), bool)
+        for i in range(ntq):
+            for h in range(w.H):
+                keep[h, i, idx[offs[s_] + i, h, :cnt[offs[s_] + i, h]]] = True
+        keeps.append(keep)
+        pairs += float((keep * rows[None, :, None] * tkeys[None, None, :]).sum())
+        full += float(w.H) * n * n
+    avg_s, avg_r = float(np.mean(sparse_ms)), float(np.mean(route_ms))
+    flops = 4.0 * w.d * pairs
+    tf = flops / (avg_s * 1e-3) / 1e12
+    rec = {
+        "kernel": "attn_fwd_block_sparse_varlen_kernel",
+        "what": "block-skip attention on the packed batch: per-segment pooled-proxy routing of 64-key tiles per "
+                "256-row query tile (keep z >= max z - tau), then exact softmax over the kept tiles",
+        "tau": tau, "density": round(pairs / full, 4), "bound": "mfma",
+        "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+        "flops_per_call": flops, "traffic": None,
+        "ms": {"sparse": round(avg_s, 4), "sparse_min": round(min(sparse_ms), 4),
+               "sparse_max": round(max(sparse_ms), 4), "route": round(avg_r, 4)},
+        "speedup_vs_dense_call": round(dense_ms / (avg_s + avg_r), 3),
+        "steps": args.block_skip_steps,
+    }
+    print(f"[bench] block-skip varlen tau={tau}: density {pairs / full:.4f}, route {avg_r:.3f} ms, sparse "
+          f"{avg_s:.3f} ms -> {tf:.1f} TFLOP/s on kept pairs ({100 * tf / PEAK_BF16_TFLOPS:.1f} % of peak), "
+          f"{dense_ms / (avg_s + avg_r):.2f}x the dense call", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        from oracle import bf16_bits_to_f64, compare
+        from oracle.block_sparse import attention_kept_varlen
+        T = int(cu_h[-1])
+        rows_s = np.random.default_rng(3).choice(w.H * T, 128, replace=False)
+        t1 = time.perf_counter()
+        o_ref, _ = attention_kept_varlen(qb, kb, vb, cu_h, w.scale, keeps, rows=rows_s)
+        cpu_s = time.perf_counter() - t1
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16).transpose(1, 0, 2).reshape(-1, w.d)[rows_s]
+        m = compare(bf16_bits_to_f64(got), o_ref)
+        rec["parity"] = {"rel_l2": round(float(m["rel_l2"]), 8), "n_elems": int(m["n_elems"]), "ok": bool(m["ok"])}
+        h_r, t_r = rows_s // T, rows_s % T
+        seg = np.searchsorted(np.asarray(cu_h), t_r, side="right") - 1
+        kept_keys = 0.0
+        for hh, tt, ss in zip(h_r, t_r, seg):
+            n = cu_h[ss + 1] - cu_h[ss]
+            tkeys = np.minimum(64, n - 64 * np.arange(-(-n // 64)))
+            kept_keys += float((keeps[ss][hh, (tt - cu_h[ss]) // 256] * tkeys).sum())
+        rec["cpu_baseline"] = {"value": round(4.0 * w.d * kept_keys / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle_cores(), "kind": "oracle",
+                               "sample": f"128 seeded query rows over their kept keys, FP64 NumPy, {cpu_s:.2f} s"}
+    del out, kv_idx, kv_cnt
+    torch.cuda.empty_cache()
+    return rec
+
+
 def oracle_cores() -> int:
     """Threads the FP64 oracle's BLAS calls use on this host."""
     from threadpoolctl import threadpool_info
@@ -578,6 +670,8 @@ def main() -> int:
 
     if w.kind == "dense" and args.block_skip_steps > 0:
         result["block_skip"] = time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, avg_kernel_ms)
+    elif args.block_skip_steps > 0:
+        result["block_skip"] = time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, avg_kernel_ms)
     if w.grid is not None and args.prologue_steps > 0:
         result["prologue"] = time_prologue(args, w, vd, dev)
     if w.grid is not None and args.linear_steps > 0:
