@@ -172,6 +172,23 @@ def test_deterministic(vd):
     assert np.array_equal(bits_of(a), bits_of(b))
 
 
+def test_long_sequence_routes_one_query_tile_per_workgroup(vd):
+    """N = 260000: 4063 key tiles, more proxies than four query tiles' worth fit in a
+    workgroup's LDS, so the routing takes one query tile per workgroup. Routing against the
+    oracle over every tile; attention on 128 seeded rows and the last 32."""
+    N = 260000
+    q, k, v = random_dense(1, 1, N, seed=260)
+    kv_idx, kv_cnt = route(vd, q, k, 0.01)
+    keep_gpu = lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), -(-N // 64))
+    check_route(keep_gpu, q, k, 0.01, 0)
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(26).choice(N, 128, replace=False), np.arange(N - 32, N)]))
+    o_ref, lse_ref = attention_kept(q, k, v, SCALE, keep_gpu, rows=rows)
+    check(f64_of(out).reshape(-1, 128)[rows], o_ref, lse.cpu().numpy().reshape(-1)[rows].astype(np.float64),
+          lse_ref, label="block-sparse N=260000 tau=0.01 sampled rows")
+
+
 @pytest.fixture(scope="module")
 def video_720p():
     return make_dense(WORKLOADS["video_720p"])

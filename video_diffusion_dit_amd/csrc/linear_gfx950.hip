@@ -236,7 +236,16 @@ struct StageOffsets {
     unsigned v[4];
 };
 
-__device__ __forceinline__ StageOffsets stage_offsets(long row_stride, int w, int lane) {
+// The lane index passed through an empty asm: values derived from it are recomputed where
+// they are used (a few VALU ops) instead of being hoisted out of the sub-block loop, where
+// they would not fit in registers and would be spilled.
+__device__ __forceinline__ int fresh_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
+__device__ __forceinline__ StageOffsets stage_offsets(long row_stride, int w, int lane_in) {
+    const int lane = fresh_lane(lane_in);
     StageOffsets o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -318,7 +327,8 @@ __device__ __forceinline__ void write_den(const QRows& qrw, const float* ksum_s,
         p = row16_sum(p);
         mine = c == i ? p : mine;
     }
-    if (c < NI) den_s[RPW * w + 4 * c + (lane >> 4)] = mine + eps;
+    const int fl = fresh_lane(lane);
+    if (c < NI) den_s[RPW * w + 4 * (fl & 15) + (fl >> 4)] = mine + eps;
 }
 
 __global__ __launch_bounds__(NT, LIN_OUT_SUB == 128 ? 2 : 1) void linear_out_kernel(LinearArgs a) {
@@ -343,7 +353,8 @@ __global__ __launch_bounds__(NT, LIN_OUT_SUB == 128 ? 2 : 1) void linear_out_ker
     };
     // per-lane offsets (recomputed where used: a few VALU ops, cheaper than keeping them live)
     auto qoff = [&]() {
-        return (unsigned)((((long)(RPW * w + (lane >> 4))) * row_stride + 8 * (lane & 15)) * 2);
+        const int l = fresh_lane(lane);
+        return (unsigned)((((long)(RPW * w + (l >> 4))) * row_stride + 8 * (l & 15)) * 2);
     };
     const unsigned step4 = (unsigned)(4 * row_stride * 2), step16 = 4 * step4;
     stage_qrot(rows_rsrc(a.qr + base + (long)n0 * row_stride, a.N - n0, row_stride), step16,
