@@ -357,9 +357,13 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
         torch.cuda.synchronize()
         return [s.elapsed_time(e) for s, e in zip(starts, ends)], res
 
-    route_ms, (kv_idx, kv_cnt) = timed(lambda: vd.block_route(q, k, tau=tau, scale=w.scale), args.block_skip_steps)
-    sparse_ms, _ = timed(lambda: vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out),
-                         args.block_skip_steps)
+    order_name = "item" if args.block_skip_order == "auto" else args.block_skip_order
+    lpt = order_name == "longest-first"
+    route_ms, routed = timed(lambda: vd.block_route(q, k, tau=tau, scale=w.scale, with_order=lpt),
+                             args.block_skip_steps)
+    kv_idx, kv_cnt, order = routed if lpt else (*routed, None)
+    sparse_ms, _ = timed(lambda: vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out,
+                                                          order=order), args.block_skip_steps)
     ntq, ntk = -(-w.N // 256), -(-w.N // 64)
     cnt = kv_cnt.cpu().numpy().astype(np.int64)
     idx = kv_idx.cpu().numpy()
@@ -376,6 +380,7 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
         "what": "block-skip attention: pooled-proxy routing of 64-key tiles per 256-row query tile "
                 "(keep z >= max z - tau), then exact softmax attention over the kept tiles",
         "tau": tau,
+        "order": order_name,
         "density": round(density, 4),
         "bound": "mfma",
         "achieved": round(tf, 2),
@@ -410,12 +415,12 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
         rec["cpu_baseline"] = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle_cores(), "kind": "oracle",
                                "sample": f"128 seeded query rows over their kept keys, FP64 NumPy, {cpu_s:.2f} s"}
-        vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out)
+        vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=w.scale, out=out, order=order)
         got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, w.d)[rows_s]
         from oracle import bf16_bits_to_f64
         m = compare(bf16_bits_to_f64(got), o_ref)
         rec["parity"] = {"rel_l2": round(float(m["rel_l2"]), 8), "n_elems": int(m["n_elems"]), "ok": bool(m["ok"])}
-    del out, lse, kv_idx, kv_cnt
+    del out, lse, kv_idx, kv_cnt, order
     torch.cuda.empty_cache()
     return rec
 
@@ -446,10 +451,14 @@ def time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, dense_ms: flo
         torch.cuda.synchronize()
         return [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)], res
 
-    route_ms, (kv_idx, kv_cnt) = timed(lambda: vd.block_route_varlen(q, k, cu_d, tau=tau, scale=w.scale,
-                                                                     cu_seqlens_host=cu_h), args.block_skip_steps)
+    order_name = "longest-first" if args.block_skip_order == "auto" else args.block_skip_order
+    lpt = order_name == "longest-first"
+    route_ms, routed = timed(lambda: vd.block_route_varlen(q, k, cu_d, tau=tau, scale=w.scale, cu_seqlens_host=cu_h,
+                                                           with_order=lpt), args.block_skip_steps)
+    kv_idx, kv_cnt, order = routed if lpt else (*routed, None)
     sparse_ms, _ = timed(lambda: vd.attn_fwd_block_sparse_varlen(q, k, v, cu_d, kv_idx, kv_cnt, scale=w.scale,
-                                                                 out=out, cu_seqlens_host=cu_h), args.block_skip_steps)
+                                                                 out=out, cu_seqlens_host=cu_h, order=order),
+                         args.block_skip_steps)
     idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
     offs = vd.varlen_tile_offsets(cu_h)
     pairs, full, keeps = 0.0, 0.0, []
@@ -475,7 +484,7 @@ def time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, dense_ms: flo
         "kernel": "attn_fwd_block_sparse_varlen_kernel",
         "what": "block-skip attention on the packed batch: per-segment pooled-proxy routing of 64-key tiles per "
                 "256-row query tile (keep z >= max z - tau), then exact softmax over the kept tiles",
-        "tau": tau, "density": round(pairs / full, 4), "bound": "mfma",
+        "tau": tau, "order": order_name, "density": round(pairs / full, 4), "bound": "mfma",
         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
         "flops_per_call": flops, "traffic": None,
         "ms": {"sparse": round(avg_s, 4), "sparse_min": round(min(sparse_ms), 4),
@@ -553,6 +562,9 @@ def main() -> int:
                     help="dense workloads: timed calls of block-skip attention on the same inputs (0: skip)")
     ap.add_argument("--block-skip-tau", type=float, default=0.02,
                     help="routing threshold of the timed block-skip calls")
+    ap.add_argument("--block-skip-order", choices=("auto", "longest-first", "item"), default="auto",
+                    help="dispatch order of the block-sparse pass: the routing's longest-first order, item "
+                         "order, or auto (item order on dense batches, longest-first on packed ones)")
     ap.add_argument("--profile-command", default="",
                     help="the command lines that produced the counter files (recorded in the profile)")
     args = ap.parse_args()

@@ -193,6 +193,12 @@ size_t attn_linear_workspace_bytes(int B, int N, int H, int d);
  *   kv_cnt : int32 [B*H*ntq].
  * A list that breaks these rules is processed memory-safely (each index is clamped to
  * [previous index, ntk], the count to [0, ntk]) with an unspecified result.
+ *   order  : int32 [B*H*ntq] or NULL: the order in which the items are started (the routing
+ *            writes the items sorted by list length, longest first, so that the last round of
+ *            the GPU holds short ones). NULL starts them in item order, which keeps the
+ *            workgroups in flight within one or two heads; on the 720p grid that measured
+ *            faster than longest-first. Results do not depend on it; entries outside the
+ *            item range are clamped.
  */
 
 /* Row stride of kv_idx in entries: ceil(N/64) + 8 (0 if N <= 0). */
@@ -208,8 +214,8 @@ int attn_block_list_stride(int N);
  * Returns an attn_status_t.
  */
 int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
-                          const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N, int d,
-                          float scale, void* stream);
+                          const int32_t* kv_idx, const int32_t* kv_cnt, const int32_t* order, int B, int H,
+                          int N, int d, float scale, void* stream);
 
 /*
  * Key-tile routing of block-skip attention: writes kv_idx and kv_cnt for dense [B, H, N, 128]
@@ -223,13 +229,16 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out
  *   sink_tokens : >= 0; the key tiles holding keys 0 .. sink_tokens-1 are always kept.
  *   kv_idx, kv_cnt : DEVICE outputs (sizes above); entries after each count up to 8 are set
  *                 to ntk.
+ *   order       : DEVICE output [B*H*ntq] (the items by list length, longest first, by a
+ *                 counting sort over 4096 bins of length; items in one bin, which holds one
+ *                 length while ntk <= 4095, in no fixed order), or NULL to skip it.
  *   workspace   : DEVICE scratch of attn_block_route_workspace_bytes(B, H, N, d) bytes,
  *                 256-byte aligned (the pooled tiles); no initialisation needed.
  * Sequences of more than 15360 key tiles (N > 983040) return ATTN_ERR_UNSUPPORTED.
  * Returns an attn_status_t.
  */
 int attn_block_route(const void* q, const void* k, int B, int H, int N, int d, float scale, float tau,
-                     int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                     int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, int32_t* order, void* workspace,
                      size_t workspace_bytes, void* stream);
 
 /* Workspace bytes attn_block_route needs (0 if the sizes are invalid). */
@@ -254,14 +263,16 @@ int attn_block_varlen_tiles(int nseg, int total_tokens);
  * Key-tile routing of a packed batch into kv_idx / kv_cnt (layout above), q and k BF16 THD.
  * cu_seqlens: DEVICE int32 [nseg + 1] as attn_fwd_varlen takes it (not checked by the
  * kernels; offsets outside [0, total_tokens] are clamped). tau, sink_tokens: as
- * attn_block_route (sinks counted from each segment's first key). workspace: DEVICE scratch of
+ * attn_block_route (sinks counted from each segment's first key). order: DEVICE output
+ * [tiles * H] (items tile * H + h by list length, longest first; only the first
+ * (number of query tiles) * H entries are written) or NULL. workspace: DEVICE scratch of
  * attn_block_route_varlen_workspace_bytes(nseg, H, total_tokens, d) bytes, 256-byte aligned.
  * total_tokens = 0 is a no-op; more than 983040 tokens return ATTN_ERR_UNSUPPORTED.
  * Returns an attn_status_t.
  */
 int attn_block_route_varlen(const void* q, const void* k, const int32_t* cu_seqlens, int nseg, int H,
                             int total_tokens, int d, float scale, float tau, int sink_tokens, int32_t* kv_idx,
-                            int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* stream);
+                            int32_t* kv_cnt, int32_t* order, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes attn_block_route_varlen needs (0 if the sizes are invalid). */
 size_t attn_block_route_varlen_workspace_bytes(int nseg, int H, int total_tokens, int d);
@@ -270,14 +281,15 @@ size_t attn_block_route_varlen_workspace_bytes(int nseg, int H, int total_tokens
  * Block-skip attention forward of a packed batch over given key-tile lists (layout above):
  * as attn_fwd_varlen, except that each query tile attends to its listed key tiles only. With
  * every tile listed the result equals attn_fwd_varlen bit for bit; a tile with kv_cnt <= 0
- * gets O = 0 and LSE = -inf. workspace: DEVICE scratch of
+ * gets O = 0 and LSE = -inf. order: as attn_block_route_varlen writes it, or NULL (the
+ * varlen schedule's order: longest segments first). workspace: DEVICE scratch of
  * attn_fwd_block_sparse_varlen_workspace_bytes(nseg, H, total_tokens) bytes, 256-byte aligned
  * (the varlen schedule and the tile numbering). Returns an attn_status_t.
  */
 int attn_fwd_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                                  const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
-                                 int nseg, int H, int total_tokens, int d, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 const int32_t* order, int nseg, int H, int total_tokens, int d, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes attn_fwd_block_sparse_varlen needs (0 if the sizes are invalid). */
 size_t attn_fwd_block_sparse_varlen_workspace_bytes(int nseg, int H, int total_tokens);

@@ -44,16 +44,17 @@ def lib():
     lib.attn_block_list_stride.argtypes = [i32]
     lib.attn_block_route_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_block_route_workspace_bytes.restype = sz
-    lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
-    lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+    lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, vp, sz, vp]
+    lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
     lib.attn_block_skip_use_dense.argtypes = [i32, i32, i32, ctypes.c_char_p]
     lib.attn_block_varlen_tiles.argtypes = [i32, i32]
     lib.attn_block_route_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_block_route_varlen_workspace_bytes.restype = sz
-    lib.attn_block_route_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+    lib.attn_block_route_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, vp, sz, vp]
     lib.attn_fwd_block_sparse_varlen_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attn_fwd_block_sparse_varlen_workspace_bytes.restype = sz
-    lib.attn_fwd_block_sparse_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.attn_fwd_block_sparse_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz,
+                                                 vp]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.restype = ctypes.c_char_p
     return lib
@@ -279,18 +280,18 @@ def test_linear_validation(lib, kw, code):
 
 
 # ---------------------------------------------------------------- block-skip attention
-SQ, SK, SV, SO, SL, SI, SC, SW = (0x8000000000 * (i + 1) for i in range(8))
+SQ, SK, SV, SO, SL, SI, SC, SW, SR = (0x8000000000 * (i + 1) for i in range(9))
 
 
-def route(lib, q=SQ, k=SK, B=1, H=2, N=1000, d=128, scale=0.088, tau=0.1, sink=0, idx=SI, cnt=SC, ws=SW,
+def route(lib, q=SQ, k=SK, B=1, H=2, N=1000, d=128, scale=0.088, tau=0.1, sink=0, idx=SI, cnt=SC, order=SR, ws=SW,
           wsb=None):
     if wsb is None:
         wsb = lib.attn_block_route_workspace_bytes(B, H, N, 128)
-    return lib.attn_block_route(q, k, B, H, N, d, scale, tau, sink, idx, cnt, ws, wsb, None)
+    return lib.attn_block_route(q, k, B, H, N, d, scale, tau, sink, idx, cnt, order, ws, wsb, None)
 
 
-def sparse(lib, q=SQ, k=SK, v=SV, o=SO, lse=SL, idx=SI, cnt=SC, B=1, H=2, N=1000, d=128, scale=0.088):
-    return lib.attn_fwd_block_sparse(q, k, v, o, lse, idx, cnt, B, H, N, d, scale, None)
+def sparse(lib, q=SQ, k=SK, v=SV, o=SO, lse=SL, idx=SI, cnt=SC, order=SR, B=1, H=2, N=1000, d=128, scale=0.088):
+    return lib.attn_fwd_block_sparse(q, k, v, o, lse, idx, cnt, order, B, H, N, d, scale, None)
 
 
 def test_block_list_stride_and_route_workspace(lib):
@@ -315,6 +316,7 @@ def test_block_list_stride_and_route_workspace(lib):
     (dict(idx=SQ + 64), INVALID),                                    # list over q
     (dict(cnt=SI + 64), INVALID),                                    # counts inside the lists
     (dict(ws=SC), INVALID),                                          # workspace over the counts
+    (dict(order=SC + 4), INVALID),                                   # order over the counts
 ])
 def test_route_validation(lib, kw, code):
     assert route(lib, **kw) == code
@@ -332,6 +334,7 @@ def test_route_accepts_infinite_tau_on_the_host(lib):
     (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID), (dict(d=64), UNSUPPORTED),
     (dict(scale=math.nan), INVALID), (dict(o=SV + 256), INVALID),   # out over v
     (dict(o=SI), INVALID), (dict(lse=SC), INVALID),                  # outputs over the lists
+    (dict(o=SR), INVALID),                                           # out over the order
 ])
 def test_block_sparse_validation(lib, kw, code):
     assert sparse(lib, **kw) == code
@@ -366,33 +369,34 @@ def test_python_block_skip_guards_without_gpu():
 
 
 # ---------------------------------------------------------------- packed block-skip
-VQ, VK, VV, VO, VL, VI, VC, VW, VCU = (0x10000000000 * (i + 1) for i in range(9))
+VQ, VK, VV, VO, VL, VI, VC, VW, VCU, VR = (0x10000000000 * (i + 1) for i in range(10))
 
 
 def route_v(lib, q=VQ, k=VK, cu=VCU, nseg=3, H=2, T=1000, d=128, scale=0.088, tau=0.01, sink=0, idx=VI, cnt=VC,
-            ws=VW, wsb=None):
+            order=VR, ws=VW, wsb=None):
     if wsb is None:
         wsb = lib.attn_block_route_varlen_workspace_bytes(nseg, H, T, 128)
-    return lib.attn_block_route_varlen(q, k, cu, nseg, H, T, d, scale, tau, sink, idx, cnt, ws, wsb, None)
+    return lib.attn_block_route_varlen(q, k, cu, nseg, H, T, d, scale, tau, sink, idx, cnt, order, ws, wsb, None)
 
 
-def sparse_v(lib, q=VQ, k=VK, v=VV, o=VO, lse=VL, cu=VCU, idx=VI, cnt=VC, nseg=3, H=2, T=1000, d=128, scale=0.088,
-             ws=VW, wsb=None):
+def sparse_v(lib, q=VQ, k=VK, v=VV, o=VO, lse=VL, cu=VCU, idx=VI, cnt=VC, order=VR, nseg=3, H=2, T=1000, d=128,
+             scale=0.088, ws=VW, wsb=None):
     if wsb is None:
         wsb = lib.attn_fwd_block_sparse_varlen_workspace_bytes(nseg, H, T)
-    return lib.attn_fwd_block_sparse_varlen(q, k, v, o, lse, cu, idx, cnt, nseg, H, T, d, scale, ws, wsb, None)
+    return lib.attn_fwd_block_sparse_varlen(q, k, v, o, lse, cu, idx, cnt, order, nseg, H, T, d, scale, ws, wsb, None)
 
 
 def test_varlen_block_sizes(lib):
     assert lib.attn_block_varlen_tiles(3, 38048) == 38048 // 256 + 3
     assert lib.attn_block_varlen_tiles(0, 100) == 0
     a = lambda x: (x + 255) // 256 * 256
-    # tile offsets (two int arrays of nseg + 1), pooled query tiles, pooled key tiles
+    # tile offsets (two int arrays of nseg + 1, then an item count), pooled query tiles,
+    # pooled key tiles
     assert lib.attn_block_route_varlen_workspace_bytes(3, 2, 1000, 128) == \
-        2 * a(4 * 4) + a((1000 // 256 + 3) * 2 * 512) + (1000 // 64 + 3) * 2 * 512
+        2 * a(4 * 4) + 256 + a((1000 // 256 + 3) * 2 * 512) + (1000 // 64 + 3) * 2 * 512
     assert lib.attn_block_route_varlen_workspace_bytes(3, 2, 1000, 64) == 0
     assert lib.attn_fwd_block_sparse_varlen_workspace_bytes(3, 2, 1000) == \
-        lib.attn_fwd_varlen_workspace_bytes(3, 2, 1000) + 2 * a(4 * 4)
+        lib.attn_fwd_varlen_workspace_bytes(3, 2, 1000) + 2 * a(4 * 4) + 256
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -402,6 +406,7 @@ def test_varlen_block_sizes(lib):
     (dict(T=983041), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(wsb=8), WORKSPACE), (dict(ws=VW + 8), WORKSPACE),
     (dict(idx=VQ + 256), INVALID), (dict(ws=VC), INVALID), (dict(cnt=VCU), INVALID),
+    (dict(order=VI + 8), INVALID),
 ])
 def test_route_varlen_validation(lib, kw, code):
     assert route_v(lib, **kw) == code
@@ -409,8 +414,9 @@ def test_route_varlen_validation(lib, kw, code):
 
 
 def test_varlen_empty_batch_is_a_no_op(lib):
-    assert route_v(lib, T=0, q=None, k=None, cu=None, idx=None, cnt=None, ws=None) == OK
-    assert sparse_v(lib, T=0, q=None, k=None, v=None, o=None, cu=None, idx=None, cnt=None, ws=None) == OK
+    assert route_v(lib, T=0, q=None, k=None, cu=None, idx=None, cnt=None, order=None, ws=None) == OK
+    assert sparse_v(lib, T=0, q=None, k=None, v=None, o=None, cu=None, idx=None, cnt=None, order=None,
+                    ws=None) == OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -418,6 +424,7 @@ def test_varlen_empty_batch_is_a_no_op(lib):
     (dict(v=None), INVALID), (dict(cu=None), INVALID), (dict(idx=None), INVALID),
     (dict(ws=None), WORKSPACE), (dict(wsb=64), WORKSPACE),
     (dict(o=VQ), INVALID), (dict(o=VI), INVALID), (dict(lse=VC), INVALID), (dict(ws=VCU), INVALID),
+    (dict(ws=VR), INVALID),
 ])
 def test_block_sparse_varlen_validation(lib, kw, code):
     assert sparse_v(lib, **kw) == code

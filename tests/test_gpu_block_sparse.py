@@ -172,6 +172,45 @@ def test_deterministic(vd):
     assert np.array_equal(bits_of(a), bits_of(b))
 
 
+def check_order(order, cnt, n, max_cnt):
+    """order (host): its first n entries are a permutation of the n items, longest list
+    first. The counting sort bins counts into 4096 bins, one count per bin while
+    max_cnt <= 4095; above that, neighbouring counts may share a bin and keep any order."""
+    o = order[:n]
+    assert np.array_equal(np.sort(o), np.arange(n))
+    c = np.clip(cnt.reshape(-1)[o].astype(np.int64), 0, max_cnt)
+    if max_cnt <= 4095:
+        assert np.all(np.diff(c) <= 0)
+    else:
+        assert np.all(np.diff((max_cnt - c) * 4095 // max_cnt) >= 0)
+
+
+@pytest.mark.parametrize("B,H,N,tau", [
+    (2, 3, 3000, 0.01),
+    (1, 2, 700, math.inf),      # every list full: all counts equal
+    (1, 1, 1, 0.0),             # one item
+])
+def test_dispatch_order(vd, B, H, N, tau):
+    """The longest-first order: a permutation of the items sorted by count; the lists are
+    the same with and without it, and so are the outputs, bit for bit."""
+    q, k, v = random_dense(B, H, N, seed=N + 7 * H)
+    kv_idx, kv_cnt = route(vd, q, k, tau)
+    idx2, cnt2, order = vd.block_route(dev(q), dev(k), tau=tau, scale=SCALE, with_order=True)
+    torch.cuda.synchronize()
+    ntk = -(-N // 64)
+    # lists are written up to their count plus 8 padding entries; compare that part
+    assert np.array_equal(cnt2.cpu().numpy(), kv_cnt.cpu().numpy())
+    assert np.array_equal(lists_to_keep(idx2.cpu().numpy(), cnt2.cpu().numpy(), ntk),
+                          lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ntk))
+    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), kv_cnt.numel(), ntk)
+    a, la = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    b, lb = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True,
+                                     order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(a), bits_of(b))
+    assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy())
+
+
 def test_long_sequence_routes_one_query_tile_per_workgroup(vd):
     """N = 260000: 4063 key tiles, more proxies than four query tiles' worth fit in a
     workgroup's LDS, so the routing takes one query tile per workgroup. Routing against the
@@ -195,17 +234,21 @@ def video_720p():
 
 
 def test_video_720p_routing_and_sampled_rows(vd, video_720p):
-    """The 720p grid (B=1, H=16, N=180320) at the timed setting tau = 0.02: routing against
-    the oracle over every (head, query tile, key tile), attention on 384 seeded rows plus the
-    last 64 rows of head 15."""
+    """The 720p grid (B=1, H=16, N=180320) at the timed setting tau = 0.02, in the timed
+    launch (longest-first order): routing against the oracle over every (head, query tile,
+    key tile), the order against the counts, attention on 384 seeded rows plus the last 64
+    rows of head 15."""
     q, k, v = video_720p
     tau = 0.02
-    kv_idx, kv_cnt = route(vd, q, k, tau)
+    kv_idx, kv_cnt, order = vd.block_route(dev(q), dev(k), tau=tau, scale=SCALE, with_order=True)
+    torch.cuda.synchronize()
     N = q.shape[2]
     ntk = -(-N // 64)
     keep_gpu = lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ntk)
     check_route(keep_gpu, q, k, tau, 0)
-    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), kv_cnt.numel(), ntk)
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True,
+                                        order=order)
     torch.cuda.synchronize()
     rng = np.random.default_rng(720)
     rows = np.unique(np.concatenate([rng.choice(16 * N, 384, replace=False), 15 * N + np.arange(N - 64, N)]))
@@ -298,6 +341,31 @@ def test_varlen_every_tile_listed_equals_varlen_bits(vd):
     assert np.array_equal(lse.cpu().numpy(), lse_ref.cpu().numpy())
 
 
+def test_varlen_dispatch_order(vd):
+    """Packed order: its first (query tiles x H) entries are a permutation of the items sorted
+    by count; the outputs with and without it are equal bit for bit."""
+    lens, H = (300, 1, 0, 520, 64, 1100), 3
+    q, k, v, cu = random_varlen(lens, H, seed=91)
+    cu_d, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, 0.01)
+    idx2, cnt2, order = vd.block_route_varlen(dev(q), dev(k), cu_d, tau=0.01, scale=SCALE, with_order=True)
+    torch.cuda.synchronize()
+    n = sum(-(-n_ // 256) for n_ in lens) * H
+    # the first n rows are written, each up to its count plus 8 padding entries
+    assert np.array_equal(cnt2.cpu().numpy().reshape(-1)[:n], kv_cnt.cpu().numpy().reshape(-1)[:n])
+    for a_, b_ in zip(varlen_keeps(vd, idx2.cpu().numpy(), cnt2.cpu().numpy(), cu, H),
+                      varlen_keeps(vd, kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), cu, H)):
+        assert (a_ is None and b_ is None) or np.array_equal(a_, b_)
+    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), n, -(-int(cu[-1]) // 64))
+    a, la = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), cu_d, kv_idx, kv_cnt, scale=SCALE,
+                                            return_lse=True)
+    b, lb = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), cu_d, kv_idx, kv_cnt, scale=SCALE,
+                                            return_lse=True, order=order)
+    c, lc = vd.block_skip_attention_varlen(dev(q), dev(k), dev(v), cu_d, tau=0.01, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(a), bits_of(b)) and np.array_equal(bits_of(a), bits_of(c))
+    assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy()) and np.array_equal(la.cpu().numpy(), lc.cpu().numpy())
+
+
 def test_varlen_hook_with_caller_lists(vd):
     """Caller lists: each tile keeps its segment's last key tile and tile 0; one tile keeps
     nothing (O = 0, LSE = -inf)."""
@@ -334,16 +402,21 @@ def test_varlen_hook_with_caller_lists(vd):
 
 
 def test_packed_varlen_workload_sampled(vd):
-    """The packed workload (segments 30000 / 6000 / 2048, H = 24) at tau = 0.02: routing of
-    every tile against the oracle, attention on 384 seeded rows plus the last 16 rows."""
+    """The packed workload (segments 30000 / 6000 / 2048, H = 24) at tau = 0.02, in the timed
+    launch (longest-first order): routing of every tile against the oracle, attention on 384
+    seeded rows plus the last 16 rows."""
     w = WORKLOADS["packed_varlen"]
     q, k, v, cu = make_varlen(w)
     T, H = q.shape[0], q.shape[1]
-    cu_d, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, 0.02)
+    cu_d = dev_i32(cu)
+    kv_idx, kv_cnt, order = vd.block_route_varlen(dev(q), dev(k), cu_d, tau=0.02, scale=SCALE, with_order=True)
+    torch.cuda.synchronize()
     keeps = varlen_keeps(vd, kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), cu, H)
     check_route_varlen(keeps, q, k, cu, 0.02, 0)
+    n = sum(-(-int(n_) // 256) for n_ in np.diff(cu)) * H
+    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), n, -(-T // 64))
     out, lse = vd.attn_fwd_block_sparse_varlen(dev(q), dev(k), dev(v), cu_d, kv_idx, kv_cnt, scale=SCALE,
-                                               return_lse=True)
+                                               return_lse=True, order=order)
     torch.cuda.synchronize()
     rng = np.random.default_rng(38)
     rows = np.unique(np.concatenate([rng.choice(H * T, 384, replace=False), (H - 1) * T + np.arange(T - 16, T)]))

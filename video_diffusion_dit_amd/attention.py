@@ -84,19 +84,20 @@ def load_library() -> ctypes.CDLL:
         lib.attn_block_list_stride.restype = i32
         lib.attn_block_route_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.attn_block_route_workspace_bytes.restype = sz
-        lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+        lib.attn_block_route.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, vp, sz, vp]
         lib.attn_block_route.restype = i32
-        lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         lib.attn_fwd_block_sparse.restype = i32
         lib.attn_block_varlen_tiles.argtypes = [i32, i32]
         lib.attn_block_varlen_tiles.restype = i32
         lib.attn_block_route_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.attn_block_route_varlen_workspace_bytes.restype = sz
-        lib.attn_block_route_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, sz, vp]
+        lib.attn_block_route_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, f32, i32, vp, vp, vp, vp, sz, vp]
         lib.attn_block_route_varlen.restype = i32
         lib.attn_fwd_block_sparse_varlen_workspace_bytes.argtypes = [i32, i32, i32]
         lib.attn_fwd_block_sparse_varlen_workspace_bytes.restype = sz
-        lib.attn_fwd_block_sparse_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+        lib.attn_fwd_block_sparse_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz,
+                                                     vp]
         lib.attn_fwd_block_sparse_varlen.restype = i32
         lib.attn_block_skip_use_dense.argtypes = [i32, i32, i32, ctypes.c_char_p]
         lib.attn_block_skip_use_dense.restype = i32
@@ -378,11 +379,13 @@ def _list_shapes(B: int, H: int, N: int):
 
 
 def block_route(q: torch.Tensor, k: torch.Tensor, *, tau: float, sink_tokens: int = 0,
-                scale: float | None = None):
+                scale: float | None = None, with_order: bool = False):
     """Key-tile lists of block-skip attention for dense BF16 [B, H, N, 128] q and k.
 
     Returns (kv_idx int32 [B, H, ntq, stride], kv_cnt int32 [B, H, ntq]) on q's device,
-    written on the current stream (see attn_block_route for the rule)."""
+    written on the current stream (see attn_block_route for the rule); with with_order, also
+    order int32 [B*H*ntq], the items by list length, longest first (the dispatch order for
+    attn_fwd_block_sparse)."""
     _check_tensors(q, k, k, 4)
     B, H, N, d = q.shape
     if d != 128:
@@ -391,22 +394,33 @@ def block_route(q: torch.Tensor, k: torch.Tensor, *, tau: float, sink_tokens: in
     idx_shape, cnt_shape = _list_shapes(B, H, N)
     kv_idx = torch.empty(idx_shape, dtype=torch.int32, device=q.device)
     kv_cnt = torch.empty(cnt_shape, dtype=torch.int32, device=q.device)
+    order = torch.empty(kv_cnt.numel(), dtype=torch.int32, device=q.device) if with_order else None
     with torch.cuda.device(q.device):
         nbytes = int(lib.attn_block_route_workspace_bytes(B, H, N, d))
         ws = _workspace(q.device, nbytes)
         st = lib.attn_block_route(_ptr(q), _ptr(k), B, H, N, d, _default_scale(d, scale), float(tau),
-                                  int(sink_tokens), _ptr(kv_idx), _ptr(kv_cnt), _ptr(ws), ws.numel(),
+                                  int(sink_tokens), _ptr(kv_idx), _ptr(kv_cnt), _ptr(order), _ptr(ws), ws.numel(),
                                   _stream_handle(q.device))
     _raise_for(lib, st)
-    return kv_idx, kv_cnt
+    return (kv_idx, kv_cnt, order) if with_order else (kv_idx, kv_cnt)
+
+
+def _check_order(order, n: int, device):
+    if order is None:
+        return
+    if not isinstance(order, torch.Tensor) or order.dtype != torch.int32 or order.numel() != n:
+        raise ValueError(f"order must be an int32 tensor of {n} entries")
+    if order.device != device or not order.is_contiguous():
+        raise ValueError("order must be contiguous on q's device")
 
 
 def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_idx: torch.Tensor,
                           kv_cnt: torch.Tensor, scale: float | None = None, return_lse: bool = False,
-                          out: torch.Tensor | None = None):
+                          out: torch.Tensor | None = None, order: torch.Tensor | None = None):
     """Attention of dense BF16 [B, H, N, 128] q, k, v where query tile I of (b, h) sees only
     the key tiles kv_idx[b, h, I, :kv_cnt[b, h, I]] (int32 device tensors shaped as
-    block_route returns them; the caller's own lists are accepted: this is the hook)."""
+    block_route returns them; the caller's own lists are accepted: this is the hook). order:
+    the dispatch order block_route(with_order=True) returns, or None (item order)."""
     _check_tensors(q, k, v, 4)
     B, H, N, d = q.shape
     if d != 128:
@@ -417,6 +431,7 @@ def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
             raise ValueError(f"{name} must be an int32 tensor of shape {shape}")
         if t.device != q.device or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on q's device")
+    _check_order(order, kv_cnt.numel(), q.device)
     lib = load_library()
     if out is None:
         out = torch.empty_like(q)
@@ -425,7 +440,7 @@ def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
         st = lib.attn_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(kv_idx),
-                                       _ptr(kv_cnt), B, H, N, d, _default_scale(d, scale),
+                                       _ptr(kv_cnt), _ptr(order), B, H, N, d, _default_scale(d, scale),
                                        _stream_handle(q.device))
     _raise_for(lib, st)
     return (out, lse) if return_lse else out
@@ -433,7 +448,9 @@ def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
 
 def block_skip_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tau: float,
                          sink_tokens: int = 0, scale: float | None = None, return_lse: bool = False):
-    """block_route, then attn_fwd_block_sparse over its lists."""
+    """block_route, then attn_fwd_block_sparse over its lists in item order, which keeps the
+    workgroups in flight within one or two heads (the longest-first order measured slower on
+    the 720p grid)."""
     kv_idx, kv_cnt = block_route(q, k, tau=tau, sink_tokens=sink_tokens, scale=scale)
     return attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=scale, return_lse=return_lse)
 
@@ -477,10 +494,12 @@ def varlen_tile_offsets(cu_host) -> list:
 
 
 def block_route_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, *, tau: float,
-                       sink_tokens: int = 0, scale: float | None = None, cu_seqlens_host=None):
+                       sink_tokens: int = 0, scale: float | None = None, cu_seqlens_host=None,
+                       with_order: bool = False):
     """Key-tile lists of block-skip attention for a packed batch (THD BF16 [T, H, 128] q, k):
     (kv_idx int32 [tiles, H, stride], kv_cnt int32 [tiles, H]); row g of the lists is query
-    tile g of the numbering segment by segment (see varlen_tile_offsets)."""
+    tile g of the numbering segment by segment (see varlen_tile_offsets). with_order adds the
+    dispatch order (items g * H + h by list length, longest first)."""
     _check_tensors(q, k, k, 3)
     T, H, d = q.shape
     if d != 128:
@@ -491,19 +510,21 @@ def block_route_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tenso
     idx_shape, cnt_shape = varlen_list_shapes(nseg, T, H)
     kv_idx = torch.empty(idx_shape, dtype=torch.int32, device=q.device)
     kv_cnt = torch.empty(cnt_shape, dtype=torch.int32, device=q.device)
+    order = torch.empty(kv_cnt.numel(), dtype=torch.int32, device=q.device) if with_order else None
     with torch.cuda.device(q.device):
         nbytes = int(lib.attn_block_route_varlen_workspace_bytes(nseg, H, T, d))
         ws = _workspace(q.device, nbytes)
         st = lib.attn_block_route_varlen(_ptr(q), _ptr(k), _ptr(cu_seqlens), nseg, H, T, d, _default_scale(d, scale),
-                                         float(tau), int(sink_tokens), _ptr(kv_idx), _ptr(kv_cnt), _ptr(ws),
-                                         ws.numel(), _stream_handle(q.device))
+                                         float(tau), int(sink_tokens), _ptr(kv_idx), _ptr(kv_cnt), _ptr(order),
+                                         _ptr(ws), ws.numel(), _stream_handle(q.device))
     _raise_for(lib, st)
-    return kv_idx, kv_cnt
+    return (kv_idx, kv_cnt, order) if with_order else (kv_idx, kv_cnt)
 
 
 def attn_fwd_block_sparse_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                                  kv_idx: torch.Tensor, kv_cnt: torch.Tensor, scale: float | None = None,
-                                 return_lse: bool = False, out: torch.Tensor | None = None, cu_seqlens_host=None):
+                                 return_lse: bool = False, out: torch.Tensor | None = None, cu_seqlens_host=None,
+                                 order: torch.Tensor | None = None):
     """Packed-batch attention where query tile g (numbered segment by segment) of head h sees
     only the key tiles kv_idx[g, h, :kv_cnt[g, h]] of its segment (the caller's own lists are
     accepted: this is the hook). Returns out (BF16 [T, H, 128]) or (out, lse FP32 [H, T])."""
@@ -519,6 +540,7 @@ def attn_fwd_block_sparse_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tens
             raise ValueError(f"{name} must be an int32 tensor of shape {shape}")
         if t.device != q.device or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on q's device")
+    _check_order(order, kv_cnt.numel(), q.device)
     lib = load_library()
     if out is None:
         out = torch.empty_like(q)
@@ -529,7 +551,18 @@ def attn_fwd_block_sparse_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tens
         nbytes = int(lib.attn_fwd_block_sparse_varlen_workspace_bytes(nseg, H, T))
         ws = _workspace(q.device, nbytes)
         st = lib.attn_fwd_block_sparse_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
-                                              _ptr(kv_idx), _ptr(kv_cnt), nseg, H, T, d, _default_scale(d, scale),
-                                              _ptr(ws), ws.numel(), _stream_handle(q.device))
+                                              _ptr(kv_idx), _ptr(kv_cnt), _ptr(order), nseg, H, T, d,
+                                              _default_scale(d, scale), _ptr(ws), ws.numel(), _stream_handle(q.device))
     _raise_for(lib, st)
     return (out, lse) if return_lse else out
+
+
+def block_skip_attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                                tau: float, sink_tokens: int = 0, scale: float | None = None,
+                                cu_seqlens_host=None, return_lse: bool = False):
+    """block_route_varlen, then attn_fwd_block_sparse_varlen with the longest lists started
+    first: a packed batch mixes segment lengths, so its list lengths spread widely."""
+    kv_idx, kv_cnt, order = block_route_varlen(q, k, cu_seqlens, tau=tau, sink_tokens=sink_tokens, scale=scale,
+                                               cu_seqlens_host=cu_seqlens_host, with_order=True)
+    return attn_fwd_block_sparse_varlen(q, k, v, cu_seqlens, kv_idx, kv_cnt, scale=scale,
+                                        cu_seqlens_host=cu_seqlens_host, return_lse=return_lse, order=order)

@@ -212,7 +212,7 @@ size_t attn_block_route_workspace_bytes(int B, int H, int N, int d) {
 }
 
 int attn_block_route(const void* q, const void* k, int B, int H, int N, int d, float scale, float tau,
-                     int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                     int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, int32_t* order, void* workspace,
                      size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     if (q == nullptr || k == nullptr || kv_idx == nullptr || kv_cnt == nullptr)
@@ -237,22 +237,22 @@ int attn_block_route(const void* q, const void* k, int B, int H, int N, int d, f
         return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     const size_t tb = (size_t)elems * 2;
     const size_t idx_bytes = (size_t)items * attn_impl::block_list_stride(N) * 4, cnt_bytes = (size_t)items * 4;
-    const void* outs[3] = {kv_idx, kv_cnt, workspace};
-    const size_t outb[3] = {idx_bytes, cnt_bytes, need};
-    for (int i = 0; i < 3; ++i) {
+    const void* outs[4] = {kv_idx, kv_cnt, workspace, order};
+    const size_t outb[4] = {idx_bytes, cnt_bytes, need, cnt_bytes};
+    for (int i = 0; i < 4; ++i) {
         if (overlaps(outs[i], outb[i], q, tb) || overlaps(outs[i], outb[i], k, tb))
-            return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt or workspace overlaps q or k");
+            return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt, order or workspace overlaps q or k");
         for (int j = 0; j < i; ++j)
             if (overlaps(outs[i], outb[i], outs[j], outb[j]))
-                return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt and workspace must not overlap");
+                return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt, order and workspace must not overlap");
     }
-    return hip_status(attn_impl::launch_block_route(q, k, B, H, N, scale, tau, sink_tokens, kv_idx, kv_cnt,
+    return hip_status(attn_impl::launch_block_route(q, k, B, H, N, scale, tau, sink_tokens, kv_idx, kv_cnt, order,
                                                     workspace, static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
-                          const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N, int d,
-                          float scale, void* stream) {
+                          const int32_t* kv_idx, const int32_t* kv_cnt, const int32_t* order, int B, int H,
+                          int N, int d, float scale, void* stream) {
     g_last_error[0] = '\0';
     int st = check_common(q, k, v, out, H, d, scale);
     if (st != ATTN_OK) return st;
@@ -268,9 +268,10 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out
     if (st != ATTN_OK) return st;
     const size_t idx_bytes = (size_t)items * attn_impl::block_list_stride(N) * 4, cnt_bytes = (size_t)items * 4;
     if (overlaps(out, tb, kv_idx, idx_bytes) || overlaps(out, tb, kv_cnt, cnt_bytes) ||
-        overlaps(lse, lb, kv_idx, idx_bytes) || overlaps(lse, lb, kv_cnt, cnt_bytes))
-        return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx or kv_cnt");
-    return hip_status(attn_impl::launch_block_sparse(q, k, v, out, lse, kv_idx, kv_cnt, B, H, N, scale,
+        overlaps(lse, lb, kv_idx, idx_bytes) || overlaps(lse, lb, kv_cnt, cnt_bytes) ||
+        overlaps(out, tb, order, cnt_bytes) || overlaps(lse, lb, order, cnt_bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx, kv_cnt or order");
+    return hip_status(attn_impl::launch_block_sparse(q, k, v, out, lse, kv_idx, kv_cnt, order, B, H, N, scale,
                                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -287,7 +288,7 @@ size_t attn_block_route_varlen_workspace_bytes(int nseg, int H, int total_tokens
 
 int attn_block_route_varlen(const void* q, const void* k, const int32_t* cu_seqlens, int nseg, int H,
                             int total_tokens, int d, float scale, float tau, int sink_tokens, int32_t* kv_idx,
-                            int32_t* kv_cnt, void* workspace, size_t workspace_bytes, void* stream) {
+                            int32_t* kv_cnt, int32_t* order, void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
     if (nseg <= 0) return fail(ATTN_ERR_INVALID_ARG, "nseg must be >= 1");
@@ -312,18 +313,18 @@ int attn_block_route_varlen(const void* q, const void* k, const int32_t* cu_seql
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
         return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     const size_t tb = (size_t)elems * 2;
-    const void* outs[3] = {kv_idx, kv_cnt, workspace};
-    const size_t outb[3] = {idx_bytes, cnt_bytes, need};
-    for (int i = 0; i < 3; ++i) {
+    const void* outs[4] = {kv_idx, kv_cnt, workspace, order};
+    const size_t outb[4] = {idx_bytes, cnt_bytes, need, cnt_bytes};
+    for (int i = 0; i < 4; ++i) {
         if (overlaps(outs[i], outb[i], q, tb) || overlaps(outs[i], outb[i], k, tb) ||
             overlaps(outs[i], outb[i], cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)))
-            return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt or workspace overlaps q, k or cu_seqlens");
+            return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt, order or workspace overlaps q, k or cu_seqlens");
         for (int j = 0; j < i; ++j)
             if (overlaps(outs[i], outb[i], outs[j], outb[j]))
-                return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt and workspace must not overlap");
+                return fail(ATTN_ERR_INVALID_ARG, "kv_idx, kv_cnt, order and workspace must not overlap");
     }
     return hip_status(attn_impl::launch_block_route_varlen(q, k, cu_seqlens, nseg, H, total_tokens, scale, tau,
-                                                           sink_tokens, kv_idx, kv_cnt, workspace,
+                                                           sink_tokens, kv_idx, kv_cnt, order, workspace,
                                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -334,8 +335,8 @@ size_t attn_fwd_block_sparse_varlen_workspace_bytes(int nseg, int H, int total_t
 
 int attn_fwd_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                                  const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
-                                 int nseg, int H, int total_tokens, int d, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 const int32_t* order, int nseg, int H, int total_tokens, int d, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
     if (nseg <= 0) return fail(ATTN_ERR_INVALID_ARG, "nseg must be >= 1");
@@ -362,17 +363,18 @@ int attn_fwd_block_sparse_varlen(const void* q, const void* k, const void* v, vo
     st = check_aliasing(q, k, v, out, lse, tb, lb);
     if (st != ATTN_OK) return st;
     if (overlaps(out, tb, kv_idx, idx_bytes) || overlaps(out, tb, kv_cnt, cnt_bytes) ||
-        overlaps(lse, lb, kv_idx, idx_bytes) || overlaps(lse, lb, kv_cnt, cnt_bytes))
-        return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx or kv_cnt");
-    const void* ins[7] = {q, k, v, out, lse, kv_idx, kv_cnt};
-    const size_t inb[7] = {tb, tb, tb, tb, lb, idx_bytes, cnt_bytes};
-    for (int i = 0; i < 7; ++i)
+        overlaps(lse, lb, kv_idx, idx_bytes) || overlaps(lse, lb, kv_cnt, cnt_bytes) ||
+        overlaps(out, tb, order, cnt_bytes) || overlaps(lse, lb, order, cnt_bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "out or lse overlaps kv_idx, kv_cnt or order");
+    const void* ins[8] = {q, k, v, out, lse, kv_idx, kv_cnt, order};
+    const size_t inb[8] = {tb, tb, tb, tb, lb, idx_bytes, cnt_bytes, cnt_bytes};
+    for (int i = 0; i < 8; ++i)
         if (overlaps(workspace, need, ins[i], inb[i]))
             return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor argument");
     if (overlaps(workspace, need, cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)))
         return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps cu_seqlens");
-    return hip_status(attn_impl::launch_block_sparse_varlen(q, k, v, out, lse, cu_seqlens, kv_idx, kv_cnt, nseg,
-                                                            H, total_tokens, scale, workspace,
+    return hip_status(attn_impl::launch_block_sparse_varlen(q, k, v, out, lse, cu_seqlens, kv_idx, kv_cnt, order,
+                                                            nseg, H, total_tokens, scale, workspace,
                                                             static_cast<hipStream_t>(stream)));
 }
 

@@ -236,9 +236,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_dense_kernel(DenseArgs a) {
                      D, a.N, qt * BM, a.c, 0, (a.N + BN - 1) / BN, nullptr);
 }
 
-// Block-skip attention over caller-given key-tile lists: workgroup = (b*H + h) * ntq + query
-// tile, its kv_cnt entry gives how many tiles of its kv_idx row (stride entries) it attends
-// to. A tile with no keys gets O = 0 and LSE = -inf (softmax over an empty set).
+// Block-skip attention over caller-given key-tile lists: item = (b*H + h) * ntq + query tile,
+// its kv_cnt entry gives how many tiles of its kv_idx row (stride entries) it attends to.
+// Workgroup x takes item order[x] (clamped to a valid item), or item x without an order. A
+// tile with no keys gets O = 0 and LSE = -inf (softmax over an empty set).
 struct SparseArgs {
     const bf16* q;
     const bf16* k;
@@ -247,12 +248,13 @@ struct SparseArgs {
     float* lse;
     const int32_t* kidx;
     const int32_t* kcnt;
+    const int32_t* order;
     int N, ntq, ntk, stride;
     float c;
 };
 
 __global__ __launch_bounds__(NT, 1) void attn_fwd_block_sparse_kernel(SparseArgs a) {
-    const int item = blockIdx.x;
+    const int item = a.order != nullptr ? min(max(a.order[blockIdx.x], 0), (int)gridDim.x - 1) : (int)blockIdx.x;
     const int bh = item / a.ntq, qt = item - bh * a.ntq;
     const long base = (long)bh * a.N * D;
     const int cnt = min(a.kcnt[item], a.ntk);
@@ -457,14 +459,39 @@ struct SparseVarlenArgs {
     const int* off_q;
     const int32_t* kidx;
     const int32_t* kcnt;
+    const int32_t* order; // item order (item = tile * H + h), or null: the schedule's order
     int nseg, H, T, stride;
     float c;
 };
 
+// segment holding query tile g of the numbering segment by segment (off ascending, off[0] = 0)
+__device__ __forceinline__ int tile_segment_of(const int* off, int nseg, int g) {
+    int lo = 0, hi = nseg;   // off[lo] <= g < off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= g) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
 __global__ __launch_bounds__(NT, 1) void attn_fwd_block_sparse_varlen_kernel(SparseVarlenArgs a) {
-    const int e = blockIdx.x / a.H, h = blockIdx.x - e * a.H;
-    if (e >= *reinterpret_cast<const int*>(a.ws)) return;
-    const int2 t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
+    int2 t;   // (segment, query tile)
+    int h;
+    if (a.order != nullptr) {
+        const int items = a.off_q[a.nseg] * a.H;
+        if ((int)blockIdx.x >= items) return;
+        const int it = min(max(a.order[blockIdx.x], 0), items - 1);
+        const int g = it / a.H;
+        h = it - g * a.H;
+        t.x = tile_segment_of(a.off_q, a.nseg, g);
+        t.y = g - a.off_q[t.x];
+    } else {
+        const int e = blockIdx.x / a.H;
+        h = blockIdx.x - e * a.H;
+        if (e >= *reinterpret_cast<const int*>(a.ws)) return;
+        t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
+    }
     const int start = min(max(a.cu[t.x], 0), a.T);
     const int n = seg_len(a.cu, t.x, a.T);
     if (t.y * BM >= n) return;
@@ -579,8 +606,8 @@ hipError_t launch_dense_split(const void* q, const void* k, const void* v, void*
 int block_list_stride(int N) { return (N + BN - 1) / BN + 8; }
 
 hipError_t launch_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
-                               const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N,
-                               float scale, hipStream_t stream) {
+                               const int32_t* kv_idx, const int32_t* kv_cnt, const int32_t* order, int B, int H,
+                               int N, float scale, hipStream_t stream) {
     SparseArgs a;
     a.q = static_cast<const bf16*>(q);
     a.k = static_cast<const bf16*>(k);
@@ -589,6 +616,7 @@ hipError_t launch_block_sparse(const void* q, const void* k, const void* v, void
     a.lse = lse;
     a.kidx = kv_idx;
     a.kcnt = kv_cnt;
+    a.order = order;
     a.N = N;
     a.ntq = (N + BM - 1) / BM;
     a.ntk = (N + BN - 1) / BN;
@@ -609,8 +637,8 @@ size_t block_sparse_varlen_workspace_bytes(int nseg, int total_tokens) {
 
 hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                                       const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
-                                      int nseg, int H, int total_tokens, float scale, void* workspace,
-                                      hipStream_t stream) {
+                                      const int32_t* order, int nseg, int H, int total_tokens, float scale,
+                                      void* workspace, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
     hipLaunchKernelGGL(build_varlen_schedule, dim3(1), dim3(1024), 0, stream, cu_seqlens, nseg, total_tokens, ws);
     hipError_t e = hipGetLastError();
@@ -629,6 +657,7 @@ hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* 
     a.off_q = reinterpret_cast<const int*>(offs);
     a.kidx = kv_idx;
     a.kcnt = kv_cnt;
+    a.order = order;
     a.nseg = nseg;
     a.H = H;
     a.T = total_tokens;

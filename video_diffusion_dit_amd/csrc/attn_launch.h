@@ -35,15 +35,16 @@ hipError_t launch_dense_split(const void* q, const void* k, const void* v, void*
 // kv_cnt [B*H*ntq]; item (b*H + h)*ntq + query tile.
 int block_list_stride(int N);
 hipError_t launch_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
-                               const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N,
-                               float scale, hipStream_t stream);
+                               const int32_t* kv_idx, const int32_t* kv_cnt, const int32_t* order, int B, int H,
+                               int N, float scale, hipStream_t stream);
 // Routing of block-skip attention into those lists (block_route_gfx950.hip); workspace holds
 // the pooled query and key tiles (route_workspace_bytes, 256-byte aligned); at most
 // route_max_tiles() key tiles per sequence.
 size_t route_workspace_bytes(int B, int H, int N);
 int route_max_tiles();
+// order (may be null): the items sorted by list length, longest first.
 hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N, float scale, float tau,
-                              int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                              int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, int32_t* order, void* workspace,
                               hipStream_t stream);
 
 // Packed (varlen) block-skip: query tiles (256 rows) and key tiles (64 keys) counted per
@@ -56,12 +57,12 @@ hipError_t launch_tile_offsets(const int32_t* cu, int nseg, int T, void* dst, hi
 size_t route_varlen_workspace_bytes(int nseg, int H, int T);
 hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t* cu, int nseg, int H, int T,
                                      float scale, float tau, int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt,
-                                     void* workspace, hipStream_t stream);
+                                     int32_t* order, void* workspace, hipStream_t stream);
 size_t block_sparse_varlen_workspace_bytes(int nseg, int total_tokens);
 hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                                       const int32_t* cu_seqlens, const int32_t* kv_idx, const int32_t* kv_cnt,
-                                      int nseg, int H, int total_tokens, float scale, void* workspace,
-                                      hipStream_t stream);
+                                      const int32_t* order, int nseg, int H, int total_tokens, float scale,
+                                      void* workspace, hipStream_t stream);
 
 // Workspace layout of the varlen schedule (bytes).
 size_t varlen_workspace_bytes(int nseg, int total_tokens);

@@ -322,9 +322,69 @@ __global__ __launch_bounds__(256) void route_varlen_kernel(RouteVarlenArgs a) {
     if (tid == 0) a.kcnt[item] = total;
 }
 
+// count * H into dst (one thread): the number of (query tile, head) items of a packed batch
+__global__ void scale_count_kernel(const int* __restrict__ count, int H, int* __restrict__ dst) {
+    *dst = *count * H;
+}
+
+// ---------------------------------------------------------------- dispatch order
+// Items sorted by their list length, longest first (a bucket sort in one workgroup), so that
+// the block-sparse kernel starts the long items first and the last round is made of short
+// ones. Within a bucket the order depends on the timing of LDS atomics; the attention
+// results do not depend on the order at all.
+constexpr int ORDER_BINS = 4096;
+
+__global__ __launch_bounds__(1024) void lpt_order_kernel(const int32_t* __restrict__ kcnt, int items,
+                                                         const int* __restrict__ items_dev, int max_cnt,
+                                                         int32_t* __restrict__ order) {
+    __shared__ int hist[ORDER_BINS];
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    const int n = items_dev != nullptr ? min(*items_dev, items) : items;
+    const int mc = max(max_cnt, 1);
+    auto bin = [&](int c) {   // descending: the longest lists in bin 0
+        c = min(max(c, 0), mc);
+        return (int)((long)(mc - c) * (ORDER_BINS - 1) / mc);
+    };
+    for (int b = tid; b < ORDER_BINS; b += 1024) hist[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) atomicAdd(&hist[bin(kcnt[i])], 1);
+    __syncthreads();
+    constexpr int PER = ORDER_BINS / 1024;
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) local += hist[tid * PER + j];
+    part[tid] = local;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < 1024; ++i) {
+            const int v = part[i];
+            part[i] = acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    int acc = part[tid];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int v = hist[tid * PER + j];
+        hist[tid * PER + j] = acc;
+        acc += v;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) order[atomicAdd(&hist[bin(kcnt[i])], 1)] = i;
+}
+
 }  // namespace
 
 namespace attn_impl {
+
+hipError_t launch_lpt_order(const int32_t* kv_cnt, int items, const int* items_dev, int max_cnt, int32_t* order,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(1024), 0, stream, kv_cnt, items, items_dev, max_cnt, order);
+    return hipGetLastError();
+}
 
 size_t route_workspace_bytes(int B, int H, int N) {
     const size_t bh = (size_t)B * H;
@@ -340,7 +400,8 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t varlen_tiles_q(int nseg, int T) { return (size_t)T / BMQ + (size_t)nseg; }
 static size_t varlen_tiles_k(int nseg, int T) { return (size_t)T / BNK + (size_t)nseg; }
 
-size_t tile_offsets_bytes(int nseg) { return 2 * align256(sizeof(int) * ((size_t)nseg + 1)); }
+// [off_q: nseg + 1][off_k: nseg + 1][item count of the order], each 256-byte aligned
+size_t tile_offsets_bytes(int nseg) { return 2 * align256(sizeof(int) * ((size_t)nseg + 1)) + 256; }
 
 hipError_t launch_tile_offsets(const int32_t* cu, int nseg, int T, void* dst, hipStream_t stream) {
     int* off_q = static_cast<int*>(dst);
@@ -356,7 +417,7 @@ size_t route_varlen_workspace_bytes(int nseg, int H, int T) {
 
 hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t* cu, int nseg, int H, int T,
                                      float scale, float tau, int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt,
-                                     void* workspace, hipStream_t stream) {
+                                     int32_t* order, void* workspace, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
     hipError_t e = launch_tile_offsets(cu, nseg, T, ws, stream);
     if (e != hipSuccess) return e;
@@ -388,11 +449,19 @@ hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t
     a.tau = tau;
     const size_t lds = (size_t)((T + BNK - 1) / BNK) * sizeof(float);
     hipLaunchKernelGGL(route_varlen_kernel, dim3((unsigned)(tq * H)), dim3(256), lds, stream, a);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess || order == nullptr) return e;
+    // items = (number of query tiles) * H, known on the device only: written into the slot
+    // after the offsets, read by the sort
+    int* items_dev = reinterpret_cast<int*>(ws + 2 * align256(sizeof(int) * ((size_t)nseg + 1)));
+    hipLaunchKernelGGL(scale_count_kernel, dim3(1), dim3(1), 0, stream, off_q + nseg, H, items_dev);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_lpt_order(kv_cnt, (int)(tq * H), items_dev, (T + BNK - 1) / BNK, order, stream);
 }
 
 hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N, float scale, float tau,
-                              int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                              int sink_tokens, int32_t* kv_idx, int32_t* kv_cnt, int32_t* order, void* workspace,
                               hipStream_t stream) {
     const long bh = (long)B * H;
     const int ntq = (N + BMQ - 1) / BMQ, ntk = (N + BNK - 1) / BNK;
@@ -426,7 +495,9 @@ hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N,
         const size_t lds = (size_t)ntk * sizeof(float);
         hipLaunchKernelGGL(route_kernel<1>, dim3((unsigned)(bh * ntq)), dim3(256), lds, stream, a);
     }
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess || order == nullptr) return e;
+    return launch_lpt_order(kv_cnt, (int)(bh * ntq), nullptr, ntk, order, stream);
 }
 
 }  // namespace attn_impl
