@@ -54,7 +54,9 @@ typedef enum {
  *   out     : BF16 [B, H, N, d], contiguous; every element is written. Must not overlap
  *             q, k, v or lse.
  *   lse     : FP32 [B, H, N] log-sum-exp of the scaled logits (natural log), or NULL.
- *   B, H, N : batch, heads, tokens; each >= 1.
+ *   B, H, N : batch, heads, tokens; each >= 1. N * d * 2 must not exceed 2^31 - 1
+ *             (N <= 8388607 at d = 128: the kernels address one sequence's K/V rows with
+ *             32-bit byte offsets); larger N returns ATTN_ERR_UNSUPPORTED.
  *   d       : head dimension; only 128 is supported (else ATTN_ERR_UNSUPPORTED).
  *   scale   : multiplier of q.k (finite; 1/sqrt(d) is the usual value).
  *   stream  : hipStream_t to launch on.
@@ -104,7 +106,9 @@ size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int slots);
  *                 callers validate them (the Python binding does, on a host copy).
  *   nseg        : number of segments, >= 1.
  *   H, d        : heads (>= 1) and head dim (only 128).
- *   total_tokens: T >= 0; T = 0 is a no-op that returns ATTN_OK.
+ *   total_tokens: T >= 0; T = 0 is a no-op that returns ATTN_OK. T * H * d * 2 must not
+ *                 exceed 2^31 - 1 (a segment's K/V rows, H * d * 2 bytes apart, are addressed
+ *                 with 32-bit byte offsets); larger batches return ATTN_ERR_UNSUPPORTED.
  *   workspace   : DEVICE scratch of at least attn_fwd_varlen_workspace_bytes(nseg, H, T)
  *                 bytes, 256-byte aligned; holds the tile schedule (longest segment first).
  *                 Its contents need no initialisation; it must not be shared by calls that

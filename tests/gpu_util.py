@@ -30,3 +30,11 @@ def check(o_gpu, o_ref, lse_gpu=None, lse_ref=None, label=""):
           f"lse_max_abs={m.get('lse_max_abs', float('nan')):.3e} n={m['n_elems']}", flush=True)
     assert m["ok"], (label, m)
     return m
+
+
+def device_normal_bf16(shape, seed: int) -> torch.Tensor:
+    """Seeded N(0, 1) values rounded to BF16, generated on cuda:0 for inputs too large to build
+    on the host. Tests copy back the rows the oracle needs, so both sides read the same bits."""
+    g = torch.Generator(device="cuda:0").manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda:0", dtype=torch.float32)
+    return x.to(torch.bfloat16)

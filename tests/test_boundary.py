@@ -95,6 +95,7 @@ def dense(lib, q=Q, k=K, v=V, o=O, lse=None, B=1, H=2, N=256, d=128, scale=0.088
     (dict(o=Q), INVALID), (dict(o=K + 64), INVALID),                         # out aliases q / k
     (dict(lse=O + 1024), INVALID),                                           # lse inside out
     (dict(B=1 << 20, H=1 << 20, N=1 << 20), UNSUPPORTED),                    # beyond index range
+    (dict(B=1, H=1, N=8388608), UNSUPPORTED),                                # K/V rows past 2^31 - 1 bytes
 ])
 def test_dense_validation(lib, kw, code):
     assert dense(lib, **kw) == code
@@ -115,6 +116,7 @@ def varlen(lib, cu=CU, nseg=3, H=2, T=300, d=128, scale=0.088, ws=WS, wsb=None, 
     (dict(o=V), INVALID), (dict(ws=O), INVALID),
     (dict(T=0), OK),                                                       # empty batch: no-op, no launch
     (dict(T=0, d=64), UNSUPPORTED), (dict(T=0, H=0), INVALID),
+    (dict(T=4194304, H=2), UNSUPPORTED),                                   # T * H * 256 = 2^31 bytes
 ])
 def test_varlen_validation(lib, kw, code):
     assert varlen(lib, **kw) == code
@@ -197,6 +199,7 @@ def splitkv(lib, q=Q, o=O, N=8192, d=128, slots=64, ws=WS, wsb=None, lse=None):
     (dict(q=None), INVALID), (dict(d=64), UNSUPPORTED), (dict(slots=65537), INVALID),
     (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=WS + 16), WORKSPACE),
     (dict(ws=O), INVALID), (dict(o=K), INVALID),
+    (dict(N=8388608), UNSUPPORTED),                                  # K/V rows past 2^31 - 1 bytes
 ])
 def test_splitkv_validation(lib, kw, code):
     assert splitkv(lib, **kw) == code
@@ -335,6 +338,7 @@ def test_route_accepts_infinite_tau_on_the_host(lib):
     (dict(scale=math.nan), INVALID), (dict(o=SV + 256), INVALID),   # out over v
     (dict(o=SI), INVALID), (dict(lse=SC), INVALID),                  # outputs over the lists
     (dict(o=SR), INVALID),                                           # out over the order
+    (dict(B=1, H=1, N=8388608), UNSUPPORTED),                        # K/V rows past 2^31 - 1 bytes
 ])
 def test_block_sparse_validation(lib, kw, code):
     assert sparse(lib, **kw) == code
@@ -425,6 +429,7 @@ def test_varlen_empty_batch_is_a_no_op(lib):
     (dict(ws=None), WORKSPACE), (dict(wsb=64), WORKSPACE),
     (dict(o=VQ), INVALID), (dict(o=VI), INVALID), (dict(lse=VC), INVALID), (dict(ws=VCU), INVALID),
     (dict(ws=VR), INVALID),
+    (dict(T=4194304, H=2), UNSUPPORTED),                             # T * H * 256 = 2^31 bytes
 ])
 def test_block_sparse_varlen_validation(lib, kw, code):
     assert sparse_v(lib, **kw) == code

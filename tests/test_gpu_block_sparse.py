@@ -16,7 +16,7 @@ import torch
 from oracle.block_sparse import attention_kept, decision_margin, route_blocks
 from workloads import WORKLOADS, make_dense, random_dense
 
-from gpu_util import bits_of, check, dev, dev_i32, f64_of
+from gpu_util import bits_of, check, dev, dev_i32, device_normal_bf16, f64_of
 
 pytestmark = pytest.mark.gpu
 
@@ -424,3 +424,88 @@ def test_packed_varlen_workload_sampled(vd):
     o = f64_of(out).transpose(1, 0, 2).reshape(-1, 128)[rows]
     check(o, o_ref, lse.cpu().numpy().reshape(-1)[rows].astype(np.float64), lse_ref,
           label="block-sparse packed_varlen tau=0.02 sampled rows")
+
+
+# ---------------------------------------------------------------- the largest sequences
+from oracle import attention_dense  # noqa: E402
+
+
+def kept_rows(ids, n):
+    """Key rows of the listed 64-key tiles of a sequence of n keys, in tile order."""
+    return np.concatenate([np.arange(64 * t, min(64 * t + 64, n)) for t in ids])
+
+
+def test_hook_at_the_largest_sequence(vd):
+    """N = 8388607, the longest sequence the kernels address (its K/V rows span N * 256 B =
+    2^31 - 256 bytes): caller lists that reach the last, ragged key tile (63 keys, 2 GiB into
+    the sequence) from query tiles at both ends. Each listed tile's rows against the oracle
+    over its listed keys (dense attention over those keys); unlisted tiles give O = 0."""
+    N = 8388607
+    ntq, ntk = -(-N // 256), -(-N // 64)
+    q, k, v = (device_normal_bf16((1, 1, N, 128), seed=s) for s in (801, 802, 803))
+    stride = vd.block_list_stride(N)
+    kv_idx = torch.full((1, 1, ntq, stride), ntk, dtype=torch.int32, device="cuda:0")
+    kv_cnt = torch.zeros((1, 1, ntq), dtype=torch.int32, device="cuda:0")
+    lists = {0: [0, 65536, ntk - 2, ntk - 1], 1: [ntk - 1], ntq // 2: [1, 2, 3, 100000], ntq - 1: [0, ntk - 1]}
+    for i, ids in lists.items():
+        kv_idx[0, 0, i, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        kv_cnt[0, 0, i] = len(ids)
+    print(f"[max] dense hook N={N}: {ntq} query tiles, lists {lists}", flush=True)
+    out, lse = vd.attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    del kv_idx
+    for i, ids in lists.items():
+        r0, r1 = 256 * i, min(256 * i + 256, N)
+        keys = torch.from_numpy(kept_rows(ids, N)).to("cuda:0")
+        qb = bits_of(q[0, 0, r0:r1])[None, None]
+        kb, vb = bits_of(k[0, 0, keys])[None, None], bits_of(v[0, 0, keys])[None, None]
+        o_ref, lse_ref = attention_dense(qb, kb, vb, SCALE)
+        check(f64_of(out[0, 0, r0:r1]), o_ref[0, 0], lse[0, 0, r0:r1].cpu().numpy().astype(np.float64),
+              lse_ref[0, 0], label=f"block-sparse N={N} query tile {i} keys {ids}")
+    idle = out[0, 0, 256 * 2:256 * 40]
+    assert bool((idle == 0).all()) and bool(torch.isneginf(lse[0, 0, 256 * 2:256 * 40]).all())
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+
+def test_varlen_hook_at_the_largest_batch(vd):
+    """T = 4194303 tokens, H = 2: the largest packed batch the kernels address (T * H * 256 B =
+    2^31 - 512 bytes). Segment 0 (4194003 tokens) lists its last, ragged key tile (19 keys,
+    2 GiB into the tensor) from both of its ends; segment 1 (300 tokens) lists every tile.
+    Checked against the oracle over the listed keys; unlisted tiles give O = 0."""
+    H, T = 2, 4194303
+    cu = [0, T - 300, T]
+    q, k, v = (device_normal_bf16((T, H, 128), seed=s) for s in (811, 812, 813))
+    (G, _, stride), _ = vd.varlen_list_shapes(2, T, H)
+    offs = vd.varlen_tile_offsets(cu)
+    n0 = cu[1]
+    ntq0, ntk0 = -(-n0 // 256), -(-n0 // 64)
+    kv_idx = torch.full((G, H, stride), 0, dtype=torch.int32, device="cuda:0")
+    kv_cnt = torch.zeros((G, H), dtype=torch.int32, device="cuda:0")
+    lists = {(0, 0, 0): [0, ntk0 - 1], (0, 0, 1): [32000, ntk0 - 1],
+             (0, ntq0 - 1, 0): [ntk0 - 2, ntk0 - 1], (0, ntq0 - 1, 1): [ntk0 - 1],
+             (1, 0, 0): [0, 1, 2, 3, 4], (1, 0, 1): [0, 1, 2, 3, 4], (1, 1, 0): [0, 1, 2, 3, 4],
+             (1, 1, 1): [0, 1, 2, 3, 4]}
+    for (s_, i, h), ids in lists.items():
+        ntk_s = -(-(cu[s_ + 1] - cu[s_]) // 64)
+        kv_idx[offs[s_] + i, h, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+        kv_idx[offs[s_] + i, h, len(ids):len(ids) + 8] = ntk_s
+        kv_cnt[offs[s_] + i, h] = len(ids)
+    print(f"[max] varlen hook T={T} H={H} cu={cu}: lists {lists}", flush=True)
+    cu_d = dev_i32(cu)
+    out, lse = vd.attn_fwd_block_sparse_varlen(q, k, v, cu_d, kv_idx, kv_cnt, scale=SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    del kv_idx
+    for (s_, i, h), ids in lists.items():
+        a, n = cu[s_], cu[s_ + 1] - cu[s_]
+        r0, r1 = a + 256 * i, a + min(256 * i + 256, n)
+        keys = torch.from_numpy(a + kept_rows(ids, n)).to("cuda:0")
+        qb = bits_of(q[r0:r1, h])[None, None]
+        kb, vb = bits_of(k[keys, h])[None, None], bits_of(v[keys, h])[None, None]
+        o_ref, lse_ref = attention_dense(qb, kb, vb, SCALE)
+        check(f64_of(out[r0:r1, h]), o_ref[0, 0], lse[h, r0:r1].cpu().numpy().astype(np.float64), lse_ref[0, 0],
+              label=f"block-sparse varlen T={T} segment {s_} tile {i} head {h} keys {ids}")
+    idle = out[256:256 * 40]
+    assert bool((idle == 0).all()) and bool(torch.isneginf(lse[:, 256:256 * 40]).all())
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()

@@ -35,6 +35,17 @@ long long product(long long a, long long b, long long c, long long d) {
     return r;
 }
 
+// The attention kernels read one sequence's K and V rows through buffer resources whose
+// record count is a signed 32-bit byte count, so the bytes from a sequence's first key row to
+// its end must stay within INT_MAX. Dense rows of one (b, h) are d*2 bytes apart, so N*d*2
+// bytes; packed rows are H*d*2 apart, and any segment is at most total_tokens long.
+int check_kv_span(long long tokens, long long row_bytes) {
+    const long long span = product(tokens, row_bytes, 1, 1);
+    if (span < 0 || span > INT_MAX)
+        return fail(ATTN_ERR_UNSUPPORTED, "a sequence's K/V rows span more than 2^31 - 1 bytes");
+    return ATTN_OK;
+}
+
 int check_common(const void* q, const void* k, const void* v, void* out, int H, int d, float scale) {
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
         return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be non-null device pointers");
@@ -88,6 +99,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     if (B <= 0 || N <= 0) return fail(ATTN_ERR_INVALID_ARG, "B and N must be >= 1");
     const long long elems = product(B, H, N, d);
     if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    st = check_kv_span(N, 2LL * d);
+    if (st != ATTN_OK) return st;
     const long long tiles = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
     if (tiles < 0 || tiles > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
     st = check_aliasing(q, k, v, out, lse, (size_t)elems * 2, (size_t)product(B, H, N, 1) * 4);
@@ -113,6 +126,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
     if (slots > ATTN_MAX_SLOTS) return fail(ATTN_ERR_INVALID_ARG, "slots exceeds ATTN_MAX_SLOTS");
     const long long elems = product(B, H, N, d);
     if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    st = check_kv_span(N, 2LL * d);
+    if (st != ATTN_OK) return st;
     const long long tiles = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
     if (tiles < 0 || tiles + ATTN_MAX_SLOTS > INT_MAX / 16)
         return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
@@ -261,6 +276,8 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out
     if (B <= 0 || N <= 0) return fail(ATTN_ERR_INVALID_ARG, "B and N must be >= 1");
     const long long elems = product(B, H, N, d);
     if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    st = check_kv_span(N, 2LL * d);
+    if (st != ATTN_OK) return st;
     const long long items = product(B, H, (N + attn_impl::tile_rows() - 1) / attn_impl::tile_rows(), 1);
     if (items < 0 || items > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
     const size_t tb = (size_t)elems * 2, lb = (size_t)product(B, H, N, 1) * 4;
@@ -351,6 +368,8 @@ int attn_fwd_block_sparse_varlen(const void* q, const void* k, const void* v, vo
     if (st != ATTN_OK) return st;
     const long long elems = product(total_tokens, H, d, 1);
     if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    st = check_kv_span(total_tokens, 2LL * H * d);
+    if (st != ATTN_OK) return st;
     size_t idx_bytes = 0, cnt_bytes = 0;
     st = check_varlen_lists(cu_seqlens, kv_idx, kv_cnt, nseg, H, total_tokens, idx_bytes, cnt_bytes);
     if (st != ATTN_OK) return st;
@@ -444,6 +463,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
     if (cu_seqlens == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens must be a non-null device pointer");
     const long long elems = product(total_tokens, H, d, 1);
     if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    st = check_kv_span(total_tokens, 2LL * H * d);
+    if (st != ATTN_OK) return st;
     const long long grid = product((long long)total_tokens / attn_impl::tile_rows() + nseg, H, 1, 1);
     if (grid < 0 || grid > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
     const size_t need = attn_impl::varlen_workspace_bytes(nseg, total_tokens);
