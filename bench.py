@@ -116,8 +116,9 @@ def write_traffic_profile(args) -> int:
     if copy_bytes <= 0:
         raise SystemExit("--calibrate-copy-mib (the copy size of the profiled run) is required")
 
-    def base(name):
-        return name.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
+    def base(name):   # "void (anonymous namespace)::pool_kernel<64>(...)" -> "pool_kernel"
+        name = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
+        return name.split("::")[-1].split()[-1]
 
     def of_call(name):
         return base(name) in names
@@ -521,6 +522,21 @@ def time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, dense_ms: flo
     return rec
 
 
+def head_share(w, heads: int):
+    """The workload restricted to its first `heads` heads: one GPU's share when the heads are
+    split over GPUs (each head's values are the full workload's, since the seeded streams are
+    spawned head by head)."""
+    import dataclasses
+    if w.kind != "dense" or not 1 <= heads <= w.H:
+        raise SystemExit(f"--heads needs a dense workload and 1 <= heads <= {w.H}")
+    if heads == w.H:
+        return w
+    desc = w.description.replace(f"H={w.H}", f"H={heads}")
+    if w.H % heads == 0:
+        desc += f", one GPU's share of a {w.H // heads}-way head split"
+    return dataclasses.replace(w, name=f"{w.name}_h{heads}", H=heads, description=desc)
+
+
 def oracle_cores() -> int:
     """Threads the FP64 oracle's BLAS calls use on this host."""
     from threadpoolctl import threadpool_info
@@ -541,6 +557,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="video_720p")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="dense workloads: run the first HEADS heads only (the same values), i.e. one "
+                         "GPU's share of a head-sharded call at full N (0: all heads)")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows of the seeded sample the FP64 oracle is timed and checked on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -585,6 +604,8 @@ def main() -> int:
     from workloads import WORKLOADS, make_dense, make_varlen, sample_rows
 
     w = WORKLOADS[args.workload]
+    if args.heads > 0:
+        w = head_share(w, args.heads)
     t0 = time.time()
     if w.kind == "dense":
         qb, kb, vb = make_dense(w)
@@ -674,8 +695,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(w.name, kernel, split),
-            "kernel_ms": {"avg": round(avg_kernel_ms, 4), "min": round(min(kernel_ms), 4),
-                          "max": round(max(kernel_ms), 4)},
+            "kernel_ms": {"avg": round(avg_kernel_ms, 4), "median": round(float(np.median(kernel_ms)), 4),
+                          "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
         },
         "cpu_baseline": None,
     }
@@ -723,6 +744,20 @@ def main() -> int:
             "sample": f"{rows.size} seeded query rows of {w.name} (each over its full key range), "
                       f"FP64 NumPy/OpenBLAS, {cpu_s:.1f} s",
         }
+        # the same oracle on one core (BLAS limited to one thread), on the first eighth of the rows
+        from threadpoolctl import threadpool_limits
+        rows1 = rows[:max(1, rows.size // 8)]
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            if w.kind == "dense":
+                attention_dense(qb, kb, vb, w.scale, rows=rows1)
+            else:
+                attention_varlen(qb, kb, vb, cu, w.scale, rows=rows1)
+            cpu1_s = time.perf_counter() - t1
+        flops1 = float(np.sum(4.0 * w.d * keys_per_row[:rows1.size]))
+        result["cpu_baseline"]["one_core"] = {
+            "value": round(flops1 / cpu1_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "sample": f"the first {rows1.size} of those rows, BLAS on one thread, {cpu1_s:.2f} s"}
         # parity of the same rows on the GPU output of the last timed step
         og = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         og = (og.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

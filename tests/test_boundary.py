@@ -259,12 +259,16 @@ def linear(lib, q=LQ, k=LK, qr=LQR, kr=LKR, v=LV, o=LO, B=1, N=300, H=2, d=128, 
 
 def test_linear_workspace_query(lib):
     f = lib.attn_linear_workspace_bytes
-    # per head: one chunk partial (128*128 + 128 floats) per 2048 tokens, then kv as three
-    # BF16 terms and ksum (FP32), each region 256-byte aligned
+    # per head: one chunk partial (128*128 + 128 floats) per chunk, then kv as three BF16
+    # terms and ksum (FP32), each region 256-byte aligned. A chunk is 2048 tokens, halved down
+    # to 256 while B*H*chunks < 512.
     a = lambda x: (x + 255) // 256 * 256
     one, terms, ks = (128 * 128 + 128) * 4, 3 * 128 * 128 * 2, 128 * 4
-    assert f(1, 300, 2, 128) == a(2 * one) + a(2 * terms) + a(2 * ks)
-    assert f(1, 180320, 16, 128) == a(16 * 89 * one) + a(16 * terms) + a(16 * ks)
+    assert f(1, 300, 2, 128) == a(2 * 2 * one) + a(2 * terms) + a(2 * ks)            # 256-token chunks
+    assert f(1, 180320, 16, 128) == a(16 * 89 * one) + a(16 * terms) + a(16 * ks)    # 2048: 1424 groups
+    assert f(1, 180320, 2, 128) == a(2 * 353 * one) + a(2 * terms) + a(2 * ks)       # 512: 706 groups
+    assert f(1, 180320, 4, 128) == a(4 * 177 * one) + a(4 * terms) + a(4 * ks)       # 1024: 708 groups
+    assert f(1, 180320, 8, 128) == a(8 * 89 * one) + a(8 * terms) + a(8 * ks)        # 2048: 712 groups
     assert f(0, 300, 2, 128) == 0 and f(1, 300, 2, 64) == 0
 
 

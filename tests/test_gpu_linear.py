@@ -44,7 +44,7 @@ def check(got_bits, exact, label):
     (1, (1, 1, 1), 1),          # one token
     (1, (2, 3, 5), 2),
     (2, (3, 4, 7), 3),
-    (1, (2, 16, 80), 4),        # 2560 tokens: two key chunks (2048 + 512), ragged output block
+    (1, (2, 16, 80), 4),        # 2560 tokens: ten 256-token key chunks, ragged output block
     (1, (1, 30, 52), 16),
 ])
 def test_small_shapes_in_full(vd, B, grid, H):
@@ -82,3 +82,16 @@ def test_480p_grid_sampled_tokens(vd):
     rng = np.random.default_rng(480)
     toks = np.unique(np.concatenate([rng.choice(N, 1024, replace=False), np.arange(N - 300, N)]))
     check(out[:, toks], linear_attention(*x, tokens=toks), "480p sampled")
+
+
+def test_720p_grid_two_heads_sampled_tokens(vd):
+    """One GPU's share of an 8-way head split at 720p (180320 tokens, 2 heads): the kv pass
+    cuts each sequence into 353 chunks of 512 tokens, the last one ragged. Outputs on 512
+    seeded tokens and the last 200 against the oracle over every token."""
+    grid = (49, 46, 80)
+    N = 49 * 46 * 80
+    x = make_linear_inputs(1, grid, 2, seed=7202)
+    out = bits_of(vd.linear_attention(*[dev(t) for t in x]))
+    rng = np.random.default_rng(7202)
+    toks = np.unique(np.concatenate([rng.choice(N, 512, replace=False), np.arange(N - 200, N)]))
+    check(out[:, toks], linear_attention(*x, tokens=toks), "720p H2 sampled")

@@ -99,3 +99,18 @@ def test_video_720p_shape_sampled_tokens(vd):
     for name, x, t in (("q", xq, q), ("k", xk, k)):
         check_qk(bits_of(t)[:, :, toks], qk_norm_rope(x, grid, tokens=toks), f"{name} 720p sampled")
     assert np.array_equal(bits_of(v)[:, :, toks], v_head_major(xv[:, toks]))
+
+
+def test_video_720p_two_heads_sampled_tokens(vd):
+    """One GPU's share of an 8-way head split at 720p (2 heads): each 16-lane group takes a
+    token of its own. 2048 seeded tokens plus the first and last 64 against the oracle."""
+    grid = (49, 46, 80)
+    N = 49 * 46 * 80
+    xq, xk, xv = make_projected(1, grid, 2, seed=7202)
+    q, k, v = vd.qk_prologue(dev(xq), dev(xk), dev(xv), grid=grid)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7202)
+    toks = np.unique(np.concatenate([rng.choice(N, 2048, replace=False), np.arange(64), np.arange(N - 64, N)]))
+    for name, x, t in (("q", xq, q), ("k", xk, k)):
+        check_qk(bits_of(t)[:, :, toks], qk_norm_rope(x, grid, tokens=toks), f"{name} 720p H2 sampled")
+    assert np.array_equal(bits_of(v), v_head_major(xv))

@@ -174,3 +174,19 @@ def test_flops_counting():
     assert WORKLOADS["packed_varlen"].flops() == pytest.approx(
         4 * 24 * 128 * (30000 ** 2 + 6000 ** 2 + 2048 ** 2))
     assert WORKLOADS["packed_varlen"].total_tokens == 38048
+
+
+def test_first_heads_do_not_depend_on_the_head_count():
+    """Per-head seeded streams: a workload cut to its first heads (one GPU's share of a
+    head-sharded call) holds exactly the full workload's values for those heads."""
+    import dataclasses
+    w = WORKLOADS["tiny_dense"]
+    full = make_dense(w)
+    part = make_dense(dataclasses.replace(w, H=1))
+    for a, b in zip(full, part):
+        assert np.array_equal(a[:, :1], b)
+    w = WORKLOADS["video_480p"]
+    two = make_dense(dataclasses.replace(w, H=2))
+    one = make_dense(dataclasses.replace(w, H=1))
+    for a, b in zip(two, one):
+        assert np.array_equal(a[:, :1], b)

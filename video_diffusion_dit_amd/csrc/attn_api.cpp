@@ -198,7 +198,8 @@ int attn_linear_fwd(const void* q, const void* k, const void* q_rot, const void*
     if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
     if (!isfinite(eps) || eps < 0.f) return fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
     const long long elems = product(B, N, H, d);
-    if (elems < 0 || product(B, H, (N + 255) / 256, 1) > INT_MAX / 2) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    if (elems < 0 || product(B, H, (N + 255) / 256, 1) > INT_MAX / 2 || product(B, H, 512, 1) > INT_MAX)
+        return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
     if (product(N, H, d, 2) > INT_MAX)   // one (b, h) slice is addressed with 32-bit buffer offsets
         return fail(ATTN_ERR_UNSUPPORTED, "N * H * d * 2 bytes exceeds 2^31 - 1");
     const size_t bytes = (size_t)elems * 2;

@@ -12,13 +12,16 @@
 //
 // Inputs q, k, q_rot, k_rot, v and the output are BF16 rows in the token-major layout the
 // QKV projection writes, [B, N, H, 128]. Three kernels:
-//   linear_kv_partial_kernel  one workgroup per (b, h, chunk of KV_CHUNK tokens): the chunk's
+//   linear_kv_partial_kernel  one workgroup per (b, h, chunk of tokens): the chunk's
 //       kv (v_mfma_f32_32x32x16_bf16, FP32 accumulation) and ksum (FP32 VALU) into the
 //       workspace. V and K_rot tiles go through LDS; transposing LDS reads
 //       (ds_read_b64_tr_b16) give each lane 8 consecutive tokens of one dim, the MFMA's
 //       operand layout for both A = V^T and B = K_rot.
-//   linear_kv_reduce_kernel   sums the chunk partials in chunk order (deterministic) and
-//       splits kv exactly into three BF16 terms.
+//   linear_kv_reduce_kernel   sums the chunk partials in a fixed order (deterministic) and
+//       splits kv exactly into three BF16 terms. A chunk is 2048 tokens, halved (down to 256)
+//       while the kv pass would have fewer than 512 workgroups, so calls with few heads
+//       (one GPU's share of a head-sharded call) still fill the compute units; the chunk
+//       depends only on B*H and N.
 //   linear_out_kernel         one workgroup per (b, h, 1024 tokens): out = kv q_rot / den;
 //       each wave keeps 32 rows of kv in registers, q_rot arrives in LDS by buffer->LDS loads.
 //       The FP32 product runs on the BF16 matrix cores: kv = hi + mid + lo with three BF16
@@ -44,7 +47,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = 128;
 constexpr int NT = 256;              // threads per workgroup (4 waves)
 constexpr int TILE = 64;             // tokens per LDS tile in the kv pass
-constexpr int KV_CHUNK = 2048;       // tokens per workgroup in the kv pass (a multiple of TILE)
+constexpr int KV_CHUNK_MAX = 2048;   // tokens per workgroup in the kv pass (multiples of TILE)
+constexpr int KV_CHUNK_MIN = 256;
+#ifndef LIN_KV_MIN_GROUPS
+#define LIN_KV_MIN_GROUPS 512        // kv-pass workgroups below which the chunk is halved
+#endif
 constexpr int ROW = D * 2 + 32;      // LDS row stride in bytes (padded: 8-bank shift per row)
 constexpr int KV_TERMS = 3;          // BF16 terms of the FP32 kv in the output pass
 #define LIN_OUT_SUB 128              // tokens per sub-block of the output pass (a multiple of 64)
@@ -76,6 +83,7 @@ struct LinearArgs {
     bf16* terms;      // [BH][KV_TERMS][D][D] kv = hi + mid + lo, BF16
     float* ksum;      // [BH][D]
     int N, H, S;      // tokens, heads, chunks per sequence
+    int chunk;        // tokens per chunk
     float eps;
 };
 
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(NT) void linear_kv_partial_kernel(LinearArgs a) {
     const int b = bh / a.H, h = bh - b * a.H;
     const long row_stride = (long)a.H * D;                       // elements between tokens
     const long base = ((long)b * a.N * a.H + h) * D;             // (b, token 0, h)
-    const int m0 = s * KV_CHUNK, m1 = min(a.N, m0 + KV_CHUNK);
+    const int m0 = s * a.chunk, m1 = min(a.N, m0 + a.chunk);
 
     // loads: thread -> (row tid/16 (+16, +32, +48), 8-dim chunk tid%16)
     const int lr = tid >> 4, lc = tid & 15;
@@ -174,26 +182,65 @@ __global__ __launch_bounds__(NT) void linear_kv_partial_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------- chunk partials -> kv, ksum
+// A partial is (D*D + D) FP32 values, read as groups of 4 (16-byte loads). RS threads share a
+// group: thread sl sums chunks sl, sl + RS, ... in order, then the RS sums are added in sl
+// order (a fixed order, so the result is deterministic). A wave reads whole 256-byte rows of
+// 64 / RG partials at once, so RS chunks are in flight per group.
+#ifndef LIN_REDUCE_SPLIT
+#define LIN_REDUCE_SPLIT 16
+#endif
+constexpr int RS = LIN_REDUCE_SPLIT;
+constexpr int RG = NT / RS;                      // 4-value groups per workgroup
+constexpr int PART_GROUPS = (D * D + D) / 4;
+constexpr int REDUCE_BLOCKS = (PART_GROUPS + RG - 1) / RG;
+static_assert((D * D + D) % 4 == 0 && RG >= 16 && 64 % RG == 0, "reduce layout");
+
+__device__ __forceinline__ void split_terms(float sum, bf16* t) {
+    // exact split of the FP32 sum into three BF16 terms (8 significant bits each)
+    const bf16 hi = (bf16)sum;
+    const float r1 = sum - (float)hi;
+    const bf16 mid = (bf16)r1;
+    const bf16 lo = (bf16)(r1 - (float)mid);
+    t[0] = hi;
+    t[D * D] = mid;
+    t[2 * D * D] = lo;
+}
+
 __global__ __launch_bounds__(NT) void linear_kv_reduce_kernel(LinearArgs a) {
-    const int per = (D * D + D + NT - 1) / NT;
-    const int bh = blockIdx.x / per, blk = blockIdx.x - bh * per;
-    const int e = blk * NT + threadIdx.x;
-    if (e >= D * D + D) return;
-    const float* p = a.part + (long)bh * a.S * (D * D + D) + e;
-    float sum = 0.f;
-    for (int s = 0; s < a.S; ++s) sum += p[(long)s * (D * D + D)];
-    if (e < D * D) {
-        // exact split of the FP32 sum into three BF16 terms (8 significant bits each)
-        const bf16 hi = (bf16)sum;
-        const float r1 = sum - (float)hi;
-        const bf16 mid = (bf16)r1;
-        const bf16 lo = (bf16)(r1 - (float)mid);
-        bf16* t = a.terms + (long)bh * KV_TERMS * D * D + e;
-        t[0] = hi;
-        t[D * D] = mid;
-        t[2 * D * D] = lo;
+    __shared__ float4 red[RS][RG];
+    const int bh = blockIdx.x / REDUCE_BLOCKS, blk = blockIdx.x - bh * REDUCE_BLOCKS;
+    const int gl = threadIdx.x % RG, sl = threadIdx.x / RG;
+    const int grp = blk * RG + gl;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (grp < PART_GROUPS) {
+        const float4* p = reinterpret_cast<const float4*>(a.part + (long)bh * a.S * (D * D + D)) + grp;
+        for (int s = sl; s < a.S; s += RS) {
+            const float4 x = p[(long)s * PART_GROUPS];
+            sum.x += x.x;
+            sum.y += x.y;
+            sum.z += x.z;
+            sum.w += x.w;
+        }
+    }
+    red[sl][gl] = sum;
+    __syncthreads();
+    if (sl != 0 || grp >= PART_GROUPS) return;
+    for (int r = 1; r < RS; ++r) {
+        const float4 x = red[r][gl];
+        sum.x += x.x;
+        sum.y += x.y;
+        sum.z += x.z;
+        sum.w += x.w;
+    }
+    const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+    const int e0 = 4 * grp;                      // D*D is a multiple of 4: a group is all kv or all ksum
+    if (e0 < D * D) {
+        bf16* t = a.terms + (long)bh * KV_TERMS * D * D + e0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_terms(v[i], t + i);
     } else {
-        a.ksum[(long)bh * D + e - D * D] = sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.ksum[(long)bh * D + e0 - D * D + i] = v[i];
     }
 }
 
@@ -466,14 +513,23 @@ __global__ __launch_bounds__(NT, LIN_OUT_SUB == 128 ? 2 : 1) void linear_out_ker
 
 namespace attn_impl {
 
-int linear_chunks(int N) { return (N + KV_CHUNK - 1) / KV_CHUNK; }
+static int kv_chunk(size_t bh, int N) {
+    int c = KV_CHUNK_MAX;
+    while (c > KV_CHUNK_MIN && bh * (size_t)((N + c - 1) / c) < (size_t)LIN_KV_MIN_GROUPS) c >>= 1;
+    return c;
+}
+
+static int linear_chunks(size_t bh, int N) {
+    const int c = kv_chunk(bh, N);
+    return (N + c - 1) / c;
+}
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // [partials: BH x S x (D*D + D) FP32][terms: BH x 3 x D x D BF16][ksum: BH x D FP32]
 size_t linear_workspace_bytes(int B, int N, int H) {
     const size_t bh = (size_t)B * H;
-    return align256(bh * (size_t)linear_chunks(N) * (D * D + D) * sizeof(float)) +
+    return align256(bh * (size_t)linear_chunks(bh, N) * (D * D + D) * sizeof(float)) +
            align256(bh * KV_TERMS * D * D * sizeof(bf16)) + align256(bh * D * sizeof(float));
 }
 
@@ -488,9 +544,10 @@ hipError_t launch_linear(const void* q, const void* k, const void* qr, const voi
     a.out = static_cast<bf16*>(out);
     a.N = N;
     a.H = H;
-    a.S = linear_chunks(N);
-    a.eps = eps;
     const size_t bh = (size_t)B * H;
+    a.chunk = kv_chunk(bh, N);
+    a.S = (N + a.chunk - 1) / a.chunk;
+    a.eps = eps;
     char* ws = static_cast<char*>(workspace);
     const size_t part = align256(bh * (size_t)a.S * (D * D + D) * sizeof(float));
     const size_t terms = align256(bh * KV_TERMS * D * D * sizeof(bf16));
@@ -500,8 +557,7 @@ hipError_t launch_linear(const void* q, const void* k, const void* qr, const voi
     hipLaunchKernelGGL(linear_kv_partial_kernel, dim3((unsigned)(bh * a.S)), dim3(NT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int per = (D * D + D + NT - 1) / NT;
-    hipLaunchKernelGGL(linear_kv_reduce_kernel, dim3((unsigned)(bh * per)), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(linear_kv_reduce_kernel, dim3((unsigned)(bh * REDUCE_BLOCKS)), dim3(NT), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long ntb = (N + OUT_TOK - 1) / OUT_TOK;

@@ -14,10 +14,12 @@
 // (Q/K/V reach attention in BF16 after RMSNorm and RoPE); page "PR #35728 report", related
 // context (a fused 3-D RoPE kernel for the LTX-2.5 decoder).
 //
-// Work decomposition: one wave per token. A 16-lane group owns one 256-byte row at a time
-// (lane j: channels 8j..8j+7, i.e. RoPE pairs 4j..4j+3), so one wave instruction moves four
-// rows; each group keeps four rows in flight (loads issued before any use). The row's sum of
-// squares is reduced across its 16 lanes. The token's angles are the same for every head
+// Work decomposition: a 16-lane group owns one 256-byte row at a time (lane j: channels
+// 8j..8j+7, i.e. RoPE pairs 4j..4j+3), so one wave instruction moves four rows; each group
+// keeps four rows in flight (loads issued before any use). The row's sum of squares is reduced
+// across its 16 lanes. With more than 4 heads a wave takes one token and its four groups split
+// the token's rows; with 4 heads or fewer (a token has at most 8 Q/K rows, e.g. one GPU's share
+// of a head-sharded call) each group takes a token of its own, so no group idles. The token's angles are the same for every head
 // and for Q and K: each lane computes its four (cos, sin) once per token, from FP64 angles
 // (theta^(-k/P) and pos * freq in FP64, then sincos), so the angle error stays near 1e-16
 // rad instead of the ~1e-5 that FP32 products reach at pos ~ 80. Memory-bound: 256 bytes
@@ -95,11 +97,16 @@ __device__ __forceinline__ u32x4 norm_rope(f32x8 x, const float (&w)[8], const f
     return out;
 }
 
+// A token's Q/K/V rows are split over GROUPS 16-lane groups (4: one token per wave; 1: one
+// token per group).
+template <int GROUPS>
 __global__ __launch_bounds__(WAVES * 64) void qk_prologue_kernel(PrologueArgs a) {
     const int lane = threadIdx.x & 63;
-    const int grp = lane >> 4, j = lane & 15;
-    const long tok = (long)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    if (tok >= a.tokens) return;
+    const int j = lane & 15;
+    const int grp = GROUPS == 4 ? lane >> 4 : 0;
+    const long tok = GROUPS == 4 ? (long)blockIdx.x * WAVES + (threadIdx.x >> 6)
+                                 : (long)blockIdx.x * WAVES * 4 + (threadIdx.x >> 4);
+    if (tok >= a.tokens) return;   // a whole group (16 lanes) leaves together
     const long b = tok / a.N;
     const int n = (int)(tok - b * a.N);
     const int pos[3] = {n / (a.Hp * a.Wp), (n / a.Wp) % a.Hp, n % a.Wp};
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(WAVES * 64) void qk_prologue_kernel(PrologueArgs a)
     const long in_row = (long)tok * a.H;                  // first row of this token in [B*N, H]
     const long out_tok = (long)b * a.H * a.N + n;         // row (b, 0, n) of [B, H, N]
     // Q and K: rows r = 0..2H-1 (r < H: Q head r, else K head r - H), four per group in flight
-    for (int r0 = grp * ROWS; r0 < 2 * a.H; r0 += 4 * ROWS) {
+    for (int r0 = grp * ROWS; r0 < 2 * a.H; r0 += GROUPS * ROWS) {
         f32x8 x[ROWS];
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) {
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(WAVES * 64) void qk_prologue_kernel(PrologueArgs a)
         }
     }
     if (a.xv == nullptr) return;
-    for (int r0 = grp * ROWS; r0 < a.H; r0 += 4 * ROWS) {
+    for (int r0 = grp * ROWS; r0 < a.H; r0 += GROUPS * ROWS) {
         u32x4 x[ROWS];
 #pragma unroll
         for (int u = 0; u < ROWS; ++u)
@@ -183,8 +190,13 @@ hipError_t launch_qk_prologue(const void* xq, const void* xk, const void* xv, vo
     a.Wp = Wp;
     a.eps = eps;
     a.log2_theta = log2((double)theta);
-    const long grid = (a.tokens + WAVES - 1) / WAVES;
-    hipLaunchKernelGGL(qk_prologue_kernel, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+    if (H <= 4) {
+        const long grid = (a.tokens + 4 * WAVES - 1) / (4 * WAVES);
+        hipLaunchKernelGGL(qk_prologue_kernel<1>, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+    } else {
+        const long grid = (a.tokens + WAVES - 1) / WAVES;
+        hipLaunchKernelGGL(qk_prologue_kernel<4>, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
