@@ -14,9 +14,12 @@ motivation (online softmax over KV blocks).
 One wave per SIMD owns 64 query rows (row blocks rb = 0, 1 of 32 rows) and walks all 64-key
 tiles t of its key range. Per tile:
     QK(t+1): 32 MFMAs  S^T = K.Q^T into the other S buffer, beside the second softmax half of
-                       tile t (keys 32..63), then the rescale check of tile t
+                       tile t (keys 32..63), then the rescale check of tile t; the first
+                       V fragments of tile t are read after its 25th MFMA
     PV(t):   32 MFMAs  O^T += V^T.P^T, beside the first softmax half of tile t+1 (keys 0..31);
-                       in its middle the one barrier of the tile, then the loads of tile t+3
+                       in its middle the one barrier of the tile, then the loads of tile t+3,
+                       and after its 25th MFMA the first K fragments of tile t+2 (visible
+                       since the barrier)
 so that about 3.5 VALU instructions issue in the shadow of every MFMA. K and V tiles sit in
 four LDS stages (K at 16 KiB * stage, V at 64 KiB + 16 KiB * stage) and arrive by
 buffer->LDS loads three tiles ahead. Tile t uses stage t%4 and S buffer t%2, so the loop body
@@ -102,8 +105,10 @@ OPTS = {
     "k_ahead": 2,        # K fragments read this many fragment pairs ahead of their MFMAs
     "v_ahead": 2,        # V fragments likewise
     "qk_valu_slots": 30, # QK phase: the exp work and the check spread over this many MFMAs
-    "pv_valu_slots": 29, # PV phase: the exp work spread over this many MFMAs
+    "pv_valu_slots": 31, # PV phase: the exp work spread over this many MFMAs
     "barrier_after": 15, # PV phase: barrier and tile loads after this MFMA
+    "kpre_after": 24,    # PV phase: the next QK phase's first K fragments read after this MFMA
+    "vpre_after": 24,    # QK phase: the next PV phase's first V fragments read after this MFMA
     "limit_bits": RESCALE_LIMIT_BITS,
 }
 
@@ -604,7 +609,7 @@ def generate(backedge=None):
     for k in range(4):
         X, Y = k % 2, (k + 1) % 2
         qk_phase(E, Y, (k + 1) % 4, softmax_half(X, 1, False, None, H2) + check_ops(), valu_slots=OPTS["qk_valu_slots"],
-                 extra={31: [lambda E, st=k: prefetch_v(E, st)]})
+                 extra={OPTS["vpre_after"]: [lambda E, st=k: prefetch_v(E, st)]})
         rare_call(E, X, k, "A%d" % k)
         add_l(E)
         E.salu("s_cmp_eq_u32 s%d, s%d" % (S_T, S_TLAST))
@@ -614,7 +619,8 @@ def generate(backedge=None):
         extra = {bar: [lambda E: E.raw("s_waitcnt vmcnt(0)"), lambda E: E.raw("s_barrier")]}
         for i, f in enumerate(tile_loads((k + 3) % 4)):
             extra.setdefault(bar + 1 + i, []).append(f)
-        extra.setdefault(30, []).append(lambda E, st=(k + 2) % 4: prefetch_k(E, st))
+        assert OPTS["kpre_after"] > bar, "K of the next tile is visible only after the barrier"
+        extra.setdefault(OPTS["kpre_after"], []).append(lambda E, st=(k + 2) % 4: prefetch_k(E, st))
         pv_phase(E, X, k, softmax_half(Y, 0, False, None, H1), valu_slots=OPTS["pv_valu_slots"], extra=extra)
         E.salu("s_add_u32 s%d, s%d, 1" % (S_T, S_T))
     loop_end = [list(h) for h in E.hists]
