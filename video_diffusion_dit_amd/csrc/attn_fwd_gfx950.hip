@@ -45,7 +45,9 @@
 // partial). The common path computes P with the current m_ref and only checks that no
 // lane's tile sum exceeds 2^24 (then no probability exceeds 2^24, far from FP32 overflow);
 // otherwise (always on a row's first tile, where m_ref = -inf) the wave recomputes S from
-// LDS and takes the exact path: true row max, rescale of O and l, recompute of P. The result
+// LDS and takes the exact path: m_ref = true row max + 32 (so the largest probability is
+// 2^-32 and a later key must beat the max by 56 before the next exact path), rescale of O
+// and l, recompute of P. The result
 // is the same softmax; only the reference the BF16 probabilities are taken against differs,
 // and BF16 rounding is relative, so its error bound does not depend on it.
 #include <hip/hip_runtime.h>

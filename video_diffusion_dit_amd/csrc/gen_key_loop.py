@@ -29,7 +29,8 @@ Softmax bookkeeping (per row block): m (the reference the probabilities are take
 log2 units of the scaled logit) and l (the lane's partial row sum). The common path computes
 p = exp2(S*c - m) and checks that no lane's tile sum exceeds 2^24; when one does (always on the
 first tile, where m = -inf) the wave calls the exact path, which recomputes S of the tile
-from LDS, moves m to the running row maximum, rescales O and l, and recomputes P.
+from LDS, moves m to the running row maximum plus a headroom of 32, rescales O and l, and
+recomputes P.
 
 Register map (per lane):
     v[0:63], v[64:127]   S buffers: block (rb, kb) at 16*(2*kb + rb); P packed to BF16 in
@@ -64,6 +65,7 @@ for the gfx950 wait states that hand-written code must provide itself:
     SALU write of M0 -> buffer load to LDS                              1
 """
 import os
+import struct
 import sys
 
 # ---------------------------------------------------------------- register map
@@ -100,6 +102,13 @@ V_STAGE = 16384
 # running maximum keeps climbing (outlier channels).
 RESCALE_LIMIT_BITS = 0x4B800000
 
+# Headroom: the exact path sets the reference m to the row's running maximum + 32 instead of
+# the maximum itself, so a later key must exceed that maximum by more than 24 + 32 log2 units
+# before the wave takes the exact path again (rows whose maximum keeps climbing, as with
+# outlier channels, take it far less often). Probabilities right after a move are <= 2^-32;
+# a key more than 94 log2 units below the maximum (relative weight < 2^-94) can fall below
+# the FP32 normal range, and sum(p v) stays normal while max|v| >= 2^-94.
+
 # Schedule knobs (the values the kernel is built with).
 OPTS = {
     "k_ahead": 2,        # K fragments read this many fragment pairs ahead of their MFMAs
@@ -110,6 +119,7 @@ OPTS = {
     "kpre_after": 24,    # PV phase: the next QK phase's first K fragments read after this MFMA
     "vpre_after": 24,    # QK phase: the next PV phase's first V fragments read after this MFMA
     "limit_bits": RESCALE_LIMIT_BITS,
+    "headroom": 32,      # the exact path moves m to the running maximum plus this (log2 units)
 }
 
 
@@ -519,6 +529,9 @@ def rare_path(E, X):
     alpha = (TMP0 + 15, TMP0 + 16)
     for rb in range(2):
         E.valu("v_max_f32 %s, %s, %s" % (vr(tm[rb]), vr(tm[rb]), vr(tm2[rb])), rd=vset(tm[rb]) | vset(tm2[rb]), wr=vset(tm[rb]))
+        if OPTS["headroom"]:
+            E.valu("v_add_f32 %s, 0x%08x, %s" % (vr(tm[rb]), struct.unpack("<I", struct.pack("<f", float(OPTS["headroom"])))[0],
+                                                 vr(tm[rb])), rd=vset(tm[rb]), wr=vset(tm[rb]))
         E.valu("v_max_f32 %s, %s, %s" % (vr(tm[rb]), vr(tm[rb]), vr(M[rb])), rd=vset(tm[rb]) | vset(M[rb]), wr=vset(tm[rb]))
         E.valu("v_sub_f32 %s, %s, %s" % (vr(alpha[rb]), vr(M[rb]), vr(tm[rb])), rd=vset(M[rb]) | vset(tm[rb]), wr=vset(alpha[rb]))
         E.trans("v_exp_f32 %s, %s" % (vr(alpha[rb]), vr(alpha[rb])), rd=vset(alpha[rb]), wr=vset(alpha[rb]))
