@@ -175,6 +175,124 @@ def write_traffic_profile(args) -> int:
     return 0
 
 
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+FLOP_PER_MFMA = 32 * 32 * 16 * 2      # v_mfma_f32_32x32x16_bf16, the only MFMA the attention kernels issue
+
+
+def write_mfma_profile(args) -> int:
+    """Turn one rocprofv3 --pmc run of SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE into the profiles/ record of one call's matrix-core use: counter FLOP per
+    call (MFMA instructions x 32768) against the algorithmic 4*B*H*N^2*d, that FLOP over the
+    kernels' own durations in the same run against the published peak, the fraction of clocked
+    cycles the matrix cores were busy, and the average shader clock."""
+    import csv
+    counter_csv, agent_csv = args.write_mfma_profile
+    kind = args.traffic_kind or ("varlen" if "varlen" in args.workload else "dense")
+    names = CALL_KERNELS[kind]
+    kernel = names[0]
+
+    def base(name):
+        name = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
+        return name.split("::")[-1].split()[-1]
+
+    vals, spans, kname = {}, {}, {}
+    with open(counter_csv) as f:
+        for row in csv.DictReader(f):
+            if base(row["Kernel_Name"]) not in names:
+                continue
+            d = int(row["Dispatch_Id"])
+            kname[d] = base(row["Kernel_Name"])
+            key = (d, row["Counter_Name"])
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+            spans[d] = (int(row["Start_Timestamp"]), int(row["End_Timestamp"]))
+    simds, xcc = 1024, 8
+    with open(agent_csv) as f:
+        for row in csv.DictReader(f):
+            if row.get("Name", "").startswith("gfx"):
+                simds, xcc = int(row["Simd_Count"]), int(row["Num_Xcc"])
+    calls = sum(1 for d in kname if kname[d] == kernel)
+    if calls == 0:
+        raise SystemExit(f"no {kernel} dispatch in {counter_csv}")
+
+    def per_call(counter):
+        return sum(v for (d, c), v in vals.items() if c == counter) / calls
+    mfma = per_call("SQ_INSTS_MFMA")
+    busy = per_call("SQ_VALU_MFMA_BUSY_CYCLES")
+    grbm = per_call("GRBM_GUI_ACTIVE")
+    ns = sum(e - s for s, e in spans.values()) / calls
+    from workloads import WORKLOADS
+    w = WORKLOADS[args.workload]
+    counter_flops = mfma * FLOP_PER_MFMA
+    algorithmic = w.flops()
+    split_kv = any(kname[d] == "attn_fwd_dense_split_kernel" for d in kname)
+    path = os.path.join(PROFILES, f"{kernel}_{args.workload}_mfma_counters.txt")
+    with open(path, "w") as f:
+        f.write(f"# Matrix-core counters of one call ({', '.join(names)} as dispatched) on the "
+                f"{args.workload} workload ({w.description})\n")
+        f.write("# from one rocprofv3 --pmc run of bench.py; durations are the same run's dispatch timestamps\n")
+        for line in (args.profile_command or "").split(";"):
+            if line.strip():
+                f.write(f"# command: {line.strip()}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash(kind)}\n")
+        f.write(f"split_kv: {'true' if split_kv else 'false'}\n")
+        f.write(f"calls: {calls}\n")
+        for name in names:
+            ds = [d for d in kname if kname[d] == name]
+            if ds:
+                m = sum(vals.get((d, "SQ_INSTS_MFMA"), 0.0) for d in ds) / calls
+                ms = sum(spans[d][1] - spans[d][0] for d in ds) / calls / 1e6
+                f.write(f"per_call {name}: SQ_INSTS_MFMA {m:.0f} duration_ms {ms:.3f}\n")
+        f.write(f"simd_count: {simds}\n")
+        f.write(f"xcc_count: {xcc}\n")
+        f.write(f"sq_insts_mfma_per_call: {mfma:.0f}\n")
+        f.write(f"sq_valu_mfma_busy_cycles_per_call: {busy:.0f}\n")
+        f.write(f"grbm_gui_active_per_call: {grbm:.0f}\n")
+        f.write(f"kernel_ms_per_call: {ns / 1e6:.4f}\n")
+        f.write(f"counter_flops_per_call: {counter_flops:.6e}\n")
+        if kind == "block_sparse":   # kept pairs only: the ratio to the dense FLOP is the density
+            f.write(f"dense_flops_per_call: {algorithmic:.6e}\n")
+            f.write(f"counter_over_dense_flops: {counter_flops / algorithmic:.4f}\n")
+        else:
+            f.write(f"algorithmic_flops_per_call: {algorithmic:.6e}\n")
+            f.write(f"counter_over_algorithmic_flops: {counter_flops / algorithmic:.4f}\n")
+        f.write(f"counter_tflops: {counter_flops / (ns * 1e-9) / 1e12:.1f}\n")
+        f.write(f"mfma_util_of_peak: {counter_flops / (ns * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f}\n")
+        f.write(f"mfma_busy_of_clocked_cycles: {(busy / simds) / (grbm / xcc):.4f}\n")
+        f.write(f"avg_shader_clock_ghz: {(grbm / xcc) / ns:.3f}\n")
+    print(open(path).read())
+    return 0
+
+
+def measured_mfma(workload: str, kernel: str, split_kv: bool, kind: str = "dense"):
+    """Matrix-core figures of one call from the committed rocprofv3 counter record, if it was
+    taken on the current kernel sources with the same split-KV setting; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_mfma_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash(kind):
+        return None
+    if fields.get("split_kv", "false") != ("true" if split_kv else "false"):
+        return None
+    keys = {"util_of_peak": "mfma_util_of_peak", "counter_tflops": "counter_tflops",
+            "counter_over_algorithmic_flops": "counter_over_algorithmic_flops",
+            "counter_over_dense_flops": "counter_over_dense_flops",
+            "busy_of_clocked_cycles": "mfma_busy_of_clocked_cycles",
+            "avg_shader_clock_ghz": "avg_shader_clock_ghz", "kernel_ms": "kernel_ms_per_call"}
+    try:
+        out = {k: float(fields[f]) for k, f in keys.items() if f in fields}
+    except ValueError:
+        return None
+    if "util_of_peak" not in out:
+        return None
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
+
+
 def time_prologue(args, w, vd, dev) -> dict:
     """Time the Q/K RMSNorm + 3-D RoPE prologue (with V re-laid) at the workload's token grid,
     on seeded projected inputs resident in HBM; check seeded tokens against the oracle."""
@@ -390,6 +508,7 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
         "flops_per_call": flops,
         "traffic": measured_traffic(w.name, "attn_fwd_block_sparse_kernel", False, "block_sparse"),
+        "mfma_counters": measured_mfma(w.name, "attn_fwd_block_sparse_kernel", False, "block_sparse"),
         "ms": {"sparse": round(avg_s, 4), "sparse_min": round(min(sparse_ms), 4),
                "sparse_max": round(max(sparse_ms), 4), "route": round(avg_r, 4)},
         "speedup_vs_dense_call": round(dense_ms / (avg_s + avg_r), 3),
@@ -571,8 +690,12 @@ def main() -> int:
     ap.add_argument("--write-traffic-profile", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
                          "WRITE_SIZE) of a run with --calibrate-copy-mib into the profiles/ record; no GPU")
+    ap.add_argument("--write-mfma-profile", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
+                    help="turn a rocprofv3 --pmc run of " + " ".join(MFMA_COUNTERS) + " (its "
+                         "counter_collection.csv and agent_info.csv) into the profiles/ record; no GPU")
     ap.add_argument("--traffic-kind", choices=sorted(CALL_KERNELS), default=None,
-                    help="with --write-traffic-profile: which call's kernels to record (default: the workload's)")
+                    help="with --write-traffic-profile / --write-mfma-profile: which call's kernels to "
+                         "record (default: the workload's)")
     ap.add_argument("--prologue-steps", type=int, default=20,
                     help="timed calls of the Q/K RMSNorm+RoPE prologue at the workload's grid (0: skip)")
     ap.add_argument("--linear-steps", type=int, default=10,
@@ -590,6 +713,8 @@ def main() -> int:
 
     if args.write_traffic_profile:
         return write_traffic_profile(args)
+    if args.write_mfma_profile:
+        return write_mfma_profile(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -694,7 +819,8 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name, kernel, split),
+            "traffic": measured_traffic(w.name, kernel, split, w.kind),
+            "mfma_counters": measured_mfma(w.name, kernel, split, w.kind),
             "kernel_ms": {"avg": round(avg_kernel_ms, 4), "median": round(float(np.median(kernel_ms)), 4),
                           "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
         },

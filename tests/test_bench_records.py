@@ -1,0 +1,73 @@
+"""bench.py's counter records (no GPU): the matrix-core record computed from a rocprofv3-style
+counter CSV, and a record taken on other kernel sources being ignored."""
+import argparse
+import csv
+
+import pytest
+
+import bench
+
+HEADER = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+          "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+          "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+NS = "(anonymous namespace)::"
+
+
+def write_csvs(tmp_path):
+    # one dense call: main kernel 190 ms, split kernel 5 ms, merge 0.02 ms; counters split over
+    # 8 rows per dispatch (as per-XCD rows would be); one unrelated kernel that must be ignored
+    calls = [(1, NS + "attn_fwd_dense_kernel(" + NS + "DenseArgs)", 0, 190_000_000, 8.0e9),
+             (2, NS + "attn_fwd_dense_split_kernel(" + NS + "DenseArgs, " + NS + "SplitArgs)",
+              190_000_000, 195_000_000, 0.2e9),
+             (3, NS + "merge_kernel(" + NS + "DenseArgs, " + NS + "SplitArgs)", 195_000_000, 195_020_000, 0.0),
+             (4, "void " + NS + "qk_prologue_kernel<4>(" + NS + "PrologueArgs)", 196_000_000, 197_000_000, 5.0e9)]
+    clock_ghz, busy = 1.6, 0.8
+    rows = []
+    for d, name, s, e, mfma in calls:
+        cycles_per_xcd = (e - s) * clock_ghz
+        for _ in range(8):
+            rows.append([d, d, "Agent 1", 1, 1, 1, 1, 1, name, 256, 0, 0, 0, 0, 0, "SQ_INSTS_MFMA", mfma / 8, s, e])
+            rows.append([d, d, "Agent 1", 1, 1, 1, 1, 1, name, 256, 0, 0, 0, 0, 0, "SQ_VALU_MFMA_BUSY_CYCLES",
+                         busy * cycles_per_xcd * 1024 / 8, s, e])
+            rows.append([d, d, "Agent 1", 1, 1, 1, 1, 1, name, 256, 0, 0, 0, 0, 0, "GRBM_GUI_ACTIVE",
+                         cycles_per_xcd, s, e])
+    c = tmp_path / "counters.csv"
+    with open(c, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(HEADER)
+        w.writerows(rows)
+    a = tmp_path / "agents.csv"
+    with open(a, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Simd_Count", "Num_Xcc"])
+        w.writerow(["gfx950", "1024", "8"])
+    return str(c), str(a)
+
+
+def test_mfma_record_from_counters(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    c, a = write_csvs(tmp_path)
+    args = argparse.Namespace(write_mfma_profile=(c, a), traffic_kind="dense", workload="video_720p",
+                              profile_command="")
+    assert bench.write_mfma_profile(args) == 0
+    got = bench.measured_mfma("video_720p", "attn_fwd_dense_kernel", True, "dense")
+    flops = 8.2e9 * 32768
+    ms = 195.02
+    assert got["kernel_ms"] == pytest.approx(ms, rel=1e-6)
+    assert got["counter_tflops"] == pytest.approx(flops / (ms * 1e-3) / 1e12, abs=0.06)
+    assert got["util_of_peak"] == pytest.approx(flops / (ms * 1e-3) / 1e12 / 2500.0, abs=1e-4)
+    assert got["counter_over_algorithmic_flops"] == pytest.approx(flops / (4.0 * 16 * 180320 ** 2 * 128), abs=1e-4)
+    assert got["busy_of_clocked_cycles"] == pytest.approx(0.8, abs=1e-4)
+    assert got["avg_shader_clock_ghz"] == pytest.approx(1.6, abs=1e-3)
+    # a record without split pieces does not describe a split call, and vice versa
+    assert bench.measured_mfma("video_720p", "attn_fwd_dense_kernel", False, "dense") is None
+
+
+def test_record_of_other_sources_is_ignored(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    c, a = write_csvs(tmp_path)
+    args = argparse.Namespace(write_mfma_profile=(c, a), traffic_kind="dense", workload="video_720p",
+                              profile_command="")
+    bench.write_mfma_profile(args)
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kind="dense": "0" * 64)
+    assert bench.measured_mfma("video_720p", "attn_fwd_dense_kernel", True, "dense") is None
