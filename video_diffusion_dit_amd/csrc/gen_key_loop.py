@@ -119,6 +119,7 @@ OPTS = {
     "kpre_after": 24,    # PV phase: the next QK phase's first K fragments read after this MFMA
     "vpre_after": 24,    # QK phase: the next PV phase's first V fragments read after this MFMA
     "limit_bits": RESCALE_LIMIT_BITS,
+    "stagger": 1,        # softmax groups: fma, exp and sum/pack of a group this many groups apart
     "headroom": 32,      # the exact path moves m to the running maximum plus this (log2 units)
 }
 
@@ -337,10 +338,11 @@ def softmax_half(buf, kb, masked, klim, hs):
         return [st1, st2, st3]
 
     staged = [group(rb, j) for j in range(8) for rb in range(2)]
-    stream = []   # stage s of group g issues at step g + s
-    for step in range(len(staged) + 2):
+    stream = []   # stage s of group g issues at step g + s * stagger
+    k = OPTS["stagger"]
+    for step in range(len(staged) + 2 * k):
         for s in range(3):
-            g = step - s
+            g = step - s * k
             if 0 <= g < len(staged):
                 stream.extend(staged[g][s])
     return stream
