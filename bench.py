@@ -679,8 +679,9 @@ def main() -> int:
     ap.add_argument("--heads", type=int, default=0,
                     help="dense workloads: run the first HEADS heads only (the same values), i.e. one "
                          "GPU's share of a head-sharded call at full N (0: all heads)")
-    ap.add_argument("--cpu-rows", type=int, default=512,
-                    help="query rows of the seeded sample the FP64 oracle is timed and checked on")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="query rows of the seeded sample the FP64 oracle is timed and checked on (2048: about 10 s of "
+                         "FP64 work on 16 host cores at 720p)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split-kv", action="store_true",
                     help="dense workloads: plain attn_fwd, without cutting the last round's tiles over keys")
