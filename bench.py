@@ -679,8 +679,8 @@ def main() -> int:
     ap.add_argument("--heads", type=int, default=0,
                     help="dense workloads: run the first HEADS heads only (the same values), i.e. one "
                          "GPU's share of a head-sharded call at full N (0: all heads)")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="query rows of the seeded sample the FP64 oracle is timed and checked on (2048: about 10 s of "
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="query rows of the seeded sample the FP64 oracle is timed and checked on (8192: 10-20 s of "
                          "FP64 work on 16 host cores at 720p)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split-kv", action="store_true",
