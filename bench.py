@@ -56,7 +56,7 @@ CALL_KERNELS = {
     "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule"),
     "prologue": ("qk_prologue_kernel",),
     "linear": ("linear_out_kernel", "linear_kv_partial_kernel", "linear_kv_reduce_kernel"),
-    "block_sparse": ("attn_fwd_block_sparse_kernel", "route_kernel", "pool_kernel"),
+    "block_sparse": ("attn_fwd_block_sparse_kernel", "route_kernel", "pool_kernel", "lpt_order_kernel"),
 }
 
 
@@ -476,8 +476,8 @@ def time_block_sparse(args, w, vd, q, k, v, qb, kb, vb, dense_ms: float) -> dict
         torch.cuda.synchronize()
         return [s.elapsed_time(e) for s, e in zip(starts, ends)], res
 
-    order_name = "item" if args.block_skip_order == "auto" else args.block_skip_order
-    lpt = order_name == "longest-first"
+    order_name = "longest-first per head" if args.block_skip_order == "auto" else args.block_skip_order
+    lpt = order_name != "item"
     route_ms, routed = timed(lambda: vd.block_route(q, k, tau=tau, scale=w.scale, with_order=lpt),
                              args.block_skip_steps)
     kv_idx, kv_cnt, order = routed if lpt else (*routed, None)
@@ -706,8 +706,9 @@ def main() -> int:
     ap.add_argument("--block-skip-tau", type=float, default=0.02,
                     help="routing threshold of the timed block-skip calls")
     ap.add_argument("--block-skip-order", choices=("auto", "longest-first", "item"), default="auto",
-                    help="dispatch order of the block-sparse pass: the routing's longest-first order, item "
-                         "order, or auto (item order on dense batches, longest-first on packed ones)")
+                    help="dispatch order of the block-sparse pass: the routing's longest-first order (per "
+                         "head on dense batches, over all items on packed ones), or item order; auto: the "
+                         "routing's order")
     ap.add_argument("--profile-command", default="",
                     help="the command lines that produced the counter files (recorded in the profile)")
     args = ap.parse_args()

@@ -197,12 +197,13 @@ size_t attn_linear_workspace_bytes(int B, int N, int H, int d);
  *   kv_cnt : int32 [B*H*ntq].
  * A list that breaks these rules is processed memory-safely (each index is clamped to
  * [previous index, ntk], the count to [0, ntk]) with an unspecified result.
- *   order  : int32 [B*H*ntq] or NULL: the order in which the items are started (the routing
- *            writes the items sorted by list length, longest first, so that the last round of
- *            the GPU holds short ones). NULL starts them in item order, which keeps the
- *            workgroups in flight within one or two heads; on the 720p grid that measured
- *            faster than longest-first. Results do not depend on it; entries outside the
- *            item range are clamped.
+ *   order  : int32 [B*H*ntq] or NULL: the order in which the items are started. The routing
+ *            writes, for each (b, h) in turn, its query tiles sorted by list length, longest
+ *            first: the last round of the GPU then holds short items, and the workgroups in
+ *            flight stay within one or two heads (on the 720p grid 7.5 % faster than item
+ *            order, which a sort over all heads was slower than). NULL starts the items in
+ *            item order. Results do not depend on it; entries outside the item range are
+ *            clamped.
  */
 
 /* Row stride of kv_idx in entries: ceil(N/64) + 8 (0 if N <= 0). */
@@ -233,9 +234,10 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out
  *   sink_tokens : >= 0; the key tiles holding keys 0 .. sink_tokens-1 are always kept.
  *   kv_idx, kv_cnt : DEVICE outputs (sizes above); entries after each count up to 8 are set
  *                 to ntk.
- *   order       : DEVICE output [B*H*ntq] (the items by list length, longest first, by a
- *                 counting sort over 4096 bins of length; items in one bin, which holds one
- *                 length while ntk <= 4095, in no fixed order), or NULL to skip it.
+ *   order       : DEVICE output [B*H*ntq]: for each (b, h) in order, its ntq items by list
+ *                 length, longest first (a counting sort over 4096 bins of length; items in
+ *                 one bin, which holds one length while ntk <= 4095, in no fixed order), or
+ *                 NULL to skip it.
  *   workspace   : DEVICE scratch of attn_block_route_workspace_bytes(B, H, N, d) bytes,
  *                 256-byte aligned (the pooled tiles); no initialisation needed.
  * Sequences of more than 15360 key tiles (N > 983040) return ATTN_ERR_UNSUPPORTED.

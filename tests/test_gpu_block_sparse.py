@@ -172,17 +172,22 @@ def test_deterministic(vd):
     assert np.array_equal(bits_of(a), bits_of(b))
 
 
-def check_order(order, cnt, n, max_cnt):
-    """order (host): its first n entries are a permutation of the n items, longest list
+def check_order(order, cnt, n, max_cnt, group=None):
+    """order (host): its first n entries are a permutation of the n items; within each run of
+    `group` entries (all n when None) the entries are that run's own items, longest list
     first. The counting sort bins counts into 4096 bins, one count per bin while
     max_cnt <= 4095; above that, neighbouring counts may share a bin and keep any order."""
     o = order[:n]
     assert np.array_equal(np.sort(o), np.arange(n))
-    c = np.clip(cnt.reshape(-1)[o].astype(np.int64), 0, max_cnt)
-    if max_cnt <= 4095:
-        assert np.all(np.diff(c) <= 0)
-    else:
-        assert np.all(np.diff((max_cnt - c) * 4095 // max_cnt) >= 0)
+    group = group or n
+    for lo in range(0, n, group):
+        run = o[lo:lo + group]
+        assert np.array_equal(np.sort(run), np.arange(lo, min(lo + group, n)))
+        c = np.clip(cnt.reshape(-1)[run].astype(np.int64), 0, max_cnt)
+        if max_cnt <= 4095:
+            assert np.all(np.diff(c) <= 0)
+        else:
+            assert np.all(np.diff((max_cnt - c) * 4095 // max_cnt) >= 0)
 
 
 @pytest.mark.parametrize("B,H,N,tau", [
@@ -191,8 +196,8 @@ def check_order(order, cnt, n, max_cnt):
     (1, 1, 1, 0.0),             # one item
 ])
 def test_dispatch_order(vd, B, H, N, tau):
-    """The longest-first order: a permutation of the items sorted by count; the lists are
-    the same with and without it, and so are the outputs, bit for bit."""
+    """The dispatch order: per (b, h), its query tiles sorted by count, longest first; the
+    lists are the same with and without it, and so are the outputs, bit for bit."""
     q, k, v = random_dense(B, H, N, seed=N + 7 * H)
     kv_idx, kv_cnt = route(vd, q, k, tau)
     idx2, cnt2, order = vd.block_route(dev(q), dev(k), tau=tau, scale=SCALE, with_order=True)
@@ -202,7 +207,7 @@ def test_dispatch_order(vd, B, H, N, tau):
     assert np.array_equal(cnt2.cpu().numpy(), kv_cnt.cpu().numpy())
     assert np.array_equal(lists_to_keep(idx2.cpu().numpy(), cnt2.cpu().numpy(), ntk),
                           lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ntk))
-    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), kv_cnt.numel(), ntk)
+    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), kv_cnt.numel(), ntk, group=-(-N // 256))
     a, la = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True)
     b, lb = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True,
                                      order=order)
@@ -235,7 +240,7 @@ def video_720p():
 
 def test_video_720p_routing_and_sampled_rows(vd, video_720p):
     """The 720p grid (B=1, H=16, N=180320) at the timed setting tau = 0.02, in the timed
-    launch (longest-first order): routing against the oracle over every (head, query tile,
+    launch (longest-first order per head): routing against the oracle over every (head, query tile,
     key tile), the order against the counts, attention on 384 seeded rows plus the last 64
     rows of head 15."""
     q, k, v = video_720p
@@ -246,7 +251,7 @@ def test_video_720p_routing_and_sampled_rows(vd, video_720p):
     ntk = -(-N // 64)
     keep_gpu = lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ntk)
     check_route(keep_gpu, q, k, tau, 0)
-    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), kv_cnt.numel(), ntk)
+    check_order(order.cpu().numpy(), kv_cnt.cpu().numpy(), kv_cnt.numel(), ntk, group=-(-N // 256))
     out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), kv_idx, kv_cnt, scale=SCALE, return_lse=True,
                                         order=order)
     torch.cuda.synchronize()

@@ -328,19 +328,27 @@ __global__ void scale_count_kernel(const int* __restrict__ count, int H, int* __
 }
 
 // ---------------------------------------------------------------- dispatch order
-// Items sorted by their list length, longest first (a bucket sort in one workgroup), so that
+// Items sorted by their list length, longest first (a bucket sort per workgroup), so that
 // the block-sparse kernel starts the long items first and the last round is made of short
-// ones. Within a bucket the order depends on the timing of LDS atomics; the attention
-// results do not depend on the order at all.
+// ones. Workgroup g sorts items [g*group, (g+1)*group) among themselves: with group = the
+// query tiles of one (b, h), the heads keep their order (the workgroups in flight then share
+// one or two heads' K/V in L2, and items of similar length walk the key range in step);
+// with group = all items, the sort is global. Within a bucket the order depends on the timing
+// of LDS atomics; the attention results do not depend on the order at all.
 constexpr int ORDER_BINS = 4096;
 
 __global__ __launch_bounds__(1024) void lpt_order_kernel(const int32_t* __restrict__ kcnt, int items,
                                                          const int* __restrict__ items_dev, int max_cnt,
-                                                         int32_t* __restrict__ order) {
+                                                         int group, int32_t* __restrict__ order) {
     __shared__ int hist[ORDER_BINS];
     __shared__ int part[1024];
     const int tid = threadIdx.x;
-    const int n = items_dev != nullptr ? min(*items_dev, items) : items;
+    const int n_all = items_dev != nullptr ? min(*items_dev, items) : items;
+    const long lo = (long)blockIdx.x * group;
+    if (lo >= n_all) return;   // uniform across the workgroup
+    const int n = (int)min((long)group, (long)n_all - lo);
+    kcnt += lo;
+    order += lo;
     const int mc = max(max_cnt, 1);
     auto bin = [&](int c) {   // descending: the longest lists in bin 0
         c = min(max(c, 0), mc);
@@ -373,16 +381,20 @@ __global__ __launch_bounds__(1024) void lpt_order_kernel(const int32_t* __restri
         acc += v;
     }
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) order[atomicAdd(&hist[bin(kcnt[i])], 1)] = i;
+    for (int i = tid; i < n; i += 1024) order[atomicAdd(&hist[bin(kcnt[i])], 1)] = (int)(lo + i);
 }
 
 }  // namespace
 
 namespace attn_impl {
 
+// group: items sorted among themselves per workgroup (0: all items in one workgroup)
 hipError_t launch_lpt_order(const int32_t* kv_cnt, int items, const int* items_dev, int max_cnt, int32_t* order,
-                            hipStream_t stream) {
-    hipLaunchKernelGGL(lpt_order_kernel, dim3(1), dim3(1024), 0, stream, kv_cnt, items, items_dev, max_cnt, order);
+                            hipStream_t stream, int group = 0) {
+    if (group <= 0 || group >= items) group = items > 0 ? items : 1;
+    const unsigned grid = (unsigned)(((long)items + group - 1) / group);
+    hipLaunchKernelGGL(lpt_order_kernel, dim3(grid > 0 ? grid : 1), dim3(1024), 0, stream, kv_cnt, items, items_dev,
+                       max_cnt, group, order);
     return hipGetLastError();
 }
 
@@ -497,7 +509,7 @@ hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N,
     }
     e = hipGetLastError();
     if (e != hipSuccess || order == nullptr) return e;
-    return launch_lpt_order(kv_cnt, (int)(bh * ntq), nullptr, ntk, order, stream);
+    return launch_lpt_order(kv_cnt, (int)(bh * ntq), nullptr, ntk, order, stream, ntq);
 }
 
 }  // namespace attn_impl
