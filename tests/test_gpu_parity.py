@@ -294,3 +294,27 @@ def test_splitkv_deterministic_and_no_split_is_plain(attn):
     assert np.array_equal(bits_of(a), bits_of(b))
     assert np.array_equal(bits_of(c), bits_of(d))
     assert not np.array_equal(bits_of(a), bits_of(d))   # cut tiles do differ in rounding
+
+
+
+@pytest.mark.parametrize("log2_scale", [-64, 60])
+def test_value_magnitude_range(attn, log2_scale):
+    # V scaled by an exact power of two, far from N(0,1): 2^-64 stays inside the range where the
+    # accumulated sum(p v) is a normal FP32 number (the probabilities after an exact-path move
+    # are 2^-32, so |v| >= 2^-94 is needed), 2^60 inside the overflow bound (accepted
+    # probabilities <= 2^24, so N * 2^24 * max|v| < 2^128). Scaling V only scales every product
+    # and sum, so the output divided back must match the unscaled call, which meets the bar
+    # against the oracle; the LSE does not depend on V.
+    from gpu_util import check, f64_of
+    qb, kb, _ = random_dense(1, 2, 1000, seed=21, std=2.0)     # peaked rows: many exact-path moves
+    _, _, vb = random_dense(1, 2, 1000, seed=22)                # V ~ N(0, 1)
+    vf = bf16_bits_to_f64(vb) * 2.0 ** log2_scale
+    vb_s = f32_to_bf16_bits(vf.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(vb_s), vf)       # the scaling is exact in BF16
+    o, lse = run_dense(attn, qb, kb, vb)
+    o_ref, lse_ref = attention_dense(qb, kb, vb, SCALE)
+    check(f64_of(o), o_ref, lse.cpu().numpy(), lse_ref, "V ~ N(0,1), peaked rows")
+    o_s, lse_s = run_dense(attn, qb, kb, vb_s)
+    back = f64_of(o_s) * 2.0 ** -log2_scale
+    assert np.linalg.norm(back - f64_of(o)) <= 1e-6 * np.linalg.norm(f64_of(o)), log2_scale
+    assert np.max(np.abs(lse_s.cpu().numpy() - lse.cpu().numpy())) <= 1e-6
