@@ -121,35 +121,138 @@ def kept_pairs(keep, N: int, bm: int = QUERY_BLOCK, bn: int = KEY_BLOCK) -> int:
     return int((keep.astype(np.int64) * rows[:, None] * keys[None, :]).sum())
 
 
-def decision_margin(q_bits, k_bits, scale: float, tau: float, bm: int = QUERY_BLOCK,
-                    bn: int = KEY_BLOCK) -> np.ndarray:
-    """[B, H, ntq, ntk]: half-width of the band around the threshold inside which an FP32
-    evaluation of the rule (block sums and the d-term dot product in FP32, any order) may
-    decide differently from the exact one.
+U32 = 2.0 ** -24          # unit roundoff of binary32, round to nearest
+F32_TINY = 2.0 ** -149    # spacing of the binary32 subnormals
 
-    With u = 2^-24, A_I and B_J the per-channel means of |q| over block I and of |k| over
-    block J: an FP32 block mean is off by at most (rows + 1) u times the mean magnitude of its
-    channel (a sum of `rows` terms, then one scaling), and a dot product of d terms by at most
-    (d + 1) u times the sum of the magnitudes of its products. So an FP32 z_IJ is off by at
-    most s u [(bm + 1) A_I.|kbar_J| + (bn + 1) |qbar_I|.B_J + (d + 3) |qbar_I|.|kbar_J|]
-    (the last term also covers the scaling by s and the cross terms). z_IJ and the block
-    maximum both carry such an error, and forming zmax - tau adds one rounding."""
+
+def _pow2_at_least(x: np.ndarray) -> np.ndarray:
+    """Smallest power of two >= x (x > 0), exactly (frexp, no logarithms)."""
+    f, e = np.frexp(x)
+    return np.ldexp(1.0, np.where(f == 0.5, e - 1, e).astype(np.int64))
+
+
+def block_mean_error(x: np.ndarray, block: int) -> np.ndarray:
+    """[ceil(N/block), d]: bound on |mean_fp32 - mean| for the per-channel mean of each row block
+    of x (float64 [N, d] holding BF16 values exactly), where mean_fp32 adds the block's m values
+    in binary32 in ANY order (any tree of round-to-nearest additions) and divides once by m.
+
+    The sum part rests on two facts of round-to-nearest arithmetic. (1) If every leaf is a
+    multiple of a power of two g and the leaves' magnitudes add up to at most 2^24 g, every
+    partial sum is a multiple of g of at most 2^24 g, hence a binary32 number, so each addition
+    is exact and the whole tree is exact. (2) Rounded addition is monotone in each operand, so
+    the tree's result is monotone in each leaf. With S the sum of |x| and g the smallest power
+    of two with S + m g <= 2^24 g, rounding every leaf that is not a multiple of g down (up) to
+    one gives a tree that is exact by (1) and, by (2), a lower (upper) bound of the computed
+    sum; the exact sum lies between the two as well. So the computed sum is off by at most g
+    times the number of leaves that are not multiples of g. For BF16 inputs of unit size that
+    number is nearly always zero: their 8 significant bits sit far above g.
+
+    The classical bound of a tree of m - 1 additions, (m - 1) u S (1 + m u), holds as well;
+    the smaller of the two is taken. The division adds one rounding, at most u times the
+    computed mean.
+    """
+    n, d = x.shape
+    nb = -(-n // block)
+    out = np.empty((nb, d))
+    for j in range(nb):
+        xb = x[j * block:(j + 1) * block]
+        m = xb.shape[0]
+        S = np.abs(xb).sum(axis=0) * (1.0 + 2.0 ** -40)      # float64 sum: inflate past its own rounding
+        g = np.maximum(_pow2_at_least(np.maximum(S, F32_TINY) / (2.0 ** 24 - m)), F32_TINY)
+        fine = (np.fmod(xb, g) != 0).sum(axis=0)
+        e_sum = np.minimum(g * fine, (m - 1) * U32 * S * (1.0 + m * U32))
+        out[j] = e_sum / m + U32 * (np.abs(xb.sum(axis=0)) + e_sum) / m
+    return out
+
+
+def _chain_bound(qb, kb, eq, ek) -> tuple:
+    """Error bound and |exact| of the dot products qbar_I . kbar_J for paired rows
+    (qb, kb, eq, ek: [P, d]), evaluated in binary32 from computed means qb + dq, kb + dk
+    (|dq| <= eq, |dk| <= ek) as a chain over the channels in index order, z_c = z_{c-1} +
+    q_c k_c, fused (one rounding per step) or not (two). Running error analysis: step c errs by
+    at most u |z_c| (+ u |q_c k_c| unfused), and |z_c| is at most the exact partial sum plus
+    the input perturbation so far, times (1 + u)^c. A step whose computed product is exactly
+    zero (both bounds zero) leaves z unchanged and is not charged."""
+    d = qb.shape[-1]
+    p = qb * kb
+    dp = eq * np.abs(kb) + np.abs(qb) * ek + eq * ek                # input perturbation per term
+    live = (np.abs(p) + dp) > 0
+    Z = np.abs(np.cumsum(p, axis=-1)) + np.cumsum(dp, axis=-1)
+    run = U32 * (1.0 + 2.0 * d * U32) * (live * (Z + np.abs(p) + dp)).sum(axis=-1)
+    return dp.sum(axis=-1) + run, np.abs(p.sum(axis=-1))
+
+
+def proxy_error(q_bits, k_bits, scale: float, pairs=None, bm: int = QUERY_BLOCK, bn: int = KEY_BLOCK):
+    """Bound on |z_fp32 - z| for the proxies of dense [B, H, N, d] BF16 inputs, where z_fp32 is
+    a binary32 evaluation of the rule: the block means as block_mean_error allows (any order,
+    one division), the dot product as a chain over the channels in index order (fused or not,
+    _chain_bound), then one multiplication by the FP32 scale (one more rounding).
+
+    pairs=None: [B, H, ntq, ntk] for every pair. pairs = (b, h, I, J) index arrays: the bound of
+    those pairs only, in that order (cheap at any N)."""
     B, H, N, d = q_bits.shape
     s = abs(scale_as_used(scale))
-    u = 2.0 ** -24
+    ntq, ntk = -(-N // bm), -(-N // bn)
+    slack = 2.0 ** -40                       # the float64 reference's own rounding
+    if pairs is None:
+        grid = np.meshgrid(np.arange(B), np.arange(H), np.arange(ntq), np.arange(ntk), indexing="ij")
+        return proxy_error(q_bits, k_bits, scale, tuple(g.ravel() for g in grid), bm, bn).reshape(B, H, ntq, ntk)
+    b_, h_, I_, J_ = (np.asarray(a, np.int64) for a in pairs)
+    out = np.empty(b_.size)
+    for bh in np.unique(b_ * H + h_):
+        b, h = divmod(int(bh), H)
+        sel = np.nonzero(b_ * H + h_ == bh)[0]
+        q = bf16_bits_to_f64(q_bits[b, h])
+        k = bf16_bits_to_f64(k_bits[b, h])
+        qb, kb = pooled_means(q, bm), pooled_means(k, bn)
+        eq, ek = block_mean_error(q, bm), block_mean_error(k, bn)
+        for lo in range(0, sel.size, 4096):
+            cut = sel[lo:lo + 4096]
+            I, J = I_[cut], J_[cut]
+            e_dot, zabs = _chain_bound(qb[I], kb[J], eq[I], ek[J])
+            mag = (np.abs(qb[I]) * np.abs(kb[J])).sum(axis=-1)
+            out[cut] = s * e_dot + U32 * s * (zabs + e_dot) + slack * s * mag
+    return out
+
+
+def decision_margin(q_bits, k_bits, scale: float, tau: float, mask=None, bm: int = QUERY_BLOCK,
+                    bn: int = KEY_BLOCK) -> np.ndarray:
+    """[B, H, ntq, ntk]: half-width of the band around the threshold inside which a binary32
+    evaluation of the rule (proxy_error) may keep or drop a tile differently from the exact
+    one: J may go either way only if |z_IJ - (zmax_I - tau)| <= margin_IJ.
+
+    margin_IJ = e_IJ + E_I + u (|zmax_I| + E_I + tau), with e the proxy bound of the pair and
+    E_I the bound of the computed row maximum: the computed max is the computed z of some tile
+    J', which can exceed zmax only by e_IJ' for a tile with z_IJ' + e_IJ' >= zmax, and is at
+    least z_IJ* - e_IJ* for the exact argmax J*. The candidates J' are found with the cheap
+    order-free bound s (d + 2) u sum_c |qbar||kbar| plus the input perturbation, which is at
+    least e. The subtraction of tau adds one rounding.
+
+    mask=None: every entry. mask = bool [B, H, ntq, ntk]: the band at the marked entries only
+    (NaN elsewhere), for large inputs where only a few entries need it."""
+    B, H, N, d = q_bits.shape
+    s = abs(scale_as_used(scale))
     t = 0.0 if math.isinf(tau) else abs(float(tau))
     ntq, ntk = -(-N // bm), -(-N // bn)
-    out = np.empty((B, H, ntq, ntk))
-    for b in range(B):
-        for h in range(H):
-            q = bf16_bits_to_f64(q_bits[b, h])
-            k = bf16_bits_to_f64(k_bits[b, h])
-            A, Bk = pooled_means(np.abs(q), bm), pooled_means(np.abs(k), bn)
-            qb, kb = pooled_means(q, bm), pooled_means(k, bn)
-            e = s * u * ((bm + 1) * (A @ np.abs(kb).T) + (bn + 1) * (np.abs(qb) @ Bk.T)
-                         + (d + 3) * (np.abs(qb) @ np.abs(kb).T))
-            zmax = (scale_as_used(scale) * (qb @ kb.T)).max(axis=1)
-            out[b, h] = e + e.max(axis=1, keepdims=True) + 2 * u * (np.abs(zmax)[:, None] + t)
+    mask = np.ones((B, H, ntq, ntk), bool) if mask is None else np.asarray(mask, bool)
+    out = np.full((B, H, ntq, ntk), np.nan)
+    for b, h in sorted({(int(b), int(h)) for b, h in zip(*np.nonzero(mask.any(axis=(2, 3))))}):
+        q = bf16_bits_to_f64(q_bits[b, h])
+        k = bf16_bits_to_f64(k_bits[b, h])
+        qb, kb = pooled_means(q, bm), pooled_means(k, bn)
+        eq, ek = block_mean_error(q, bm), block_mean_error(k, bn)
+        z = scale_as_used(scale) * (qb @ kb.T)
+        zmax = z.max(axis=1)
+        for I in np.nonzero(mask[b, h].any(axis=1))[0]:
+            crude = s * ((d + 2) * U32 * 1.01 * ((np.abs(qb[I]) + eq[I]) @ (np.abs(kb) + ek).T)
+                         + eq[I] @ np.abs(kb).T + np.abs(qb[I]) @ ek.T + eq[I] @ ek.T)
+            cand = np.nonzero(z[I] >= zmax[I] - crude)[0]
+            want = np.nonzero(mask[b, h, I])[0]
+            Js = np.concatenate([cand, want])
+            e = proxy_error(q_bits, k_bits, scale, (np.full(Js.size, b), np.full(Js.size, h),
+                                                    np.full(Js.size, I), Js), bm, bn)
+            E = e[:cand.size].max()
+            out[b, h, I, want] = e[cand.size:] + E + U32 * (abs(zmax[I]) + E + t)
     return out
 
 

@@ -2,8 +2,9 @@
 FP64 oracle of oracle/block_sparse.py.
 
 Routing: the kept tiles must equal the oracle's except where the oracle's z lies within the
-FP32 decision band around the threshold (oracle.block_sparse.decision_margin), and the lists
-must be well formed (ascending, counted, padded). Attention: the oracle's exact softmax over
+FP32 decision band around the threshold (oracle.block_sparse.decision_margin, pinned against
+binary32 replays of the rule in tests/test_oracle_margin.py), such tiles must stay rare, and
+the lists must be well formed (ascending, counted, padded). Attention: the oracle's exact softmax over
 the tiles the GPU kept, with the dense bar (rel-L2 <= 5e-3, max-abs <= 2e-2, |dLSE| <= 1e-3).
 With every tile listed the output must equal the dense kernel's bit for bit.
 """
@@ -48,12 +49,19 @@ def lists_to_keep(kv_idx, kv_cnt, ntk):
     return keep
 
 
+def in_band_budget(n_tiles):
+    """Disagreements allowed inside the FP32 band: the band is about 1e-7 wide against a proxy
+    spread near 1e-2, so on these inputs a tile lands in it about once per 10^4-10^5 tiles."""
+    return 2 + n_tiles // 10000
+
+
 def check_route(keep_gpu, q, k, tau, sink):
     keep, z, zmax = route_blocks(q, k, SCALE, tau, sink_tokens=sink)
     diff = keep_gpu != keep
     if diff.any():
-        band = np.abs(z - (zmax[..., None] - tau)) <= decision_margin(q, k, SCALE, tau)
+        band = np.abs(z - (zmax[..., None] - tau)) <= decision_margin(q, k, SCALE, tau, mask=diff)
         assert not (diff & ~band).any(), f"{int((diff & ~band).sum())} tiles routed differently outside the band"
+    assert int(diff.sum()) <= in_band_budget(diff.size), int(diff.sum())
     print(f"[route] tau={tau} sink={sink}: density {keep_gpu.mean():.4f}, "
           f"{int(diff.sum())} tiles inside the FP32 band differ", flush=True)
     return keep
@@ -293,7 +301,7 @@ def varlen_keeps(vd, kv_idx, kv_cnt, cu, H):
 
 def check_route_varlen(keeps, q, k, cu, tau, sink):
     ref = route_blocks_varlen(q, k, cu, SCALE, tau, sink)
-    n_diff = 0
+    n_diff = n_tiles = 0
     for s, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
         if ref[s] is None:
             assert keeps[s] is None
@@ -303,9 +311,11 @@ def check_route_varlen(keeps, q, k, cu, tau, sink):
         if diff.any():
             qs = np.ascontiguousarray(q[a:e].transpose(1, 0, 2))[None]
             ks = np.ascontiguousarray(k[a:e].transpose(1, 0, 2))[None]
-            band = np.abs(z - (zmax[..., None] - tau)) <= decision_margin(qs, ks, SCALE, tau)[0]
+            band = np.abs(z - (zmax[..., None] - tau)) <= decision_margin(qs, ks, SCALE, tau, mask=diff[None])[0]
             assert not (diff & ~band).any()
             n_diff += int(diff.sum())
+        n_tiles += diff.size
+    assert n_diff <= in_band_budget(n_tiles), n_diff
     print(f"[route varlen] tau={tau} sink={sink}: {n_diff} tiles inside the FP32 band differ", flush=True)
 
 
