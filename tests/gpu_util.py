@@ -38,3 +38,53 @@ def device_normal_bf16(shape, seed: int) -> torch.Tensor:
     g = torch.Generator(device="cuda:0").manual_seed(seed)
     x = torch.randn(shape, generator=g, device="cuda:0", dtype=torch.float32)
     return x.to(torch.bfloat16)
+
+
+# ---- the split-KV plan of attn_fwd_splitkv, restated for choosing rows to check
+
+def split_plan(B, H, N, slots, min_tiles=16):
+    """(D, R, G, ntk) of the library's split plan (rows of 256 queries, 64-key tiles)."""
+    ntq, ntk = -(-N // 256), -(-N // 64)
+    items = B * H * ntq
+    full, r = divmod(items, slots)
+    if slots < 2 or r == 0 or ntk < min_tiles:
+        return items, 0, 0, ntk
+    if full >= 1:
+        R, G = slots + r, slots
+    else:
+        R, G = items, min(slots, items * ntk // min_tiles)
+        if G <= R:
+            return items, 0, 0, ntk
+    return items - R, R, G, ntk
+
+
+def cut_tiles(B, H, N, slots):
+    """Query tiles (flat index b*H*ntq + h*ntq + qt) whose key range the plan splits."""
+    D, R, G, ntk = split_plan(B, H, N, slots)
+    cut = set()
+    for i in range(R):
+        first, last = i * ntk, (i + 1) * ntk - 1
+        g0 = max(g for g in range(G) if g * R * ntk // G <= first)
+        g1 = max(g for g in range(G) if g * R * ntk // G <= last)
+        if g0 != g1:
+            cut.add(D + i)
+    return cut
+
+
+def cut_tile_rows(B, H, N, slots, per_tile=2, seed=0):
+    """Flat rows ((b*H + h)*N + n) to check in the tiles the plan cuts: each cut tile's first and
+    last valid row plus `per_tile` seeded rows inside it."""
+    rng = np.random.default_rng(seed)
+    ntq = -(-N // 256)
+    rows = []
+    for t in sorted(cut_tiles(B, H, N, slots)):
+        bh, qt = divmod(t, ntq)
+        lo, hi = qt * 256, min(N, (qt + 1) * 256)
+        pick = {lo, hi - 1, *rng.integers(lo, hi, per_tile).tolist()}
+        rows += [bh * N + n for n in pick]
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def device_slots() -> int:
+    """Workgroups of the attention kernel that run at once on cuda:0: one per compute unit."""
+    return torch.cuda.get_device_properties(0).multi_processor_count

@@ -14,6 +14,8 @@ import pytest
 from oracle import attention_dense, attention_varlen, bf16_bits_to_f64
 from workloads import WORKLOADS, f32_to_bf16_bits, make_dense, random_dense, random_varlen
 
+from gpu_util import cut_tiles, split_plan
+
 pytestmark = pytest.mark.gpu
 
 SCALE = 1 / math.sqrt(128)
@@ -217,35 +219,6 @@ def test_varlen_empty_batch_is_noop(attn):
 
 
 # ---- split-KV (attn_fwd_splitkv): the last, partly filled round of query tiles is cut over keys
-
-def split_plan(B, H, N, slots, min_tiles=16):
-    """(D, R, G, ntk) of the library's split plan (rows of 256 queries, 64-key tiles)."""
-    ntq, ntk = -(-N // 256), -(-N // 64)
-    items = B * H * ntq
-    full, r = divmod(items, slots)
-    if slots < 2 or r == 0 or ntk < min_tiles:
-        return items, 0, 0, ntk
-    if full >= 1:
-        R, G = slots + r, slots
-    else:
-        R, G = items, min(slots, items * ntk // min_tiles)
-        if G <= R:
-            return items, 0, 0, ntk
-    return items - R, R, G, ntk
-
-
-def cut_tiles(B, H, N, slots):
-    """Query tiles (flat index b*H*ntq + h*ntq + qt) whose key range the plan splits."""
-    D, R, G, ntk = split_plan(B, H, N, slots)
-    cut = set()
-    for i in range(R):
-        first, last = i * ntk, (i + 1) * ntk - 1
-        g0 = max(g for g in range(G) if g * R * ntk // G <= first)
-        g1 = max(g for g in range(G) if g * R * ntk // G <= last)
-        if g0 != g1:
-            cut.add(D + i)
-    return cut
-
 
 @pytest.mark.parametrize("B,H,N,slots", [
     (1, 3, 4133, 7),      # 51 tiles: 42 whole, the last 9 cut over 7 workgroups; ragged last key tile

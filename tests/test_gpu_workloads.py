@@ -38,9 +38,12 @@ def varlen_rows_with_tails(w, rows, cu, T):
     return np.unique(np.concatenate([rows, np.array(extra, dtype=np.int64)]))
 
 
-def run_dense_check(attn, w, label, split_kv=True):
+def run_dense_check(attn, w, label, split_kv=True, cut_rows=False):
+    """The bench's launch (split-KV on the device's compute units by default) on the workload's
+    full tensors, checked on its seeded row sample plus the ragged tails; with cut_rows, also
+    the first and last row and two seeded rows of every query tile the split plan cuts."""
     import torch
-    from gpu_util import check, dev, f64_of
+    from gpu_util import check, cut_tile_rows, dev, device_slots, f64_of, split_plan
     print(f"[case] {label}: generating {w.description}", flush=True)
     qb, kb, vb = make_dense(w)
     q, k, v = dev(qb), dev(kb), dev(vb)
@@ -48,6 +51,14 @@ def run_dense_check(attn, w, label, split_kv=True):
     o, lse = attn.attn_fwd(q, k, v, scale=w.scale, return_lse=True, split_kv=split_kv)
     torch.cuda.synchronize()
     rows = dense_rows_with_tails(w, sample_rows(w))
+    if cut_rows:
+        slots = device_slots()
+        D, R, G, _ = split_plan(w.B, w.H, w.N, slots)
+        extra = cut_tile_rows(w.B, w.H, w.N, slots, seed=w.index)
+        assert extra.size > 0, "the plan cuts no tile at this size"
+        print(f"[case] {label}: {slots} slots, {R} tiles over {G} split workgroups, "
+              f"{extra.size} rows in cut tiles", flush=True)
+        rows = np.unique(np.concatenate([rows, extra]))
     o_ref, lse_ref = attention_dense(qb, kb, vb, w.scale, rows=rows)
     og = f64_of(o).reshape(-1, w.d)[rows]
     lg = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
@@ -107,4 +118,15 @@ def test_numerics_stress_dense_and_ragged(attn):
 
 
 def test_video_720p_sampled(attn):
-    run_dense_check(attn, WORKLOADS["video_720p"], "video_720p")
+    run_dense_check(attn, WORKLOADS["video_720p"], "video_720p", cut_rows=True)
+
+
+def test_video_720p_one_gpu_share(attn):
+    """One GPU's share of an 8-way head split of the 720p call: B=1, H=2, N=180320 (the first
+    two heads, same values). 1410 query tiles are 5.5 rounds of 256 workgroups, so the split
+    plan cuts its last 386 tiles; every cut tile is checked."""
+    import dataclasses
+    w = WORKLOADS["video_720p"]
+    share = dataclasses.replace(w, name="video_720p_h2", H=2,
+                                description=w.description.replace("H=16", "H=2"))
+    run_dense_check(attn, share, "video_720p H=2 share", cut_rows=True)
