@@ -20,7 +20,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library keeps no
  *     reference after the call returns and allocates nothing (scratch comes from the
- *     caller's workspace argument).
+ *     caller's workspace argument; attn_fwd_varlen_noalloc alone uses a fixed array of the
+ *     library instead).
  *   - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *     Only launch failures are reported (ATTN_ERR_HIP).
  *   - All argument validation happens on the host before any HIP call; on an error
@@ -121,6 +122,32 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
 
 /* Workspace bytes attn_fwd_varlen needs for these sizes (0 if the sizes are invalid). */
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens);
+
+/* Bytes of the fixed device scratch array behind attn_fwd_varlen_noalloc (per device). */
+#define ATTN_NOALLOC_SCRATCH_BYTES 524288
+
+/*
+ * attn_fwd_varlen for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same result bits, but the tile schedule lives in a fixed library array of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes per device instead of a caller workspace. No allocation
+ * happens in this call (no hipMalloc/hipFree, no allocating library routine).
+ *   Arguments: as attn_fwd_varlen, without workspace/workspace_bytes. The device is the calling
+ *   thread's current device, which must own `stream` and the tensors.
+ *   Limit: attn_fwd_varlen_workspace_bytes(nseg, H, total_tokens) must not exceed
+ *   ATTN_NOALLOC_SCRATCH_BYTES -- every nseg <= 16384 fits at any valid total_tokens --
+ *   else ATTN_ERR_UNSUPPORTED (use attn_fwd_varlen with a workspace).
+ *   Sharing: every call on one device uses that device's one array, and the array keeps what
+ *   the last call wrote (nothing in it needs clearing: each call rebuilds the schedule before
+ *   reading it). Calls that may overlap on one device (different streams or threads) race on
+ *   it and must be serialised by the caller.
+ *   The first call on a device looks up the array's device address (hipGetSymbolAddress);
+ *   a failure there returns ATTN_ERR_HIP.
+ * Returns an attn_status_t.
+ */
+int attn_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d,
+                            float scale, void* stream);
 
 /*
  * Attention prologue: per-head RMSNorm and interleaved 3-D rotary embedding (RoPE) of the

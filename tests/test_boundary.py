@@ -31,6 +31,7 @@ def lib():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.attn_fwd_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
     lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attn_fwd_varlen_workspace_bytes.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -68,7 +69,7 @@ def test_header_declares_the_expected_api():
                  "attn_block_route", "attn_block_route_workspace_bytes", "attn_fwd_block_sparse",
                  "attn_block_skip_use_dense", "attn_block_varlen_tiles", "attn_block_route_varlen",
                  "attn_block_route_varlen_workspace_bytes", "attn_fwd_block_sparse_varlen",
-                 "attn_fwd_block_sparse_varlen_workspace_bytes",
+                 "attn_fwd_block_sparse_varlen_workspace_bytes", "attn_fwd_varlen_noalloc",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -120,6 +121,33 @@ def varlen(lib, cu=CU, nseg=3, H=2, T=300, d=128, scale=0.088, ws=WS, wsb=None, 
 ])
 def test_varlen_validation(lib, kw, code):
     assert varlen(lib, **kw) == code
+
+
+def varlen_noalloc(lib, cu=CU, nseg=3, H=2, T=300, d=128, scale=0.088, lse=None, o=O):
+    return lib.attn_fwd_varlen_noalloc(Q, K, V, o, lse, cu, nseg, H, T, d, scale, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nseg=0), INVALID), (dict(T=-1), INVALID), (dict(cu=None), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(H=0), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(o=V), INVALID), (dict(lse=O + 64), INVALID),
+    (dict(T=0), OK),                                                       # empty batch: no-op, no launch
+    (dict(T=4194304, H=2), UNSUPPORTED),                                   # T * H * 256 = 2^31 bytes
+    (dict(nseg=60000, T=60000), UNSUPPORTED),                              # schedule beyond the fixed scratch
+])
+def test_varlen_noalloc_validation(lib, kw, code):
+    assert varlen_noalloc(lib, **kw) == code
+    if code == UNSUPPORTED and kw.get("nseg") == 60000:
+        assert "scratch" in lib.attn_last_error().decode()
+
+
+def test_noalloc_scratch_covers_every_nseg_up_to_16384(lib):
+    # the header's promise: the schedule of nseg <= 16384 segments fits the fixed scratch at
+    # any total_tokens the kernels accept (T * H <= 8388607, so T <= 8388607)
+    text = open(HEADER).read()
+    limit = int(text.split("#define ATTN_NOALLOC_SCRATCH_BYTES")[1].split()[0])
+    assert lib.attn_fwd_varlen_workspace_bytes(16384, 1, 8388607) <= limit
+    assert lib.attn_fwd_varlen_workspace_bytes(60000, 1, 60000) > limit
 
 
 def test_workspace_query(lib):

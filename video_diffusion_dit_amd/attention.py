@@ -61,6 +61,8 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i32
         lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
         lib.attn_fwd_varlen.restype = i32
+        lib.attn_fwd_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        lib.attn_fwd_varlen_noalloc.restype = i32
         lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
         lib.attn_fwd_varlen_workspace_bytes.restype = sz
         lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -293,6 +295,33 @@ def _launch_varlen(q, k, v, cu_seqlens, out, lse, scale: float, cu_seqlens_host=
         st = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
                                  nseg, H, T, d, scale, _ptr(ws), ws.numel(), _stream_handle(q.device))
     _raise_for(lib, st)
+
+
+def attn_fwd_varlen_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                            out: torch.Tensor, lse: torch.Tensor | None = None, scale: float | None = None):
+    """attn_fwd_varlen into caller-given out (and lse), with the tile schedule in the library's
+    fixed per-device scratch instead of a workspace: nothing is allocated, so the call can sit
+    in code that must not allocate. Arguments are checked as attn_fwd_varlen checks them,
+    except the segment offsets, which are not copied to the host here (that would synchronise):
+    the caller guarantees cu_seqlens[0] = 0, non-decreasing, cu_seqlens[-1] = T. Calls that may
+    overlap on one device share the scratch and must be serialised by the caller."""
+    _check_tensors(q, k, v, 3)
+    T, H, d = q.shape
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dtype == torch.int32
+            and cu_seqlens.device == q.device and cu_seqlens.dim() == 1 and cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on q's device")
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    if lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [H, T] tensor on q's device")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                                         cu_seqlens.numel() - 1, H, T, d, _default_scale(d, scale),
+                                         _stream_handle(q.device))
+    _raise_for(lib, st)
+    return out
 
 
 def qk_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor | None = None, *, grid,

@@ -445,10 +445,15 @@ size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens) {
     return attn_impl::varlen_workspace_bytes(nseg, total_tokens);
 }
 
-int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
-                    const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d, float scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-    g_last_error[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// Validation shared by attn_fwd_varlen and attn_fwd_varlen_noalloc, everything but the
+// workspace. Returns ATTN_OK with `empty` set for the T = 0 no-op, else the tensor size.
+int check_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens,
+                 int nseg, int H, int total_tokens, int d, float scale, bool& empty, long long& elems) {
+    empty = false;
     if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
     if (nseg <= 0) return fail(ATTN_ERR_INVALID_ARG, "nseg must be >= 1");
     if (total_tokens == 0) {
@@ -457,30 +462,63 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
         if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
         if (d != 128) return fail(d <= 0 ? ATTN_ERR_INVALID_ARG : ATTN_ERR_UNSUPPORTED,
                                   "only head dimension 128 is supported");
+        empty = true;
         return ATTN_OK;
     }
     int st = check_common(q, k, v, out, H, d, scale);
     if (st != ATTN_OK) return st;
     if (cu_seqlens == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens must be a non-null device pointer");
-    const long long elems = product(total_tokens, H, d, 1);
+    elems = product(total_tokens, H, d, 1);
     if (elems < 0) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
     st = check_kv_span(total_tokens, 2LL * H * d);
     if (st != ATTN_OK) return st;
     const long long grid = product((long long)total_tokens / attn_impl::tile_rows() + nseg, H, 1, 1);
     if (grid < 0 || grid > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "too many query tiles for one launch");
+    return check_aliasing(q, k, v, out, lse, (size_t)elems * 2, (size_t)product(H, total_tokens, 1, 1) * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    bool empty;
+    long long elems = 0;
+    int st = check_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens, d, scale, empty, elems);
+    if (st != ATTN_OK || empty) return st;
     const size_t need = attn_impl::varlen_workspace_bytes(nseg, total_tokens);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_fwd_varlen_workspace_bytes()");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
         return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    st = check_aliasing(q, k, v, out, lse, (size_t)elems * 2, (size_t)product(H, total_tokens, 1, 1) * 4);
-    if (st != ATTN_OK) return st;
     if (overlaps(workspace, need, out, (size_t)elems * 2) || overlaps(workspace, need, q, (size_t)elems * 2) ||
         overlaps(workspace, need, k, (size_t)elems * 2) || overlaps(workspace, need, v, (size_t)elems * 2) ||
         overlaps(workspace, need, cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)))
         return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor argument");
     return hip_status(attn_impl::launch_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens,
                                                scale, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d, float scale,
+                            void* stream) {
+    g_last_error[0] = '\0';
+    bool empty;
+    long long elems = 0;
+    int st = check_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens, d, scale, empty, elems);
+    if (st != ATTN_OK || empty) return st;
+    if (attn_impl::varlen_workspace_bytes(nseg, total_tokens) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "the tile schedule exceeds the library's fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES); "
+                    "use attn_fwd_varlen with a workspace");
+    void* scratch = nullptr;
+    st = hip_status(attn_impl::noalloc_scratch(&scratch));
+    if (st != ATTN_OK) return st;
+    return hip_status(attn_impl::launch_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens,
+                                               scale, scratch, static_cast<hipStream_t>(stream)));
 }
 
 const char* attn_status_string(int status) {

@@ -56,7 +56,15 @@
 
 #include <algorithm>
 
+#include <mutex>
+
+#include "attn.h"
 #include "attn_launch.h"
+
+// Fixed scratch of attn_fwd_varlen_noalloc (the varlen tile schedule), for callers that cannot
+// allocate. Each device holds its own copy; host code never passes this name to a kernel, only
+// the device address noalloc_scratch() looks up.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -668,6 +676,25 @@ hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* 
     const long grid = max_entries(nseg, total_tokens) * H;
     hipLaunchKernelGGL(attn_fwd_block_sparse_varlen_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
     return hipGetLastError();
+}
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex lock;
+    static void* addr[MAX_DEVICES] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(lock);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_varlen(const void* q, const void* k, const void* v, void* out, float* lse,

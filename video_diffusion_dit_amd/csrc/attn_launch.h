@@ -67,6 +67,10 @@ hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* 
 // Workspace layout of the varlen schedule (bytes).
 size_t varlen_workspace_bytes(int nseg, int total_tokens);
 
+// Device address of the library's fixed scratch array (ATTN_NOALLOC_SCRATCH_BYTES bytes,
+// 256-byte aligned) on the calling thread's current device, looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 // Packed THD [T,H,128] BF16 forward over segments cu_seqlens[0..nseg]; lse [H,T] may be null.
 hipError_t launch_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                          const int32_t* cu_seqlens, int nseg, int H, int total_tokens, float scale,
