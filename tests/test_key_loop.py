@@ -258,3 +258,67 @@ def test_tile_list_variant_differs_only_in_tile_movement():
     assert [l for l in a if l.startswith("v_mfma")] == [l for l in b if l.startswith("v_mfma")]
     labels = lambda xs: [l for l in xs if l.endswith(":") or l.startswith(("s_branch", "s_cbranch", "s_barrier"))]
     assert labels(a) == labels(b)
+
+
+# ---- the fast exact path (rebase): new reference from the packed BF16 probabilities
+
+def bf16_value(bits):
+    import numpy as np
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_rebase_arithmetic_is_an_exact_power_of_two_shift(gen):
+    """The rebase path's integer steps, emulated exactly: k = max(e + 1 + headroom, 0) from the
+    u16 maximum of the BF16 patterns, then each BF16 p becomes max(p, k<<7) - (k<<7) (u16).
+    For every finite non-negative BF16 value and every k the kernel can form, that is exactly
+    p * 2^-k when the result is a normal number, and below 2^-126 otherwise (weights under
+    2^-126 of the new reference); the largest probability ends in [2^-(h+1), 2^-h)."""
+    import numpy as np
+    p = np.arange(0, 0x7F80, dtype=np.uint32)              # every finite non-negative BF16 pattern
+    exact = bf16_value(p)
+    for k in range(0, 127 + 1 + gen.OPTS["headroom"] + 1):
+        kk = k << 7
+        got = bf16_value(np.maximum(p, kk) - kk)
+        want = exact * 2.0 ** -k
+        normal = want >= 2.0 ** -126
+        assert np.array_equal(got[normal], want[normal]), k
+        assert np.all(got[~normal] < 2.0 ** -126) and np.all(got >= 0), k
+    h = gen.OPTS["headroom"]
+    bias = 126 - h
+    for mx in range(0, 0x7F80):
+        k = max((mx >> 7) - bias, 0)
+        top = bf16_value(mx) * 2.0 ** -k
+        if k > 0:
+            assert 2.0 ** -(h + 1) <= top < 2.0 ** -h, mx
+        else:   # the row already sits below 2^-h: its reference stays
+            assert top < 2.0 ** -h, mx
+
+
+def test_rebase_path_leaves_the_state_alone_until_it_commits(gen, asm_lines):
+    """Each rebase path reads the packed probabilities and may still hand the tile to the full
+    path (an inf/NaN maximum): up to that branch it writes only its temporaries, never m, l,
+    the tile sums, P or O, so the full path starts from the state the check saw."""
+    owned = {("v", r) for r in range(gen.TMP0, gen.TMP0 + 24)}
+    for X in range(2):
+        start = asm_lines.index(".Lrare%d_%%=:" % X)
+        branch = next(i for i in range(start, len(asm_lines))
+                      if asm_lines[i].startswith("s_cbranch_scc1 .Lfull%d_" % X))
+        assert asm_lines[branch + 1:].index(".Lfull%d_%%=:" % X) > 0
+        for line in asm_lines[start + 1:branch]:
+            op, ops = parse(line)
+            if op.startswith("s_") or not ops:
+                continue
+            dst = regs(ops[0])
+            assert dst <= owned or op.startswith("v_cmp"), line
+        # after the branch the path moves m, l, the tile sums, every packed P register and O
+        tail = asm_lines[branch:asm_lines.index(".Lfull%d_%%=:" % X)]
+        written = set()
+        for line in tail:
+            op, ops = parse(line)
+            if ops and not op.startswith("s_"):
+                written |= regs(ops[0])
+        for rb in range(2):
+            assert ("v", gen.M[rb]) in written and ("v", gen.L[rb]) in written and ("v", gen.TS[rb]) in written
+            assert {("v", r) for r in gen.packed_p(X, rb)} <= written
+        assert {("a", i) for i in range(128)} <= written
+        assert tail[-1] == "s_setpc_b64 s[54:55]"

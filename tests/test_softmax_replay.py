@@ -1,0 +1,173 @@
+"""CPU replay of the key loop's softmax bookkeeping, against the FP64 oracle.
+
+The kernel keeps, per query row, a reference m (log2 units of the scaled logit) and takes the
+probabilities of each 64-key tile as p = exp2(x - m) in FP32, rounded to BF16 for the PV
+product, with the normaliser l summing the FP32 p. It keeps m until some lane's tile sum
+exceeds 2^24; then
+  * rebase (fast exact path): if every BF16 p of the wave is finite, the row's largest BF16 p
+    has binary exponent e and m moves up by k = max(e + 1 + 32, 0); P (BF16, exponent field
+    minus k, flushed below 2^-126), the tile sums, l and O scale by 2^-k exactly;
+  * full exact path: otherwise (the first tile, where m = -inf, or a p beyond the FP32
+    range), m = max(row max + 32, m), O and l scale by exp2(m_old - m), and P and the tile
+    sums are recomputed.
+Both keep the softmax exact in exact arithmetic; the replay shows they do in FP32/BF16 too,
+on the outlier workload whose rows climb hundreds of log2 units (the rebase shifts reach
+k = 161 there), to the same bar as the GPU (rel-L2 <= 5e-3, max-abs <= 2e-2, |dLSE| <= 1e-3).
+
+It also pins two facts the code relies on:
+  * scaling by a multiplication with the FP32 number 2^-k instead (k above 149 makes it 0)
+    loses the tile's own sum and fails the bar -- the mistake the ldexp scaling avoids;
+  * the value range stated in include/attn.h: accepted probabilities stay at or below 2^24,
+    so before normalisation |O| <= N * 2^24 * max|v|; a replay of the worst climb (every key
+    just below the point where a lane's tile sum reaches 2^24) stays under that bound.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention_dense, bf16_bits_to_f64, compare
+from workloads import WORKLOADS, make_dense
+
+f32 = np.float32
+LIMIT = f32(2.0 ** 24)
+HEADROOM = 32
+
+
+def bf16(x):
+    """Round FP32 values to BF16 (nearest even), returned as float64 values."""
+    b = np.asarray(x, f32).view(np.uint32).astype(np.uint64)
+    rounded = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    out = rounded.astype(np.uint32).view(f32).astype(np.float64)
+    return np.where(np.isnan(np.asarray(x, f32)), np.nan, out)
+
+
+def lane_of_key():
+    """Lane half (0 or 1) holding each of a tile's 64 keys: 8 consecutive keys per lane within
+    every 16-key group (the MFMA accumulator layout the kernel reads its scores in)."""
+    return (np.arange(64) % 16) // 8
+
+
+def replay(x, v, n, scale_mode="ldexp"):
+    """Rows of one wave: x [R, N] FP32 scores in log2 units (scale*log2(e)*q.k), v [N, d] float64.
+    Returns o [R, d], lse [R] (natural log), and the counts of rebase and full moves."""
+    R, N = x.shape
+    ntk = -(-N // 64)
+    lane = lane_of_key()
+    m = np.full(R, -np.inf, f32)
+    l = np.zeros((R, 2), f32)
+    O = np.zeros((R, v.shape[1]))
+    moves = {"rebase": 0, "full": 0}
+    for t in range(ntk):
+        xs = np.full((R, 64), -np.inf, f32)
+        w = min(64, n - 64 * t)
+        xs[:, :w] = x[:, 64 * t:64 * t + w]
+        valid = np.arange(64) < w
+
+        def probs(mref):
+            with np.errstate(over="ignore", invalid="ignore"):
+                p = np.exp2((xs - mref[:, None]).astype(f32)).astype(f32)
+            return np.where(valid[None, :], p, f32(0))
+
+        def sums(p):
+            return np.stack([p[:, lane == g].sum(axis=1, dtype=f32) for g in (0, 1)], axis=1)
+
+        p = probs(m)
+        ts = sums(p)
+        pb = bf16(p)
+        if not np.all(ts <= LIMIT):                       # the wave leaves the common path
+            if np.all(np.isfinite(pb)):
+                moves["rebase"] += 1
+                e = np.frexp(np.maximum(pb.max(axis=1), 0.0))[1] - 1        # binary exponent
+                k = np.where(pb.max(axis=1) > 0, np.maximum(e + 1 + HEADROOM, 0), 0)
+                scaled = pb * 2.0 ** -k[:, None]
+                pb = np.where(scaled >= 2.0 ** -126, scaled, 0.0)
+                if scale_mode == "ldexp":
+                    s = 2.0 ** -k.astype(np.float64)                         # exact scaling
+                    ts, l = (ts * s[:, None]).astype(f32), (l * s[:, None]).astype(f32)
+                    O *= s[:, None]
+                else:                                                        # the FP32 factor 2^-k
+                    alpha = np.where(k <= 149, 2.0 ** -k.astype(np.float64), 0.0).astype(f32)
+                    ts, l = (ts * alpha[:, None]).astype(f32), (l * alpha[:, None]).astype(f32)
+                    O *= alpha[:, None]
+                m = (m + k.astype(f32)).astype(f32)
+            else:
+                moves["full"] += 1
+                mx = np.where(valid[None, :], xs, -np.inf).max(axis=1)
+                mn = np.maximum((mx + f32(HEADROOM)).astype(f32), m)
+                with np.errstate(invalid="ignore"):
+                    alpha = np.where(np.isinf(m), f32(0), np.exp2((m - mn).astype(f32))).astype(f32)
+                O *= alpha[:, None]
+                l = (l * alpha[:, None]).astype(f32)
+                m = mn
+                p = probs(m)
+                ts = sums(p)
+                pb = bf16(p)
+        l = (l + ts).astype(f32)
+        O += pb[:, :w] @ v[64 * t:64 * t + w]
+    ltot = l.sum(axis=1, dtype=f32).astype(np.float64)
+    return O / ltot[:, None], (m.astype(np.float64) + np.log2(ltot)) * math.log(2), moves, O
+
+
+@pytest.fixture(scope="module")
+def stress():
+    w = WORKLOADS["numerics_stress"]
+    return w, make_dense(w)
+
+
+def stress_wave(stress, b, h, q0):
+    w, (qb, kb, vb) = stress
+    q = bf16_bits_to_f64(qb[b, h, q0:q0 + 64]).astype(f32)
+    k = bf16_bits_to_f64(kb[b, h]).astype(f32)
+    c = f32(w.scale * math.log2(math.e))
+    x = ((q @ k.T).astype(f32) * c).astype(f32)      # FP32 scores, as the matrix cores and one scaling give
+    v = bf16_bits_to_f64(vb[b, h])
+    rows = (b * w.H + h) * w.N + q0 + np.arange(64)
+    o_ref, lse_ref = attention_dense(qb, kb, vb, w.scale, rows=rows)
+    return x, v, o_ref, lse_ref
+
+
+@pytest.mark.parametrize("b,h,q0", [(0, 0, 0), (0, 5, 4096), (1, 11, 8128), (1, 15, 2048)])
+def test_replay_meets_the_bar_on_the_outlier_workload(stress, b, h, q0):
+    x, v, o_ref, lse_ref = stress_wave(stress, b, h, q0)
+    o, lse, moves, _ = replay(x, v, x.shape[1])
+    m = compare(o, o_ref, lse, lse_ref)
+    print(f"[replay] b={b} h={h} rows {q0}..: {moves}, rel_l2 {m['rel_l2']:.2e}, max_abs {m['max_abs']:.2e}, "
+          f"lse {m['lse_max_abs']:.2e}")
+    assert moves["rebase"] > 0 and moves["full"] >= 1
+    assert m["ok"], m
+
+
+def test_scaling_by_an_fp32_factor_fails_where_shifts_pass_149(stress):
+    """Find a wave whose rebase shifts exceed 149 and show the FP32-factor scaling fails there
+    while the exact scaling passes: the test would catch that mistake."""
+    found = False
+    for (b, h, q0) in [(0, 0, 0), (0, 5, 4096), (1, 11, 8128), (1, 15, 2048), (0, 3, 1024), (1, 7, 512)]:
+        x, v, o_ref, lse_ref = stress_wave(stress, b, h, q0)
+        o, lse, _, _ = replay(x, v, x.shape[1], "ldexp")
+        ob, lseb, _, _ = replay(x, v, x.shape[1], "fp32_factor")
+        bad = compare(ob, o_ref, lseb, lse_ref)
+        if not bad["ok"]:
+            assert compare(o, o_ref, lse, lse_ref)["ok"]
+            found = True
+            break
+    assert found, "no wave of the sample exercises shifts beyond 149"
+
+
+@pytest.mark.parametrize("N", [4096, 131072])
+def test_worst_climb_stays_inside_the_stated_value_bound(N):
+    """Rows whose every key sits just below the point where a lane's tile sum would reach 2^24
+    (the reference never moves after the first tile, and every accepted probability is as large
+    as the check allows): |O| before normalisation grows to about N * 2^19 * |v| and never
+    exceeds N * 2^24 * max|v|, so FP32 holds it while N * max|v| < 2^104."""
+    R = 2
+    x = np.zeros((R, N), f32)
+    x[:, :64] = 0.0                                   # first tile: the full path sets m = 0 + 32
+    x[:, 64:] = f32(32 + 24 - 5 - 1e-3)               # 32 keys per lane at just under 2^19 each
+    v = np.ones((N, 4))
+    o, lse, moves, O = replay(x, v, N)
+    assert moves["full"] == 1 and moves["rebase"] == 0
+    bound = N * 2.0 ** 24 * 1.0
+    assert np.abs(O).max() <= bound
+    assert np.abs(O).max() >= bound / 64              # the bound is reached within a factor 2^6
+    np.testing.assert_allclose(o, 1.0, rtol=2.0 ** -8)   # o = sum bf16(p) / sum p: P's rounding only

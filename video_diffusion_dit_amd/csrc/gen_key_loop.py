@@ -488,11 +488,94 @@ KLIM_IN = ("%[klim]", set())
 KLIM_EXACT = (vr(KLIM_R), vset(KLIM_R))
 
 
+def packed_p(X, rb):
+    """The 16 registers that hold row block rb's 64 probabilities of S buffer X as BF16 pairs."""
+    return [sblk(X, rb, kb) + off for kb in range(2) for off in (0, 1, 2, 3, 8, 9, 10, 11)]
+
+
+def rescale_o(E, factor, op="v_mul_f32"):
+    """O^T rows of row block rb scaled by factor[rb] (AGPR read, op, write back): op v_mul_f32
+    with an FP32 factor, or v_ldexp_f32 with an integer exponent."""
+    tmps = [TMP0 + 17 + i for i in range(7)]
+    k = 0
+    for rb in range(2):
+        for db in range(4):
+            for r in range(16):
+                a, t = oblk(db, rb) + r, tmps[k % 7]
+                k += 1
+                E.valu("v_accvgpr_read_b32 %s, %s" % (vr(t), ar(a)), rd=aset(a), wr=vset(t))
+                E.valu("%s %s, %s, %s" % (op, vr(t), vr(t), vr(factor[rb])), rd=vset(t) | vset(factor[rb]), wr=vset(t))
+                E.valu("v_accvgpr_write_b32 %s, %s" % (ar(a), vr(t)), rd=vset(t), wr=aset(a))
+
+
+def rebase_path(E, X):
+    """Fast exact path for the tile in S buffer X: move the reference without recomputing S.
+
+    The probabilities of the tile are already BF16 in registers, taken against the old
+    reference m. Any reference keeps the softmax exact; it only has to bound them. Their
+    largest value across the row (u16 maximum of the packed BF16 patterns, which order like
+    the non-negative values; the partner lane l^32 holds the row's other keys) has binary
+    exponent e, so with k = max(e + 1 + headroom, 0) the new reference m + k puts every
+    probability below 2^-headroom. Scaling by 2^-k is exact: P in place by subtracting k
+    from each BF16 exponent field (u16 max then subtract, so values that would drop below the
+    normal range, weights under 2^-126 of the new reference, become 0), l, the tile sums and
+    O by v_ldexp_f32 with -k. (Not by a multiplication with 2^-k: k reaches 161 when a key
+    lies up to 128 log2 units above the old reference, and 2^-k then is no FP32 number, while
+    the tile's own sum times 2^-k is about 2^-33.) A probability that is inf or NaN (the first tile, where
+    m = -inf, or a key beyond the FP32 range of the old reference) carries no usable maximum:
+    then the full path below recomputes S. Entered and left with all wait states satisfied."""
+    E.label(".Lrare%d_%%=" % X)
+    E.fresh()
+    E.nop(12)
+    E.raw("s_waitcnt lgkmcnt(0)")
+    E.pending = []
+    mx, px, kk, negk = (TMP0 + 2, TMP0 + 3), (TMP0 + 4, TMP0 + 5), (TMP0 + 6, TMP0 + 7), (TMP0 + 8, TMP0 + 9)
+    ki, t = TMP0 + 10, TMP0 + 11
+    for rb in range(2):
+        regs = packed_p(X, rb)
+        E.valu("v_pk_max_u16 %s, %s, %s" % (vr(mx[rb]), vr(regs[0]), vr(regs[1])), rd=vset(regs[0]) | vset(regs[1]),
+               wr=vset(mx[rb]))
+        for r in regs[2:]:
+            E.valu("v_pk_max_u16 %s, %s, %s" % (vr(mx[rb]), vr(mx[rb]), vr(r)), rd=vset(mx[rb]) | vset(r), wr=vset(mx[rb]))
+        E.valu("v_lshrrev_b32 %s, 16, %s" % (vr(t), vr(mx[rb])), rd=vset(mx[rb]), wr=vset(t))
+        E.valu("v_and_b32 %s, 0xffff, %s" % (vr(mx[rb]), vr(mx[rb])), rd=vset(mx[rb]), wr=vset(mx[rb]))
+        E.valu("v_max_u32 %s, %s, %s" % (vr(mx[rb]), vr(mx[rb]), vr(t)), rd=vset(mx[rb]) | vset(t), wr=vset(mx[rb]))
+    for rb in range(2):
+        E.emit(Ins("ds_bpermute_b32 %s, %%[bperm], %s" % (vr(px[rb]), vr(mx[rb])), "lds", rd=vset(mx[rb]), wr=vset(px[rb]),
+                   lds=True))
+    for rb in range(2):   # any lane whose maximum is an inf/NaN pattern (>= 0x7f80)?
+        E.valu("v_max_u32 %s, %s, %s" % (vr(mx[rb]), vr(mx[rb]), vr(px[rb])), rd=vset(mx[rb]) | vset(px[rb]), wr=vset(mx[rb]))
+        E.valu("v_cmp_le_u32 vcc, 0x7f80, %s" % vr(mx[rb]), rd=vset(mx[rb]), wr=VCC)
+        if rb == 0:
+            E.salu("s_mov_b64 s[%d:%d], vcc" % (S_C1, S_C1 + 1))
+    E.salu("s_or_b64 s[%d:%d], s[%d:%d], vcc" % (S_C1, S_C1 + 1, S_C1, S_C1 + 1))
+    E.raw("s_cbranch_scc1 .Lfull%d_%%=" % X)
+    bias = 126 - OPTS["headroom"]    # k = (biased exponent - 127) + 1 + headroom
+    for rb in range(2):
+        E.valu("v_lshrrev_b32 %s, 7, %s" % (vr(ki), vr(mx[rb])), rd=vset(mx[rb]), wr=vset(ki))
+        E.valu("v_subrev_u32 %s, %d, %s" % (vr(ki), bias, vr(ki)), rd=vset(ki), wr=vset(ki))
+        E.valu("v_max_i32 %s, 0, %s" % (vr(ki), vr(ki)), rd=vset(ki), wr=vset(ki))
+        E.valu("v_cvt_f32_i32 %s, %s" % (vr(t), vr(ki)), rd=vset(ki), wr=vset(t))
+        E.valu("v_add_f32 %s, %s, %s" % (vr(M[rb]), vr(M[rb]), vr(t)), rd=vset(M[rb]) | vset(t), wr=vset(M[rb]))
+        E.valu("v_sub_u32 %s, 0, %s" % (vr(negk[rb]), vr(ki)), rd=vset(ki), wr=vset(negk[rb]))
+        E.valu("v_lshlrev_b32 %s, 7, %s" % (vr(kk[rb]), vr(ki)), rd=vset(ki), wr=vset(kk[rb]))
+        E.valu("v_lshl_or_b32 %s, %s, 16, %s" % (vr(kk[rb]), vr(kk[rb]), vr(kk[rb])), rd=vset(kk[rb]), wr=vset(kk[rb]))
+        for r in packed_p(X, rb):
+            E.valu("v_pk_max_u16 %s, %s, %s" % (vr(r), vr(r), vr(kk[rb])), rd=vset(r) | vset(kk[rb]), wr=vset(r))
+            E.valu("v_pk_sub_u16 %s, %s, %s" % (vr(r), vr(r), vr(kk[rb])), rd=vset(r) | vset(kk[rb]), wr=vset(r))
+        for x in (L[rb], TS[rb]):
+            E.valu("v_ldexp_f32 %s, %s, %s" % (vr(x), vr(x), vr(negk[rb])), rd=vset(x) | vset(negk[rb]), wr=vset(x))
+    rescale_o(E, negk, "v_ldexp_f32")
+    E.fresh()
+    E.nop(12)
+    E.raw("s_setpc_b64 s[%d:%d]" % (S_RA, S_RA + 1))
+
+
 def rare_path(E, X):
-    """Exact path for the tile in S buffer X whose K sits at LDS offset s[S_STG] (+ the ka
+    """Full exact path for the tile in S buffer X whose K sits at LDS offset s[S_STG] (+ the ka
     operands): recompute S, take the row maximum (masked keys excluded), rescale O and l,
     recompute P and the tile sums. Entered and left with all wait states satisfied."""
-    E.label(".Lrare%d_%%=" % X)
+    E.label(".Lfull%d_%%=" % X)
     E.fresh()
     E.nop(12)
     E.raw("s_waitcnt lgkmcnt(0)")
@@ -540,16 +623,7 @@ def rare_path(E, X):
         E.valu("v_mov_b32 %s, %s" % (vr(M[rb]), vr(tm[rb])), rd=vset(tm[rb]), wr=vset(M[rb]))
     for rb in range(2):
         E.valu("v_mul_f32 %s, %s, %s" % (vr(L[rb]), vr(L[rb]), vr(alpha[rb])), rd=vset(L[rb]) | vset(alpha[rb]), wr=vset(L[rb]))
-    tmps = [TMP0 + 17 + i for i in range(7)]
-    k = 0
-    for rb in range(2):
-        for db in range(4):
-            for r in range(16):
-                a, t = oblk(db, rb) + r, tmps[k % 7]
-                k += 1
-                E.valu("v_accvgpr_read_b32 %s, %s" % (vr(t), ar(a)), rd=aset(a), wr=vset(t))
-                E.valu("v_mul_f32 %s, %s, %s" % (vr(t), vr(t), vr(alpha[rb])), rd=vset(t) | vset(alpha[rb]), wr=vset(t))
-                E.valu("v_accvgpr_write_b32 %s, %s" % (ar(a), vr(t)), rd=vset(t), wr=aset(a))
+    rescale_o(E, alpha)
     for f in softmax_half(X, 0, True, KLIM_EXACT, H1) + softmax_half(X, 1, True, KLIM_EXACT, H2) + check_ops()[:6]:
         f(E)
     E.fresh()
@@ -660,6 +734,7 @@ def generate(backedge=None):
     final_phase(E, 0, 0, "S")
 
     for X in range(2):
+        rebase_path(E, X)
         rare_path(E, X)
 
     E.label(".Ldone_%=")
