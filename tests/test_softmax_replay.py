@@ -48,14 +48,17 @@ def lane_of_key():
     return (np.arange(64) % 16) // 8
 
 
-def replay(x, v, n, scale_mode="ldexp"):
+def replay(x, v, n, scale_mode="ldexp", divisor="fp32"):
     """Rows of one wave: x [R, N] FP32 scores in log2 units (scale*log2(e)*q.k), v [N, d] float64.
-    Returns o [R, d], lse [R] (natural log), and the counts of rebase and full moves."""
+    Returns o [R, d], lse [R] (natural log), the counts of rebase and full moves, and O before
+    normalisation. divisor: "fp32" (the kernel: O / l) or "bf16" (O divided by the sum of the
+    BF16 probabilities, a measured alternative)."""
     R, N = x.shape
     ntk = -(-N // 64)
     lane = lane_of_key()
     m = np.full(R, -np.inf, f32)
     l = np.zeros((R, 2), f32)
+    lb = np.zeros(R, f32)
     O = np.zeros((R, v.shape[1]))
     moves = {"rebase": 0, "full": 0}
     for t in range(ntk):
@@ -85,10 +88,12 @@ def replay(x, v, n, scale_mode="ldexp"):
                 if scale_mode == "ldexp":
                     s = 2.0 ** -k.astype(np.float64)                         # exact scaling
                     ts, l = (ts * s[:, None]).astype(f32), (l * s[:, None]).astype(f32)
+                    lb = (lb * s).astype(f32)
                     O *= s[:, None]
                 else:                                                        # the FP32 factor 2^-k
                     alpha = np.where(k <= 149, 2.0 ** -k.astype(np.float64), 0.0).astype(f32)
                     ts, l = (ts * alpha[:, None]).astype(f32), (l * alpha[:, None]).astype(f32)
+                    lb = (lb * alpha).astype(f32)
                     O *= alpha[:, None]
                 m = (m + k.astype(f32)).astype(f32)
             else:
@@ -99,14 +104,17 @@ def replay(x, v, n, scale_mode="ldexp"):
                     alpha = np.where(np.isinf(m), f32(0), np.exp2((m - mn).astype(f32))).astype(f32)
                 O *= alpha[:, None]
                 l = (l * alpha[:, None]).astype(f32)
+                lb = (lb * alpha).astype(f32)
                 m = mn
                 p = probs(m)
                 ts = sums(p)
                 pb = bf16(p)
         l = (l + ts).astype(f32)
+        lb = (lb + pb.sum(axis=1)).astype(f32)
         O += pb[:, :w] @ v[64 * t:64 * t + w]
     ltot = l.sum(axis=1, dtype=f32).astype(np.float64)
-    return O / ltot[:, None], (m.astype(np.float64) + np.log2(ltot)) * math.log(2), moves, O
+    div = {"bf16": lb.astype(np.float64), "fp32": ltot}[divisor]
+    return O / div[:, None], (m.astype(np.float64) + np.log2(ltot)) * math.log(2), moves, O
 
 
 @pytest.fixture(scope="module")
