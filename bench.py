@@ -53,7 +53,8 @@ def kernel_source_hash(kind: str = "dense") -> str:
 # Kernels one call dispatches (the first is the dominant one).
 CALL_KERNELS = {
     "dense": ("attn_fwd_dense_kernel", "attn_fwd_dense_split_kernel", "merge_kernel"),
-    "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule"),
+    "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule", "varlen_split_plan", "attn_fwd_varlen_split_kernel",
+               "varlen_merge_kernel"),
     "prologue": ("qk_prologue_kernel",),
     "linear": ("linear_out_kernel", "linear_kv_partial_kernel", "linear_kv_reduce_kernel"),
     "block_sparse": ("attn_fwd_block_sparse_kernel", "route_kernel", "pool_kernel", "lpt_order_kernel"),
@@ -131,7 +132,7 @@ def write_traffic_profile(args) -> int:
 
     f_att, f_calls, (_, copy_key, f_copy_kib) = split(_pmc_dispatches(fetch_csv, "FETCH_SIZE"))
     w_att, w_calls, (_, _, w_copy_kib) = split(_pmc_dispatches(write_csv, "WRITE_SIZE"))
-    split_kv = any("attn_fwd_dense_split_kernel" in name for name, _ in f_att)
+    split_kv = any(k in name for name, _ in f_att for k in ("attn_fwd_dense_split_kernel", "varlen_split_plan"))
     f_copy, w_copy = f_copy_kib * 1024.0, w_copy_kib * 1024.0
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
     fetch_b = sum(v for _, v in f_att) / f_calls * 1024.0 * f_scale
@@ -224,7 +225,7 @@ def write_mfma_profile(args) -> int:
     w = WORKLOADS[args.workload]
     counter_flops = mfma * FLOP_PER_MFMA
     algorithmic = w.flops()
-    split_kv = any(kname[d] == "attn_fwd_dense_split_kernel" for d in kname)
+    split_kv = any(kname[d] in ("attn_fwd_dense_split_kernel", "varlen_split_plan") for d in kname)
     path = os.path.join(PROFILES, f"{kernel}_{args.workload}_mfma_counters.txt")
     with open(path, "w") as f:
         f.write(f"# Matrix-core counters of one call ({', '.join(names)} as dispatched) on the "
@@ -684,7 +685,7 @@ def main() -> int:
                          "FP64 work on 16 host cores at 720p)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split-kv", action="store_true",
-                    help="dense workloads: plain attn_fwd, without cutting the last round's tiles over keys")
+                    help="plain attn_fwd / attn_fwd_varlen, without cutting the last tiles over keys")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many MiB "
                          "(the known-size reference for the HBM byte counters)")
@@ -753,7 +754,10 @@ def main() -> int:
     cu_d = None if cu is None else torch.from_numpy(cu).to("cuda:0")
     cu_host = None if cu is None else [int(x) for x in cu]
     vd.load_library()
-    split = w.kind == "dense" and not args.no_split_kv and vd.splitkv_workspace_bytes(w.B, w.H, w.N) > 0
+    if w.kind == "dense":
+        split = not args.no_split_kv and vd.splitkv_workspace_bytes(w.B, w.H, w.N) > 0
+    else:   # the packed call plans its split on the device; it may split nothing
+        split = not args.no_split_kv
     kernel = CALL_KERNELS[w.kind][0]
 
     def step():
@@ -761,6 +765,8 @@ def main() -> int:
             vd.attention._launch_dense_splitkv(q, k, v, out, lse, w.scale, 0)
         elif w.kind == "dense":
             vd.attention._launch_dense(q, k, v, out, lse, w.scale)
+        elif split:
+            vd.attention._launch_varlen_splitkv(q, k, v, cu_d, out, lse, w.scale, 0)
         else:
             vd.attention._launch_varlen(q, k, v, cu_d, out, lse, w.scale, cu_host)
 
@@ -815,8 +821,11 @@ def main() -> int:
             "bound": "mfma",
             "kernel": kernel,
             "timed": ("whole call on its stream: " + kernel +
-                      (" for whole query tiles, then attn_fwd_dense_split_kernel and merge_kernel"
-                       " for the last round's tiles" if split else "")),
+                      ((" for whole query tiles, then attn_fwd_dense_split_kernel and merge_kernel"
+                        " for the last round's tiles") if split and w.kind == "dense" else
+                       (" after build_varlen_schedule and varlen_split_plan, then attn_fwd_varlen_split_kernel"
+                        " and varlen_merge_kernel for the planned tail") if split else
+                       " after build_varlen_schedule" if w.kind == "varlen" else "")),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

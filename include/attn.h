@@ -123,6 +123,35 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
 /* Workspace bytes attn_fwd_varlen needs for these sizes (0 if the sizes are invalid). */
 size_t attn_fwd_varlen_workspace_bytes(int nseg, int H, int total_tokens);
 
+/*
+ * Packed variable-length forward with split-KV of the schedule's tail. Page "PR #33702
+ * report", implementation breakdown item 2: the varlen backend there splits the key range of
+ * long sequences (kv_splits, chosen from the device and the lengths). Here the split is
+ * planned on the device from the segment lengths, for `slots` resident workgroups: items
+ * (segment query tile, head) cost their segment's key tiles and run longest segment first;
+ * the leading whole rounds of slots equal-cost items run whole, and the remaining items are
+ * cut into equal shares of (item, key tile) pairs, one per workgroup, when a share is shorter
+ * than the longest remaining item (otherwise nothing is split and the call equals
+ * attn_fwd_varlen). The pieces of a cut item are merged as attn_fwd_splitkv merges them.
+ * The result equals attn_fwd_varlen's within rounding (each piece takes its BF16
+ * probabilities against its own reference); items that are not cut are bit-identical to it;
+ * for the same inputs, slots and device it is bitwise repeatable.
+ *   q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens, d, scale, stream : as attn_fwd_varlen.
+ *   slots      : workgroups that run at once; <= 0 means the current device's compute units;
+ *                1 means no split; at most ATTN_MAX_SLOTS.
+ *   workspace  : DEVICE scratch of at least attn_fwd_varlen_splitkv_workspace_bytes(nseg, H,
+ *                total_tokens, d, slots) bytes, 256-byte aligned (schedule, plan, cost
+ *                prefix, partial results of cut items); no initialisation needed; not to be
+ *                shared by calls that may run concurrently.
+ * Returns an attn_status_t.
+ */
+int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d,
+                            float scale, int slots, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_varlen_splitkv needs (0 if the sizes are invalid). */
+size_t attn_fwd_varlen_splitkv_workspace_bytes(int nseg, int H, int total_tokens, int d, int slots);
+
 /* Bytes of the fixed device scratch array behind attn_fwd_varlen_noalloc (per device). */
 #define ATTN_NOALLOC_SCRATCH_BYTES 524288
 

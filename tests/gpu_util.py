@@ -88,3 +88,60 @@ def cut_tile_rows(B, H, N, slots, per_tile=2, seed=0):
 def device_slots() -> int:
     """Workgroups of the attention kernel that run at once on cuda:0: one per compute unit."""
     return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# ---- the split-KV plan of attn_fwd_varlen_splitkv (made on the device), restated
+
+def varlen_plan(seqlens, H, slots, min_tiles=16, sort_limit=8192):
+    """(entries, D, G, cut) of the device plan: entries [(segment, query tile, key tiles)] in
+    schedule order (longest segment first), D plain items, G split workgroups (0: no split) and
+    the set of cut items (item = entry * H + head)."""
+    lens = [int(x) for x in seqlens]
+    order = sorted(range(len(lens)), key=lambda s: (-lens[s], s)) if len(lens) <= sort_limit else list(range(len(lens)))
+    entries = [(s, i, -(-lens[s] // 64)) for s in order for i in range(-(-lens[s] // 256))]
+    cum = [0]
+    for _, _, c in entries:
+        cum.append(cum[-1] + c)
+    items = len(entries) * H
+    cost = lambda it: entries[it // H][2]
+    cum_item = lambda it: H * cum[it // H] + (it % H) * cost(it)
+    r = 0
+    while (r + 1) * slots <= items and cost(r * slots) == cost((r + 1) * slots - 1):
+        r += 1
+    D = r * slots
+    if D >= items:
+        return entries, items, 0, set()
+    base, W = cum_item(D), H * cum[-1] - cum_item(D)
+    cmax = max(c for _, _, c in entries[D // H:])
+    G = min(slots, W // min_tiles)
+    if G < 2 or W // G >= cmax:
+        return entries, items, 0, set()
+
+    def item_at(u):
+        e = max(i for i in range(len(entries)) if H * cum[i] <= u)
+        return e * H + (u - H * cum[e]) // entries[e][2]
+    cut = set()
+    for g in range(1, G):
+        u = base + W * g // G
+        it = item_at(u)
+        if u != cum_item(it):
+            cut.add(it)
+    return entries, D, G, cut
+
+
+def varlen_cut_rows(seqlens, H, slots, per_item=2, seed=0):
+    """Flat rows h * T + t in the items the plan cuts: each cut item's first and last row plus
+    `per_item` seeded rows (LSE layout [H, T])."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in seqlens]
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    T = int(starts[-1])
+    entries, _, _, cut = varlen_plan(lens, H, slots)
+    rows = set()
+    for it in cut:
+        s, i, _ = entries[it // H]
+        h = it % H
+        lo, hi = i * 256, min(lens[s], (i + 1) * 256)
+        for r in {lo, hi - 1, *rng.integers(lo, hi, per_item).tolist()}:
+            rows.add(h * T + int(starts[s]) + r)
+    return np.array(sorted(rows), dtype=np.int64)

@@ -61,6 +61,10 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i32
         lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
         lib.attn_fwd_varlen.restype = i32
+        lib.attn_fwd_varlen_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+        lib.attn_fwd_varlen_splitkv.restype = i32
+        lib.attn_fwd_varlen_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.attn_fwd_varlen_splitkv_workspace_bytes.restype = sz
         lib.attn_fwd_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
         lib.attn_fwd_varlen_noalloc.restype = i32
         lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
@@ -253,11 +257,15 @@ def check_cu_seqlens(cu_host, total_tokens: int):
 
 def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                     scale: float | None = None, return_lse: bool = False,
-                    out: torch.Tensor | None = None, cu_seqlens_host=None):
+                    out: torch.Tensor | None = None, cu_seqlens_host=None, split_kv: bool = True,
+                    slots: int = 0):
     """Packed varlen forward: q, k, v BF16 [T, H, 128] (THD), attention within each segment.
 
     cu_seqlens: int32 tensor [nseg + 1] on q's device. The offsets are validated on a host
     copy (``cu_seqlens_host`` if given, else copied from the device, which synchronises).
+    With split_kv (default) the schedule's tail is split over keys when that shortens it
+    (attn_fwd_varlen_splitkv; ``slots`` = concurrent workgroups, 0 = the device's compute
+    units); otherwise the plain attn_fwd_varlen call.
     Returns out (BF16 [T,H,128]) or (out, lse FP32 [H,T]).
     """
     _check_tensors(q, k, v, 3)
@@ -278,8 +286,24 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
-    _launch_varlen(q, k, v, cu_seqlens, out, lse, _default_scale(d, scale))
+    if split_kv:
+        _launch_varlen_splitkv(q, k, v, cu_seqlens, out, lse, _default_scale(d, scale), slots)
+    else:
+        _launch_varlen(q, k, v, cu_seqlens, out, lse, _default_scale(d, scale))
     return (out, lse) if return_lse else out
+
+
+def _launch_varlen_splitkv(q, k, v, cu_seqlens, out, lse, scale: float, slots: int = 0):
+    """One attn_fwd_varlen_splitkv call on already-checked tensors, with a cached workspace."""
+    lib = load_library()
+    T, H, d = q.shape
+    nseg = cu_seqlens.numel() - 1
+    with torch.cuda.device(q.device):
+        nbytes = int(lib.attn_fwd_varlen_splitkv_workspace_bytes(nseg, H, T, d, slots))
+        ws = _workspace(q.device, nbytes)
+        st = lib.attn_fwd_varlen_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+                                         nseg, H, T, d, scale, slots, _ptr(ws), ws.numel(), _stream_handle(q.device))
+    _raise_for(lib, st)
 
 
 def _launch_varlen(q, k, v, cu_seqlens, out, lse, scale: float, cu_seqlens_host=None):

@@ -502,6 +502,41 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* out, floa
                                                scale, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_fwd_varlen_splitkv_workspace_bytes(int nseg, int H, int total_tokens, int d, int slots) {
+    if (nseg <= 0 || H <= 0 || total_tokens < 0 || d != 128 || slots > ATTN_MAX_SLOTS) return 0;
+    if (slots <= 0) slots = attn_impl::concurrent_workgroups();
+    if (slots < 2) return attn_impl::varlen_workspace_bytes(nseg, total_tokens);
+    return attn_impl::varlen_split_workspace_bytes(nseg, total_tokens, slots);
+}
+
+int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d, float scale,
+                            int slots, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = '\0';
+    bool empty;
+    long long elems = 0;
+    int st = check_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens, d, scale, empty, elems);
+    if (st != ATTN_OK || empty) return st;
+    if (slots > ATTN_MAX_SLOTS) return fail(ATTN_ERR_INVALID_ARG, "slots exceeds ATTN_MAX_SLOTS");
+    if (slots <= 0) slots = attn_impl::concurrent_workgroups();
+    const size_t need = slots < 2 ? attn_impl::varlen_workspace_bytes(nseg, total_tokens)
+                                  : attn_impl::varlen_split_workspace_bytes(nseg, total_tokens, slots);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace missing or smaller than attn_fwd_varlen_splitkv_workspace_bytes()");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (overlaps(workspace, need, out, (size_t)elems * 2) || overlaps(workspace, need, q, (size_t)elems * 2) ||
+        overlaps(workspace, need, k, (size_t)elems * 2) || overlaps(workspace, need, v, (size_t)elems * 2) ||
+        overlaps(workspace, need, cu_seqlens, sizeof(int32_t) * ((size_t)nseg + 1)) ||
+        overlaps(workspace, need, lse, lse ? (size_t)product(H, total_tokens, 1, 1) * 4 : 0))
+        return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps a tensor argument");
+    if (slots < 2)
+        return hip_status(attn_impl::launch_varlen(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens, scale,
+                                                   workspace, static_cast<hipStream_t>(stream)));
+    return hip_status(attn_impl::launch_varlen_split(q, k, v, out, lse, cu_seqlens, nseg, H, total_tokens, scale,
+                                                     slots, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
                             const int32_t* cu_seqlens, int nseg, int H, int total_tokens, int d, float scale,
                             void* stream) {

@@ -51,6 +51,7 @@
 // is the same softmax; only the reference the BF16 probabilities are taken against differs,
 // and BF16 rounding is relative, so its error bound does not depend on it.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -363,8 +364,12 @@ __global__ __launch_bounds__(256) void merge_kernel(DenseArgs a, SplitArgs sp) {
     *reinterpret_cast<bf16x8*>(a.o + base + (long)row * D + 8 * k) = ov;
     if (a.lse != nullptr && k == 0) a.lse[(long)bh * a.N + row] = (M + __log2f(l)) * LN2;
 }
-// Varlen schedule in the workspace: [0] entry count, then order[nseg] (segment ids, longest
-// first), then entries (segment, query tile) in that order.
+// Varlen schedule in the workspace: a 256-byte header, then order[nseg] (segment ids, longest
+// first), then entries (segment, query tile) in that order. Header: int [0] entry count,
+// [1] items the plain kernel runs (item = entry * H + head; all of them unless a split plan
+// took the tail), [2] workgroups of the split kernel (0: no split); int64 at byte 16 the cost
+// (key tiles) of the items before the split ones, at byte 24 the cost of the split ones;
+// [3] 1 when every entry was listed (offsets that overrun the list cap are not split).
 constexpr size_t WS_HEADER = 256;
 constexpr int SORT_LIMIT = 8192;   // above this many segments keep the given order
 
@@ -380,9 +385,13 @@ __device__ __forceinline__ int seg_len(const int32_t* cu, int s, int T) {
     return e - a;
 }
 
+// cum (if not null): int64 [entries + 1], the key tiles of the entries before each entry
+// (an entry's cost is its segment's key-tile count, the same for every head).
 __global__ __launch_bounds__(1024) void build_varlen_schedule(const int32_t* __restrict__ cu,
-                                                              int nseg, int T, char* ws) {
+                                                              int nseg, int T, char* ws, int H,
+                                                              long long* __restrict__ cum) {
     __shared__ int chunk[1024];
+    __shared__ long long cost_chunk[1024];
     int* count = reinterpret_cast<int*>(ws);
     int* order = reinterpret_cast<int*>(ws + WS_HEADER);
     int2* list = reinterpret_cast<int2*>(ws + ws_list_offset(nseg));
@@ -407,27 +416,80 @@ __global__ __launch_bounds__(1024) void build_varlen_schedule(const int32_t* __r
     const int per = (nseg + 1023) / 1024;
     const int r0 = min(tid * per, nseg), r1 = min(r0 + per, nseg);
     int sum = 0;
-    for (int r = r0; r < r1; ++r) sum += (seg_len(cu, order[r], T) + BM - 1) / BM;
+    long long csum = 0;
+    for (int r = r0; r < r1; ++r) {
+        const int len = seg_len(cu, order[r], T);
+        sum += (len + BM - 1) / BM;
+        csum += (long long)((len + BM - 1) / BM) * ((len + BN - 1) / BN);
+    }
     chunk[tid] = sum;
+    cost_chunk[tid] = csum;
     __syncthreads();
     if (tid == 0) {
         int acc = 0;
+        long long cacc = 0;
         for (int i = 0; i < 1024; ++i) {
             const int v = chunk[i];
+            const long long cv = cost_chunk[i];
             chunk[i] = acc;
+            cost_chunk[i] = cacc;
             acc += v;
+            cacc += cv;
         }
-        *count = (int)min((long)acc, cap);   // malformed offsets cannot push readers past the list
+        const int n = (int)min((long)acc, cap);   // malformed offsets cannot push readers past the list
+        count[0] = n;
+        count[1] = (int)min((long long)n * H, (long long)INT_MAX);   // every item runs whole
+        count[2] = 0;
+        count[3] = n == acc;   // every entry listed (the cost prefix is whole)
+        if (cum != nullptr && n == acc) cum[n] = cacc;
     }
     __syncthreads();
     long off = chunk[tid];
+    long long cc = cost_chunk[tid];
     for (int r = r0; r < r1; ++r) {
         const int s = order[r];
-        const int nt = (seg_len(cu, s, T) + BM - 1) / BM;
+        const int len = seg_len(cu, s, T);
+        const int nt = (len + BM - 1) / BM, ntk = (len + BN - 1) / BN;
         for (int i = 0; i < nt; ++i)
-            if (off + i < cap) list[off + i] = make_int2(s, i);
+            if (off + i < cap) {
+                list[off + i] = make_int2(s, i);
+                if (cum != nullptr) cum[off + i] = cc + (long long)i * ntk;
+            }
         off += nt;
+        cc += (long long)nt * ntk;
     }
+}
+
+// Split-KV plan of a packed call for `slots` resident workgroups (one workgroup, after
+// build_varlen_schedule). Items (entry e, head h) = e * H + h cost their segment's key tiles;
+// the list runs longest segments first. The leading whole rounds of slots items of equal cost
+// run whole in the plain kernel (they finish together); the rest is shared by G workgroups in
+// equal contiguous shares of (item, key tile) pairs, if a share is shorter than the tail's
+// longest item (else splitting would not shorten the tail, and nothing is split).
+__global__ __launch_bounds__(64) void varlen_split_plan(char* ws, const long long* __restrict__ cum, int H,
+                                                        int slots) {
+    if (threadIdx.x != 0) return;
+    int* hdr = reinterpret_cast<int*>(ws);
+    long long* hdr64 = reinterpret_cast<long long*>(ws + 16);
+    const long long n = hdr[0];
+    const long long items = n * H;
+    auto cost = [&](long long item) { const long long e = item / H; return cum[e + 1] - cum[e]; };
+    if (!hdr[3]) return;
+    long long r = 0;
+    while ((r + 1) * slots <= items && cost(r * slots) == cost((r + 1) * slots - 1)) ++r;
+    const long long D = r * slots;
+    hdr[2] = 0;
+    if (!hdr[3] || D >= items || items > INT_MAX) return;
+    auto cum_item = [&](long long item) { const long long e = item / H; return H * cum[e] + (item - e * H) * (cum[e + 1] - cum[e]); };
+    const long long base = cum_item(D), W = H * cum[n] - base;
+    long long cmax = 0;
+    for (long long e = D / H; e < n; ++e) cmax = max(cmax, cum[e + 1] - cum[e]);
+    const long long G = min((long long)slots, W / SPLIT_MIN_TILES);
+    if (G < 2 || W / G >= cmax) return;
+    hdr[1] = (int)D;
+    hdr[2] = (int)G;
+    hdr64[0] = base;
+    hdr64[1] = W;
 }
 
 struct VarlenArgs {
@@ -444,7 +506,7 @@ struct VarlenArgs {
 
 __global__ __launch_bounds__(NT, 1) void attn_fwd_varlen_kernel(VarlenArgs a) {
     const int e = blockIdx.x / a.H, h = blockIdx.x - e * a.H;
-    if (e >= *reinterpret_cast<const int*>(a.ws)) return;
+    if (e >= reinterpret_cast<const int*>(a.ws)[0] || (int)blockIdx.x >= reinterpret_cast<const int*>(a.ws)[1]) return;
     const int2 t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
     const int start = min(max(a.cu[t.x], 0), a.T);
     const int n = seg_len(a.cu, t.x, a.T);
@@ -452,6 +514,121 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_varlen_kernel(VarlenArgs a) {
     const long base = ((long)start * a.H + h) * D;
     attn_rows<false>(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)h * a.T + start : nullptr,
                      (long)a.H * D, n, t.y * BM, a.c, 0, (n + BN - 1) / BN, nullptr);
+}
+
+// Split-KV of a packed call (the plan of varlen_split_plan): workgroup g covers the cost units
+// [lo(g), lo(g+1)) of the split items, lo(g) = base + W g / G; an item's units are its key
+// tiles. Whole items write O and LSE; a cut item's piece writes its partial rows to slot 2g if
+// the item is the share's first, else 2g+1 (only a share's first and last items can be cut).
+struct VarlenSplitArgs {
+    const long long* cum;
+    float* part;
+};
+
+__device__ __forceinline__ long long vs_cost(const long long* cum, int H, long long item) {
+    const long long e = item / H;
+    return cum[e + 1] - cum[e];
+}
+__device__ __forceinline__ long long vs_cum_item(const long long* cum, int H, long long item) {
+    const long long e = item / H;
+    return H * cum[e] + (item - e * H) * (cum[e + 1] - cum[e]);
+}
+// the item holding cost unit u (0 <= u < H * cum[n])
+__device__ __forceinline__ long long vs_item_at(const long long* cum, int H, int n, long long u) {
+    int lo = 0, hi = n;   // H*cum[lo] <= u < H*cum[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (H * cum[mid] <= u) lo = mid;
+        else hi = mid;
+    }
+    return (long long)lo * H + (u - H * cum[lo]) / (cum[lo + 1] - cum[lo]);
+}
+__device__ __forceinline__ long long vs_share_begin(long long base, long long W, int G, int g) {
+    return base + W * g / G;
+}
+// the share holding unit u (base <= u < base + W)
+__device__ __forceinline__ int vs_share_of(long long base, long long W, int G, long long u) {
+    int g = (int)((u - base) * G / W);
+    while (g + 1 < G && vs_share_begin(base, W, G, g + 1) <= u) ++g;
+    while (g > 0 && vs_share_begin(base, W, G, g) > u) --g;
+    return g;
+}
+
+__global__ __launch_bounds__(NT, 1) void attn_fwd_varlen_split_kernel(VarlenArgs a, VarlenSplitArgs sp) {
+    const int* hdr = reinterpret_cast<const int*>(a.ws);
+    const int G = hdr[2], g = blockIdx.x;
+    if (g >= G) return;
+    const int n_ent = hdr[0];
+    const long long base = reinterpret_cast<const long long*>(a.ws + 16)[0];
+    const long long W = reinterpret_cast<const long long*>(a.ws + 16)[1];
+    const long long lo = vs_share_begin(base, W, G, g), hi = vs_share_begin(base, W, G, g + 1);
+    const int2* list = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg));
+    const long long first = vs_item_at(sp.cum, a.H, n_ent, lo);
+    for (long long it = first; it < (long long)n_ent * a.H; ++it) {
+        const long long ci = vs_cum_item(sp.cum, a.H, it);
+        if (ci >= hi) break;
+        const long long c = vs_cost(sp.cum, a.H, it);
+        const long long t0 = lo > ci ? lo - ci : 0, t1 = hi < ci + c ? hi - ci : c;
+        const int e = (int)(it / a.H), h = (int)(it - (long long)e * a.H);
+        const int2 t = list[e];
+        const int start = min(max(a.cu[t.x], 0), a.T);
+        const int n = seg_len(a.cu, t.x, a.T);
+        const long base_el = ((long)start * a.H + h) * D;
+        float* part = nullptr;
+        if (t0 != 0 || t1 != c) part = sp.part + (size_t)(2 * g + (it == first ? 0 : 1)) * (PART_BYTES / sizeof(float));
+        if (it != first) __syncthreads();   // the previous piece's waves are done with LDS
+        attn_rows<false>(a.q + base_el, a.k + base_el, a.v + base_el, a.o + base_el,
+                         a.lse ? a.lse + (long)h * a.T + start : nullptr, (long)a.H * D, n, t.y * BM, a.c,
+                         (int)t0, (int)t1, part);
+    }
+}
+
+// One block per (share boundary b = 1 .. G-1, 16 rows): the item cut by boundary b is merged
+// by the block of the first boundary inside it, O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p.
+__global__ __launch_bounds__(256) void varlen_merge_kernel(VarlenArgs a, VarlenSplitArgs sp) {
+    const int* hdr = reinterpret_cast<const int*>(a.ws);
+    const int G = hdr[2], b = blockIdx.x / 16 + 1, rblk = blockIdx.x & 15;
+    if (b >= G) return;
+    const int n_ent = hdr[0];
+    const long long base = reinterpret_cast<const long long*>(a.ws + 16)[0];
+    const long long W = reinterpret_cast<const long long*>(a.ws + 16)[1];
+    const long long u = vs_share_begin(base, W, G, b);
+    const long long it = vs_item_at(sp.cum, a.H, n_ent, u);
+    const long long ci = vs_cum_item(sp.cum, a.H, it), c = vs_cost(sp.cum, a.H, it);
+    if (u == ci) return;                                   // the boundary falls between items
+    const int g0 = vs_share_of(base, W, G, ci);
+    if (b != g0 + 1) return;                               // an earlier boundary's block merges it
+    const int g1 = vs_share_of(base, W, G, ci + c - 1);
+    const int e = (int)(it / a.H), h = (int)(it - (long long)e * a.H);
+    const int2 t = reinterpret_cast<const int2*>(a.ws + ws_list_offset(a.nseg))[e];
+    const int start = min(max(a.cu[t.x], 0), a.T);
+    const int n = seg_len(a.cu, t.x, a.T);
+    const int r = rblk * 16 + (threadIdx.x >> 4), k = threadIdx.x & 15;
+    const int row = t.y * BM + r;
+    if (row >= n) return;
+    auto slot_row = [&](int g) {
+        const int slot = 2 * g + (vs_item_at(sp.cum, a.H, n_ent, vs_share_begin(base, W, G, g)) == it ? 0 : 1);
+        return sp.part + (size_t)slot * (PART_BYTES / sizeof(float)) + (size_t)r * PART_STRIDE;
+    };
+    float M = -INFINITY;
+    for (int g = g0; g <= g1; ++g) M = fmaxf(M, slot_row(g)[128]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int g = g0; g <= g1; ++g) {
+        const float* prow = slot_row(g);
+        const float wgt = exp2_hw(prow[128] - M);
+        l += wgt * prow[129];
+        const float4 x0 = reinterpret_cast<const float4*>(prow + 8 * k)[0];
+        const float4 x1 = reinterpret_cast<const float4*>(prow + 8 * k)[1];
+        acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
+        acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
+    }
+    const float inv = 1.0f / l;
+    bf16x8 ov;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ov[x] = (bf16)(acc[x] * inv);
+    *reinterpret_cast<bf16x8*>(a.o + ((long)(start + row) * a.H + h) * D + 8 * k) = ov;
+    if (a.lse != nullptr && k == 0) a.lse[(long)h * a.T + start + row] = (M + __log2f(l)) * LN2;
 }
 
 // Block-skip attention over a packed batch: the varlen schedule's entry (segment s, query
@@ -650,7 +827,8 @@ hipError_t launch_block_sparse_varlen(const void* q, const void* k, const void* 
                                       const int32_t* order, int nseg, int H, int total_tokens, float scale,
                                       void* workspace, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
-    hipLaunchKernelGGL(build_varlen_schedule, dim3(1), dim3(1024), 0, stream, cu_seqlens, nseg, total_tokens, ws);
+    hipLaunchKernelGGL(build_varlen_schedule, dim3(1), dim3(1024), 0, stream, cu_seqlens, nseg, total_tokens, ws, H,
+                       (long long*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     char* offs = ws + varlen_workspace_bytes(nseg, total_tokens);
@@ -697,12 +875,56 @@ hipError_t noalloc_scratch(void** ptr) {
     return hipSuccess;
 }
 
+size_t varlen_split_workspace_bytes(int nseg, int total_tokens, int slots) {
+    return varlen_workspace_bytes(nseg, total_tokens) + ws_align(sizeof(long long) * (size_t)(max_entries(nseg, total_tokens) + 1)) +
+           2 * (size_t)slots * PART_BYTES;
+}
+
+hipError_t launch_varlen_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                               const int32_t* cu_seqlens, int nseg, int H, int total_tokens, float scale, int slots,
+                               void* workspace, hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    long long* cum = reinterpret_cast<long long*>(ws + varlen_workspace_bytes(nseg, total_tokens));
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(cum) +
+                                           ws_align(sizeof(long long) * (size_t)(max_entries(nseg, total_tokens) + 1)));
+    hipLaunchKernelGGL(build_varlen_schedule, dim3(1), dim3(1024), 0, stream, cu_seqlens, nseg, total_tokens, ws, H, cum);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(varlen_split_plan, dim3(1), dim3(64), 0, stream, ws, (const long long*)cum, H, slots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    VarlenArgs a;
+    a.q = static_cast<const bf16*>(q);
+    a.k = static_cast<const bf16*>(k);
+    a.v = static_cast<const bf16*>(v);
+    a.o = static_cast<bf16*>(out);
+    a.lse = lse;
+    a.cu = cu_seqlens;
+    a.ws = ws;
+    a.nseg = nseg;
+    a.H = H;
+    a.T = total_tokens;
+    a.c = log2e_scale(scale);
+    VarlenSplitArgs sp;
+    sp.cum = cum;
+    sp.part = part;
+    const long grid = max_entries(nseg, total_tokens) * H;
+    hipLaunchKernelGGL(attn_fwd_varlen_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_fwd_varlen_split_kernel, dim3((unsigned)slots), dim3(NT), 0, stream, a, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(varlen_merge_kernel, dim3((unsigned)(slots - 1) * 16), dim3(256), 0, stream, a, sp);
+    return hipGetLastError();
+}
+
 hipError_t launch_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                          const int32_t* cu_seqlens, int nseg, int H, int total_tokens, float scale,
                          void* workspace, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
     hipLaunchKernelGGL(build_varlen_schedule, dim3(1), dim3(1024), 0, stream, cu_seqlens, nseg,
-                       total_tokens, ws);
+                       total_tokens, ws, H, (long long*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     VarlenArgs a;

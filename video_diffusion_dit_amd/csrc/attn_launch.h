@@ -76,6 +76,14 @@ hipError_t launch_varlen(const void* q, const void* k, const void* v, void* out,
                          const int32_t* cu_seqlens, int nseg, int H, int total_tokens, float scale,
                          void* workspace, hipStream_t stream);
 
+// Packed forward with split-KV of the schedule's tail (slots >= 2 resident workgroups): the
+// plan is made on the device from the segment lengths; workspace >=
+// varlen_split_workspace_bytes(nseg, T, slots), 256-byte aligned.
+size_t varlen_split_workspace_bytes(int nseg, int total_tokens, int slots);
+hipError_t launch_varlen_split(const void* q, const void* k, const void* v, void* out, float* lse,
+                               const int32_t* cu_seqlens, int nseg, int H, int total_tokens, float scale, int slots,
+                               void* workspace, hipStream_t stream);
+
 // Prologue: per-head RMSNorm + interleaved 3-D RoPE on xq/xk (token-major [B,N,H,128] BF16)
 // into q/k ([B,H,N,128] BF16); xv -> v re-laid only (both may be null). N = F * Hp * Wp.
 hipError_t launch_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, void* k, void* v,
