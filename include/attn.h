@@ -14,8 +14,19 @@
  *
  * Numerics: QK^T in FP32 (BF16 MFMA), softmax statistics in FP32, probabilities
  * exp(x - m_ref) rounded to BF16 (round-to-nearest-even) before the PV product, where
- * m_ref is a per-row running reference never above the row's running maximum; the
- * normaliser l sums the FP32 probabilities; O = (PV accumulator) / l rounded to BF16 RNE.
+ * m_ref is a per-row reference the kernel moves only when some probability of a 64-key
+ * tile would make a lane's tile sum exceed 2^24 (then to about the row's running maximum
+ * plus 32 log2 units); the normaliser l sums the FP32 probabilities; O = (PV accumulator)
+ * / l rounded to BF16 RNE. Any reference gives the same softmax; this one keeps the work of
+ * moving it rare.
+ *
+ * Value range (every attention entry point): accepted probabilities never exceed 2^24, so
+ * before normalisation |O| < N * 2^24 * max|v| (N: keys of the sequence): FP32 holds it while
+ * N * max|v| < 2^104, e.g. max|v| < 2^87 at N = 2^17. Right after a move the probabilities
+ * are at most 2^-32, so keys whose weight is below 2^-94 of the row maximum's may fall under
+ * the FP32 normal range (their share of the output is far below its precision), and the
+ * products p * v keep full precision while max|v| >= 2^-94. Q and K: any finite BF16 values
+ * (logits up to the FP32 range; the tests use up to about +-1150).
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library keeps no
