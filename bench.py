@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "prologue": ("prologue_gfx950.hip",),
     "linear": ("linear_gfx950.hip",),
     "block_sparse": ("attn_fwd_gfx950.hip", "key_loop_idx_gfx950.inc", "block_route_gfx950.hip"),
+    "block_sparse_varlen": ("attn_fwd_gfx950.hip", "key_loop_idx_gfx950.inc", "block_route_gfx950.hip"),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -58,6 +59,8 @@ CALL_KERNELS = {
     "prologue": ("qk_prologue_kernel",),
     "linear": ("linear_out_kernel", "linear_kv_partial_kernel", "linear_kv_reduce_kernel"),
     "block_sparse": ("attn_fwd_block_sparse_kernel", "route_kernel", "pool_kernel", "lpt_order_kernel"),
+    "block_sparse_varlen": ("attn_fwd_block_sparse_varlen_kernel", "route_varlen_kernel", "pool_varlen_kernel",
+                            "tile_offsets_kernel", "lpt_order_kernel", "scale_count_kernel", "build_varlen_schedule"),
 }
 
 
@@ -250,7 +253,7 @@ def write_mfma_profile(args) -> int:
         f.write(f"grbm_gui_active_per_call: {grbm:.0f}\n")
         f.write(f"kernel_ms_per_call: {ns / 1e6:.4f}\n")
         f.write(f"counter_flops_per_call: {counter_flops:.6e}\n")
-        if kind == "block_sparse":   # kept pairs only: the ratio to the dense FLOP is the density
+        if kind.startswith("block_sparse"):   # kept pairs only: the ratio to the dense FLOP is the density
             f.write(f"dense_flops_per_call: {algorithmic:.6e}\n")
             f.write(f"counter_over_dense_flops: {counter_flops / algorithmic:.4f}\n")
         else:

@@ -240,8 +240,18 @@ struct DenseArgs {
     float c;
 };
 
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup x on XCD x % 8), each XCD with its
+// own L2. Workgroup x takes item xcd_item(x): the first 8*(n/8) items are dealt so that each XCD
+// walks a contiguous run of them (the query tiles of one or two heads, whose K/V its L2 then
+// shares); the last n % 8 keep their index. A bijection on [0, n).
+__device__ __forceinline__ int xcd_item(int x, int n) {
+    const int per = n / 8;
+    return x < 8 * per ? (x % 8) * per + x / 8 : x;
+}
+
 __global__ __launch_bounds__(NT, 1) void attn_fwd_dense_kernel(DenseArgs a) {
-    const int bh = blockIdx.x / a.ntq, qt = blockIdx.x - bh * a.ntq;
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int bh = item / a.ntq, qt = item - bh * a.ntq;
     const long base = (long)bh * a.N * D;
     attn_rows<false>(a.q + base, a.k + base, a.v + base, a.o + base, a.lse ? a.lse + (long)bh * a.N : nullptr,
                      D, a.N, qt * BM, a.c, 0, (a.N + BN - 1) / BN, nullptr);
