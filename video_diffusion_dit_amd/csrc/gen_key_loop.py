@@ -36,7 +36,7 @@ Register map (per lane):
     v[0:63], v[64:127]   S buffers: block (rb, kb) at 16*(2*kb + rb); P packed to BF16 in
                          place (pair j of a block at 8*(j/4) + j%4)
     v[128:143]           K fragment ring (4 x 4)       v[144:159]   V fragment ring (4 x 4)
-    v160..v175           m, l, half sums, mask limit, -inf, tile sums
+    v160..v175           m, l, partial sums, mask limit, -inf, tile sums (v168..v171 unused)
     v176..v199           temporaries (check, exact path)
     s[40:61]             resource cursors, counters, masks, return address; s61 keeps the
                          caller's M0 (the loads move it), which is restored at the end
@@ -73,8 +73,8 @@ S_BASE = (0, 64)
 KR, VR = 128, 144
 M = (160, 161)
 L = (162, 163)
-H1 = ((164, 165), (166, 167))      # first-half partial sums [rb][2]
-H2 = ((168, 169), (170, 171))      # second-half partial sums
+H1 = ((164, 165), (166, 167))      # the tile's partial sums [rb][2]: the first key half starts
+H2 = H1                            # them, the second half adds to the same registers
 KLIM_R = 172                       # key limit the exact path masks with (1000: no mask)
 NEG_INF = 173
 TS = (174, 175)                    # tile sums
@@ -327,7 +327,7 @@ def softmax_half(buf, kb, masked, klim, hs):
                     E.valu("v_cmp_lt_i32 vcc, %d, %s" % (kc, klim[0]), rd=klim[1], wr=VCC),
                     E.valu("v_cndmask_b32 %s, 0, %s, vcc" % (vr(x), vr(x)), rd=vset(x) | VCC, wr=vset(x))))
         h0, h1 = hs[rb]
-        if j == 0:
+        if j == 0 and kb == 0:   # the first pair of a tile starts its two partial sums
             st3 = [lambda E: E.valu("v_mov_b32 %s, %s" % (vr(h0), vr(a)), rd=vset(a), wr=vset(h0)),
                    lambda E: E.valu("v_mov_b32 %s, %s" % (vr(h1), vr(b)), rd=vset(b), wr=vset(h1))]
         else:
@@ -348,14 +348,15 @@ def softmax_half(buf, kb, masked, klim, hs):
     return stream
 
 
-def check_ops():
-    """Tile sums per row block (into TS) and the rescale condition (into S_C1/S_C2)."""
-    t0, t1 = TMP0, TMP0 + 1
+N_TILE_SUM_OPS = 2    # the VALU instructions of check_ops() that form the tile sums
 
+
+def check_ops():
+    """Tile sums per row block (into TS, from the two partial sums both key halves added to)
+    and the rescale condition (into S_C1/S_C2)."""
     def add(d, x, y):
         return lambda E: E.valu("v_add_f32 %s, %s, %s" % (vr(d), vr(x), vr(y)), rd=vset(x) | vset(y), wr=vset(d))
-    ops = [add(TS[0], *H1[0]), add(TS[1], *H1[1]), add(t0, *H2[0]), add(t1, *H2[1]),
-           add(TS[0], TS[0], t0), add(TS[1], TS[1], t1)]
+    ops = [add(TS[0], *H1[0]), add(TS[1], *H1[1])]
     for rb, sc in ((0, S_C1), (1, S_C2)):
         ops.append(lambda E, rb=rb, sc=sc: E.valu("v_cmp_nge_f32_e64 s[%d:%d], s%d, %s" % (sc, sc + 1, S_LIM, vr(TS[rb])),
                                                   rd=vset(TS[rb])))
@@ -624,7 +625,8 @@ def rare_path(E, X):
     for rb in range(2):
         E.valu("v_mul_f32 %s, %s, %s" % (vr(L[rb]), vr(L[rb]), vr(alpha[rb])), rd=vset(L[rb]) | vset(alpha[rb]), wr=vset(L[rb]))
     rescale_o(E, alpha)
-    for f in softmax_half(X, 0, True, KLIM_EXACT, H1) + softmax_half(X, 1, True, KLIM_EXACT, H2) + check_ops()[:6]:
+    for f in softmax_half(X, 0, True, KLIM_EXACT, H1) + softmax_half(X, 1, True, KLIM_EXACT, H2) + \
+            check_ops()[:N_TILE_SUM_OPS]:
         f(E)
     E.fresh()
     E.nop(12)
