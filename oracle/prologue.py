@@ -85,6 +85,24 @@ def qk_norm_rope(x_bits, grid, weight=None, eps: float = 1e-6, theta: float = 10
     return np.ascontiguousarray(out.transpose(0, 2, 1, 3))
 
 
+def qk_norm(x_bits, weight=None, eps: float = 1e-6, tokens=None) -> np.ndarray:
+    """Per-head RMSNorm of packed (THD) rows, [T, H, d] uint16 -> [T, H, d] float64 (or the
+    rows of `tokens` only): y_c = x_c / sqrt(mean_c x^2 + eps) * w_c.
+
+    The prologue of the packed (varlen) path. Page "PR #35728 report", key source excerpts:
+    the projected Q and K go through an RMSNorm before attention; page "PR #33702 report",
+    motivation: packed tokens reach the varlen forward in the THD layout, which is the
+    projection's own token-major layout. The pages give no positions for packed segments, so
+    no rotation is applied here (the packed workload's recipe is RMSNorm only); eps and the
+    per-head reading as for qk_norm_rope."""
+    x_bits = np.asarray(x_bits, np.uint16)
+    toks = slice(None) if tokens is None else np.asarray(tokens, np.int64)
+    x = bf16_bits_to_f64(x_bits[toks])
+    w = np.ones(x.shape[-1]) if weight is None else np.asarray(weight, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(np.float32(eps))) * w
+
+
 def v_head_major(v_bits) -> np.ndarray:
     """V is not transformed, only laid out [B, N, H, d] -> [B, H, N, d] (uint16, exact)."""
     return np.ascontiguousarray(np.asarray(v_bits, np.uint16).transpose(0, 2, 1, 3))

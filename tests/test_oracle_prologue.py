@@ -224,3 +224,59 @@ def test_selected_tokens_match_the_full_evaluation():
     full = qk_norm_rope(xb, (3, 4, 5))
     toks = [0, 7, 19, 20, 59]
     assert np.array_equal(qk_norm_rope(xb, (3, 4, 5), tokens=toks), full[:, :, toks])
+
+
+# ---------------------------------------------------------------- packed prologue (RMSNorm only)
+def test_qk_norm_brute_force_tiny():
+    """Scalar loops over a 3-token, 2-head packed batch: y = x / sqrt(mean x^2 + eps) * w."""
+    from oracle import qk_norm
+    xb = rand_bits((3, 2, 128), seed=21)
+    w = np.random.default_rng(22).uniform(0.5, 1.5, 128)
+    out = qk_norm(xb, weight=w, eps=EPS)
+    x = widen(xb)
+    for t in range(3):
+        for h in range(2):
+            row = [float(v) for v in x[t, h]]
+            r = 1.0 / math.sqrt(math.fsum(v * v for v in row) / 128.0 + EPS32)
+            for c in (0, 1, 64, 127):
+                assert out[t, h, c] == pytest.approx(row[c] * r * w[c], rel=1e-14, abs=1e-300)
+
+
+def test_qk_norm_closed_forms():
+    """RMS of each output row is sqrt(ms / (ms + eps)) without a weight; a row of +-a gives
+    +-a / sqrt(a^2 + eps); the weight scales each channel; rows are independent."""
+    from oracle import qk_norm
+    xb = rand_bits((5, 3, 128), seed=23, scale=3.0)
+    x = widen(xb)
+    y = qk_norm(xb, eps=EPS)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), np.sqrt(ms / (ms + EPS32)), rtol=1e-13)
+    a = 0.375                                          # exact in BF16
+    row = np.where(np.arange(128) % 3 == 0, -a, a)
+    yb = qk_norm(bits(row[None, None, :]), eps=EPS)[0, 0]
+    np.testing.assert_allclose(yb, row / math.sqrt(a * a + EPS32), rtol=1e-15)
+    w = np.linspace(0.25, 2.0, 128)
+    np.testing.assert_allclose(qk_norm(xb, weight=w, eps=EPS), y * w, rtol=1e-15)
+    x2 = xb.copy()
+    x2[2, 1] = bits(np.full(128, 7.0))
+    y2 = qk_norm(x2, eps=EPS)
+    mask = np.ones((5, 3), bool)
+    mask[2, 1] = False
+    np.testing.assert_array_equal(y2[mask], y[mask])
+
+
+def test_qk_norm_is_the_unrotated_prologue_of_token_zero():
+    """Position 0 turns no pair, so token 0 of the 3-D prologue is the plain RMSNorm."""
+    from oracle import qk_norm
+    xb = rand_bits((1, 6, 4, 128), seed=24)
+    dense = qk_norm_rope(xb, (1, 2, 3), eps=EPS)        # [1, H, N, d]
+    packed = qk_norm(xb[0], eps=EPS)                    # the same rows seen as THD [N, H, d]
+    np.testing.assert_allclose(packed[0], dense[0, :, 0], rtol=1e-15, atol=1e-300)
+    assert not np.allclose(packed[1], dense[0, :, 1])   # later tokens are rotated there
+
+
+def test_qk_norm_selected_tokens():
+    from oracle import qk_norm
+    xb = rand_bits((40, 2, 128), seed=25)
+    toks = np.array([0, 7, 39])
+    np.testing.assert_array_equal(qk_norm(xb, eps=EPS, tokens=toks), qk_norm(xb, eps=EPS)[toks])
