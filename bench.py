@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "dense": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
     "varlen": ("attn_fwd_gfx950.hip", "key_loop_gfx950.inc"),
     "prologue": ("prologue_gfx950.hip",),
+    "packed_prologue": ("prologue_gfx950.hip",),
     "linear": ("linear_gfx950.hip",),
     "block_sparse": ("attn_fwd_gfx950.hip", "key_loop_idx_gfx950.inc", "block_route_gfx950.hip"),
     "block_sparse_varlen": ("attn_fwd_gfx950.hip", "key_loop_idx_gfx950.inc", "block_route_gfx950.hip"),
@@ -57,6 +58,7 @@ CALL_KERNELS = {
     "varlen": ("attn_fwd_varlen_kernel", "build_varlen_schedule", "varlen_split_plan", "attn_fwd_varlen_split_kernel",
                "varlen_merge_kernel"),
     "prologue": ("qk_prologue_kernel",),
+    "packed_prologue": ("qk_norm_packed_kernel",),
     "linear": ("linear_out_kernel", "linear_kv_partial_kernel", "linear_kv_reduce_kernel"),
     "block_sparse": ("attn_fwd_block_sparse_kernel", "route_kernel", "pool_kernel", "lpt_order_kernel"),
     "block_sparse_varlen": ("attn_fwd_block_sparse_varlen_kernel", "route_varlen_kernel", "pool_varlen_kernel",
@@ -145,6 +147,8 @@ def write_traffic_profile(args) -> int:
     tokens = w.B * w.N if w.kind == "dense" else w.total_tokens
     if kind == "prologue":
         algorithmic = prologue_bytes(w.B, w.N, w.H, w.d)
+    elif kind == "packed_prologue":
+        algorithmic = float(w.total_tokens) * w.H * w.d * 2 * 4
     elif kind == "linear":
         algorithmic = linear_bytes(w.B, w.N, w.H, w.d)
     else:
@@ -377,6 +381,86 @@ def time_prologue(args, w, vd, dev) -> dict:
                              "ms": round(copy_ms, 4)}
     print(f"[bench] plain copy of the same bytes: {copy_ms:.4f} ms -> {nbytes / (copy_ms * 1e-3) / 1e9:.0f} GB/s",
           file=sys.stderr, flush=True)
+    del xs, outs
+    torch.cuda.empty_cache()
+    return rec
+
+
+def time_packed_norm(args, w, vd, dev) -> dict:
+    """Time the packed prologue (per-head RMSNorm of THD Q and K, in their own layout) at the
+    packed workload's tokens and heads, on seeded projected rows resident in HBM; check seeded
+    tokens against the oracle."""
+    import numpy as np
+    import torch
+
+    T = w.total_tokens
+    g = torch.Generator(device="cuda:0").manual_seed(20261202)
+    xs = [torch.randn((T, w.H, w.d), generator=g, device="cuda:0").to(torch.bfloat16) for _ in range(2)]
+    outs = [torch.empty_like(x) for x in xs]
+    lib = vd.load_library()
+
+    def call():
+        st = lib.attn_qk_norm_packed(xs[0].data_ptr(), xs[1].data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                                     None, None, T, w.H, w.d, 1e-6, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.prologue_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.prologue_steps)]
+    torch.cuda.synchronize()
+    for i in range(args.prologue_steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg = float(np.mean(ms))
+    nbytes = float(T) * w.H * w.d * 2 * 4          # Q and K rows read once and written once
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    rec = {
+        "kernel": "qk_norm_packed_kernel",
+        "what": "per-head RMSNorm of packed Q and K, THD [T,H,128] BF16 in and out (V untouched)",
+        "bound": "hbm",
+        "achieved": round(gbs, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic(w.name, "qk_norm_packed_kernel", False, "packed_prologue"),
+        "algorithmic_bytes": nbytes,
+        "ms": {"avg": round(avg, 4), "min": round(min(ms), 4), "max": round(max(ms), 4)},
+        "steps": args.prologue_steps,
+    }
+    print(f"[bench] packed prologue {args.prologue_steps} calls: {avg:.4f} ms -> {gbs:.0f} GB/s "
+          f"({100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f})", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        from oracle import bf16_bits_to_f64, bf16_faithful, qk_norm
+        toks = np.random.default_rng(1).choice(T, 4096, replace=False)
+        xq = xs[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        got = outs[0].view(torch.int16).cpu().numpy().view(np.uint16)[toks]
+        t1 = time.perf_counter()
+        exact = qk_norm(xq, tokens=toks)
+        cpu_s = time.perf_counter() - t1
+        m = bf16_faithful(bf16_bits_to_f64(got), exact)
+        rec["parity"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in m.items()}
+        sample_bytes = float(len(toks)) * w.H * w.d * 2 * 2             # Q rows read and written
+        rec["cpu_baseline"] = {"value": round(sample_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
+                               "cores": oracle_cores(), "kind": "oracle",
+                               "sample": f"Q of {len(toks)} seeded tokens x {w.H} heads (the GPU call also does K), "
+                                         f"FP64 NumPy, {cpu_s:.2f} s"}
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(5):
+        for x, o in zip(xs, outs):
+            o.copy_(x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 5
+    rec["copy_reference"] = {"what": "device-to-device copies of Q and K (same bytes read and written)",
+                             "achieved": round(nbytes / (copy_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                             "ms": round(copy_ms, 4)}
     del xs, outs
     torch.cuda.empty_cache()
     return rec
@@ -847,6 +931,8 @@ def main() -> int:
         result["block_skip"] = time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, avg_kernel_ms)
     if w.grid is not None and args.prologue_steps > 0:
         result["prologue"] = time_prologue(args, w, vd, dev)
+    elif w.kind == "varlen" and args.prologue_steps > 0:
+        result["prologue"] = time_packed_norm(args, w, vd, dev)
     if w.grid is not None and args.linear_steps > 0:
         result["linear_attention"] = time_linear(args, w, vd, dev)
     if args.calibrate_copy_mib > 0:

@@ -217,6 +217,25 @@ int attn_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, vo
                      int frames, int grid_h, int grid_w, float eps, float theta, void* stream);
 
 /*
+ * Prologue of the packed (varlen) path: per-head RMSNorm of the projected Q and K rows, rounded
+ * to BF16 once, in the THD layout attn_fwd_varlen reads -- which is the projection's own
+ * token-major layout, so nothing is re-laid and V needs no pass at all. Page "PR #35728 report",
+ * key source excerpts (RMSNorm on Q and K before attention); page "PR #33702 report",
+ * motivation (packed tokens reach the varlen forward in THD). The pages give no positions for
+ * packed segments, so no rotation is applied. Per token t and head h, in FP32:
+ *   y = x / sqrt(mean(x^2) + eps) * w                     (w = 1 when the weight is NULL)
+ *   xq, xk      : BF16 [T, H, d] inputs, contiguous.
+ *   q, k        : BF16 [T, H, d] outputs; q == xq and k == xk run in place, any other overlap
+ *                 (and any overlap with a weight) is ATTN_ERR_INVALID_ARG.
+ *   weight_q/k  : FP32 [d] RMSNorm weights or NULL (all ones). Device pointers.
+ *   total_tokens: T >= 0 (0 is a no-op); H >= 1; d must be 128 (ATTN_ERR_UNSUPPORTED otherwise).
+ *   eps         : finite, >= 0 (1e-6 in the workloads).
+ * Asynchronous on `stream`; allocates nothing. Returns an attn_status_t.
+ */
+int attn_qk_norm_packed(const void* xq, const void* xk, void* q, void* k, const float* weight_q,
+                        const float* weight_k, int total_tokens, int H, int d, float eps, void* stream);
+
+/*
  * SANA-Video linear attention (ReLU feature map, rotated Q/K in the numerator, un-rotated Q/K
  * in the normaliser), per batch b and head h over the N tokens:
  *   ksum = sum_m k_m;  den_n = q_n . ksum + eps;  kv = sum_m v_m k_rot_m^T (d x d);

@@ -35,6 +35,10 @@ def lib():
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_fwd_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+    lib.attn_qk_norm_packed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp]
+    lib.attn_fwd_varlen_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.attn_fwd_varlen_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_fwd_varlen_splitkv_workspace_bytes.restype = sz
     lib.attn_fwd_varlen_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attn_fwd_varlen_workspace_bytes.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -73,6 +77,7 @@ def test_header_declares_the_expected_api():
                  "attn_block_skip_use_dense", "attn_block_varlen_tiles", "attn_block_route_varlen",
                  "attn_block_route_varlen_workspace_bytes", "attn_fwd_block_sparse_varlen",
                  "attn_fwd_block_sparse_varlen_workspace_bytes", "attn_fwd_varlen_noalloc",
+                 "attn_fwd_varlen_splitkv", "attn_fwd_varlen_splitkv_workspace_bytes", "attn_qk_norm_packed",
                  "attn_status_string", "attn_last_error", "attn_tile_rows", "attn_tile_keys"):
         assert name in fns, fns
 
@@ -266,6 +271,40 @@ def prologue(lib, xq=XQ, xk=XK, xv=XV, q=PQ, k=PK, v=PV, wq=None, wk=None, B=1, 
 def test_prologue_validation(lib, kw, code):
     assert prologue(lib, **kw) == code
     assert lib.attn_last_error().decode()
+
+
+def qk_norm_packed(lib, xq=XQ, xk=XK, q=PQ, k=PK, wq=None, wk=None, T=300, H=4, d=128, eps=1e-6):
+    return lib.attn_qk_norm_packed(xq, xk, q, k, wq, wk, T, H, d, eps, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(xq=None), INVALID), (dict(k=None), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
+    (dict(d=0), INVALID), (dict(d=64), UNSUPPORTED), (dict(eps=-1.0), INVALID), (dict(eps=math.inf), INVALID),
+    (dict(T=0), OK),                                                       # empty batch: no-op
+    (dict(q=XQ + 256), INVALID),                                           # partial overlap with its input
+    (dict(q=XK), INVALID), (dict(k=XQ), INVALID), (dict(k=PQ + 512), INVALID),
+    (dict(wk=PK + 64), INVALID),                                           # weight inside an output
+    (dict(T=1 << 24, H=1 << 10), UNSUPPORTED),                             # more rows than one launch indexes
+])
+def test_qk_norm_packed_validation(lib, kw, code):
+    assert qk_norm_packed(lib, **kw) == code
+
+
+def test_varlen_splitkv_validation(lib):
+    wsb = lib.attn_fwd_varlen_splitkv_workspace_bytes(3, 2, 300, 128, 16)
+    assert wsb >= lib.attn_fwd_varlen_workspace_bytes(3, 2, 300)
+    assert lib.attn_fwd_varlen_splitkv_workspace_bytes(3, 2, 300, 128, 1) == lib.attn_fwd_varlen_workspace_bytes(3, 2, 300)
+    assert lib.attn_fwd_varlen_splitkv_workspace_bytes(3, 2, 300, 64, 16) == 0
+    call = lambda **kw: lib.attn_fwd_varlen_splitkv(Q, K, V, kw.get("o", O), None, kw.get("cu", CU), 3, 2, 300,
+                                                    kw.get("d", 128), 0.088, kw.get("slots", 16), kw.get("ws", WS),
+                                                    kw.get("wsb", wsb), None)
+    assert call(cu=None) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(slots=1 << 20) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=wsb - 1) == WORKSPACE
+    assert call(ws=WS + 8) == WORKSPACE
+    assert call(o=V) == INVALID
 
 
 def test_python_prologue_guards_without_gpu():

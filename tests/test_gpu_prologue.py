@@ -114,3 +114,52 @@ def test_video_720p_two_heads_sampled_tokens(vd):
     for name, x, t in (("q", xq, q), ("k", xk, k)):
         check_qk(bits_of(t)[:, :, toks], qk_norm_rope(x, grid, tokens=toks), f"{name} 720p H2 sampled")
     assert np.array_equal(bits_of(v), v_head_major(xv))
+
+
+# ---- the packed (varlen) prologue: per-head RMSNorm of THD rows, no re-layout, no rotation
+
+def thd_rows(T, H, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    f = (rng.standard_normal((T, H, 128)) * scale).astype(np.float32)
+    t = torch.from_numpy(f).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("T,H,weighted,in_place", [
+    (1, 1, False, False),         # 2 rows: one group, half empty
+    (5, 3, True, False),          # 30 rows: the last group straddles Q and K
+    (257, 24, False, True),       # in place
+    (1000, 2, True, True),
+])
+def test_packed_norm_in_full(vd, T, H, weighted, in_place):
+    from oracle import qk_norm
+    xq, xk = thd_rows(T, H, seed=T + H), thd_rows(T, H, seed=T + H + 1, scale=3.0)
+    wq = wk = None
+    if weighted:
+        rng = np.random.default_rng(H)
+        wq = torch.from_numpy(rng.uniform(0.5, 1.5, 128).astype(np.float32)).to("cuda:0")
+        wk = torch.from_numpy(rng.uniform(0.5, 1.5, 128).astype(np.float32)).to("cuda:0")
+    dq, dk = dev(xq), dev(xk)
+    q, k = vd.qk_norm_packed(dq, dk, weight_q=wq, weight_k=wk, in_place=in_place)
+    torch.cuda.synchronize()
+    if in_place:
+        assert q.data_ptr() == dq.data_ptr() and k.data_ptr() == dk.data_ptr()
+    wq_h = None if wq is None else wq.cpu().numpy()
+    wk_h = None if wk is None else wk.cpu().numpy()
+    check_qk(bits_of(q), qk_norm(xq, weight=wq_h), f"packed q T{T} H{H}")
+    check_qk(bits_of(k), qk_norm(xk, weight=wk_h), f"packed k T{T} H{H}")
+
+
+def test_packed_norm_workload_size(vd):
+    """The packed workload's token count and heads (38048 x 24), seeded tokens checked,
+    including the first and the last."""
+    from oracle import qk_norm
+    from workloads import WORKLOADS
+    w = WORKLOADS["packed_varlen"]
+    T = w.total_tokens
+    xq, xk = thd_rows(T, w.H, seed=31), thd_rows(T, w.H, seed=32)
+    q, k = vd.qk_norm_packed(dev(xq), dev(xk))
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(33).choice(T, 256, replace=False)]))
+    check_qk(bits_of(q)[toks], qk_norm(xq, tokens=toks), f"packed q {T}x{w.H} ({toks.size} tokens)")
+    check_qk(bits_of(k)[toks], qk_norm(xk, tokens=toks), f"packed k {T}x{w.H} ({toks.size} tokens)")

@@ -8,12 +8,13 @@ from .attention import (AttnError, attn_fwd, attn_fwd_block_sparse, attn_fwd_blo
                         attn_fwd_varlen_noalloc,
                         block_list_stride, block_route, block_route_varlen, block_skip_attention,
                         block_skip_attention_varlen, block_skip_use_dense,
-                        check_cu_seqlens, linear_attention, load_library, qk_prologue, splitkv_workspace_bytes,
+                        check_cu_seqlens, linear_attention, load_library, qk_norm_packed, qk_prologue, splitkv_workspace_bytes,
                         try_attn_fwd, varlen_list_shapes, varlen_tile_offsets, varlen_workspace_bytes)
 
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_block_sparse", "attn_fwd_block_sparse_varlen", "attn_fwd_varlen",
            "attn_fwd_varlen_noalloc",
            "block_list_stride", "block_route", "block_route_varlen", "block_skip_attention",
            "block_skip_attention_varlen", "block_skip_use_dense",
-           "check_cu_seqlens", "linear_attention", "load_library", "qk_prologue", "splitkv_workspace_bytes",
+           "check_cu_seqlens", "linear_attention", "load_library", "qk_norm_packed", "qk_prologue",
+           "splitkv_workspace_bytes",
            "try_attn_fwd", "varlen_list_shapes", "varlen_tile_offsets", "varlen_workspace_bytes"]

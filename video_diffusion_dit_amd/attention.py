@@ -82,6 +82,8 @@ def load_library() -> ctypes.CDLL:
         lib.attn_qk_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          f32, f32, vp]
         lib.attn_qk_prologue.restype = i32
+        lib.attn_qk_norm_packed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp]
+        lib.attn_qk_norm_packed.restype = i32
         lib.attn_linear_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, sz, vp]
         lib.attn_linear_fwd.restype = i32
         lib.attn_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -388,6 +390,32 @@ def qk_prologue(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor | None = No
                               float(eps), float(theta), _stream_handle(xq.device))
     _raise_for(lib, st)
     return tuple(out)
+
+
+def qk_norm_packed(xq: torch.Tensor, xk: torch.Tensor, *, weight_q: torch.Tensor | None = None,
+                   weight_k: torch.Tensor | None = None, eps: float = 1e-6, in_place: bool = False):
+    """Per-head RMSNorm of packed Q and K: xq, xk BF16 [T, H, 128] (THD, the projection's own
+    layout, which attn_fwd_varlen reads) -> (q, k) BF16 [T, H, 128], rounded once. Weights: FP32
+    [128] or None. in_place writes into xq and xk."""
+    for t in (xq, xk):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError("xq and xk must be bfloat16 tensors")
+    if xq.dim() != 3 or xq.shape != xk.shape or xq.shape[-1] != 128:
+        raise ValueError("xq and xk must be [T, H, 128] with the same shape")
+    if not (xq.is_contiguous() and xk.is_contiguous()) or xq.device != xk.device:
+        raise ValueError("xq and xk must be contiguous and on one device")
+    for w in (weight_q, weight_k):
+        if w is not None and (w.dtype != torch.float32 or w.shape != (128,) or not w.is_contiguous()
+                              or w.device != xq.device):
+            raise ValueError("weights must be contiguous float32 [128] tensors on the inputs' device")
+    T, H, d = xq.shape
+    q, k = (xq, xk) if in_place else (torch.empty_like(xq), torch.empty_like(xk))
+    lib = load_library()
+    with torch.cuda.device(xq.device):
+        st = lib.attn_qk_norm_packed(_ptr(xq), _ptr(xk), _ptr(q), _ptr(k), _ptr(weight_q), _ptr(weight_k), T, H, d,
+                                     float(eps), _stream_handle(xq.device))
+    _raise_for(lib, st)
+    return q, k
 
 
 def linear_attention(q: torch.Tensor, k: torch.Tensor, q_rot: torch.Tensor, k_rot: torch.Tensor,

@@ -182,6 +182,31 @@ int attn_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, vo
                                                     static_cast<hipStream_t>(stream)));
 }
 
+int attn_qk_norm_packed(const void* xq, const void* xk, void* q, void* k, const float* weight_q,
+                        const float* weight_k, int total_tokens, int H, int d, float eps, void* stream) {
+    g_last_error[0] = '\0';
+    if (xq == nullptr || xk == nullptr || q == nullptr || k == nullptr)
+        return fail(ATTN_ERR_INVALID_ARG, "xq, xk, q and k must be non-null device pointers");
+    if (total_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (H <= 0) return fail(ATTN_ERR_INVALID_ARG, "H must be >= 1");
+    if (d <= 0) return fail(ATTN_ERR_INVALID_ARG, "d must be >= 1");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "only head dimension 128 is supported");
+    if (!isfinite(eps) || eps < 0.f) return fail(ATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const long long elems = product(total_tokens, H, d, 1);
+    if (elems < 0 || product(total_tokens, H, 1, 1) > INT_MAX) return fail(ATTN_ERR_UNSUPPORTED, "tensor too large");
+    if (total_tokens == 0) return ATTN_OK;
+    const size_t bytes = (size_t)elems * 2;
+    // in place is allowed (q == xq, k == xk); any other overlap is not
+    if ((q != xq && overlaps(q, bytes, xq, bytes)) || overlaps(q, bytes, xk, bytes) || overlaps(q, bytes, k, bytes) ||
+        (k != xk && overlaps(k, bytes, xk, bytes)) || overlaps(k, bytes, xq, bytes))
+        return fail(ATTN_ERR_INVALID_ARG, "an output overlaps another tensor (only q == xq and k == xk may share memory)");
+    if (overlaps(q, bytes, weight_q, 512) || overlaps(q, bytes, weight_k, 512) || overlaps(k, bytes, weight_q, 512) ||
+        overlaps(k, bytes, weight_k, 512))
+        return fail(ATTN_ERR_INVALID_ARG, "an output overlaps a weight");
+    return hip_status(attn_impl::launch_qk_norm_packed(xq, xk, q, k, weight_q, weight_k, total_tokens, H, eps,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_linear_workspace_bytes(int B, int N, int H, int d) {
     if (B <= 0 || N <= 0 || H <= 0 || d != 128 || product(B, N, H, d) < 0) return 0;
     return attn_impl::linear_workspace_bytes(B, N, H);

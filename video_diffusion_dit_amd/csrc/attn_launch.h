@@ -90,6 +90,11 @@ hipError_t launch_qk_prologue(const void* xq, const void* xk, const void* xv, vo
                               const float* wq, const float* wk, int B, int N, int H, int Hp, int Wp,
                               float eps, float theta, hipStream_t stream);
 
+// Packed prologue: per-head RMSNorm of THD [T,H,128] BF16 Q and K rows into THD outputs (q == xq
+// and k == xk allowed).
+hipError_t launch_qk_norm_packed(const void* xq, const void* xk, void* q, void* k, const float* wq, const float* wk,
+                                 int T, int H, float eps, hipStream_t stream);
+
 // Linear attention: q, k (ReLU'd), q_rot, k_rot, v, out BF16 [B,N,H,128] token-major;
 // workspace >= linear_workspace_bytes(B, N, H), 256-byte aligned.
 size_t linear_workspace_bytes(int B, int N, int H);

@@ -167,9 +167,83 @@ __global__ __launch_bounds__(WAVES * 64) void qk_prologue_kernel(PrologueArgs a)
     }
 }
 
+// Packed (THD) prologue: per-head RMSNorm of the Q and K rows, which stay in their token-major
+// layout -- the layout the packed attention reads -- with no rotation (the pages give no
+// positions for packed segments). Rows 0 .. TH-1 are Q, TH .. 2TH-1 K; each 16-lane group
+// normalises 4 consecutive rows, all loads issued before any store, so q == xq (and
+// k == xk) works in place.
+struct NormArgs {
+    const bf16* xq;
+    const bf16* xk;
+    bf16* q;
+    bf16* k;
+    const float* wq;
+    const float* wk;
+    long rows;                  // T * H
+    float eps;
+};
+
+__global__ __launch_bounds__(256) void qk_norm_packed_kernel(NormArgs a) {
+    const int j = threadIdx.x & 15;
+    const long r0 = ((long)blockIdx.x * 16 + (threadIdx.x >> 4)) * ROWS;
+    if (r0 >= 2 * a.rows) return;   // a whole group (16 lanes) leaves together
+    float wq[8], wk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        wq[i] = a.wq ? a.wq[8 * j + i] : 1.0f;
+        wk[i] = a.wk ? a.wk[8 * j + i] : 1.0f;
+    }
+    f32x8 x[ROWS];
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u) {
+        const long r = r0 + u;
+        if (r < 2 * a.rows) x[u] = load_row((r < a.rows ? a.xq + r * D : a.xk + (r - a.rows) * D) + 8 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < ROWS; ++u) {
+        const long r = r0 + u;
+        if (r >= 2 * a.rows) continue;
+        const bool isq = r < a.rows;
+        const float* w = isq ? wq : wk;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(x[u][i], x[u][i], ss);
+        ss += __shfl_xor(ss, 1, 16);
+        ss += __shfl_xor(ss, 2, 16);
+        ss += __shfl_xor(ss, 4, 16);
+        ss += __shfl_xor(ss, 8, 16);
+        const float rn = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+        u32x4 out;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const bf16 be = (bf16)(x[u][2 * p] * rn * w[2 * p]), bo = (bf16)(x[u][2 * p + 1] * rn * w[2 * p + 1]);
+            out[p] = (unsigned)__builtin_bit_cast(unsigned short, be) |
+                     ((unsigned)__builtin_bit_cast(unsigned short, bo) << 16);
+        }
+        *reinterpret_cast<u32x4*>((isq ? a.q + r * D : a.k + (r - a.rows) * D) + 8 * j) = out;
+    }
+}
+
 }  // namespace
 
 namespace attn_impl {
+
+hipError_t launch_qk_norm_packed(const void* xq, const void* xk, void* q, void* k, const float* wq, const float* wk,
+                                 int T, int H, float eps, hipStream_t stream) {
+    NormArgs a;
+    a.xq = static_cast<const bf16*>(xq);
+    a.xk = static_cast<const bf16*>(xk);
+    a.q = static_cast<bf16*>(q);
+    a.k = static_cast<bf16*>(k);
+    a.wq = wq;
+    a.wk = wk;
+    a.rows = (long)T * H;
+    a.eps = eps;
+    const long grid = (2 * a.rows + 16 * ROWS - 1) / (16 * ROWS);
+    hipLaunchKernelGGL(qk_norm_packed_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 
 hipError_t launch_qk_prologue(const void* xq, const void* xk, const void* xv, void* q, void* k, void* v,
                               const float* wq, const float* wk, int B, int N, int H, int Hp, int Wp,
