@@ -16,9 +16,13 @@
  * exp(x - m_ref) rounded to BF16 (round-to-nearest-even) before the PV product, where
  * m_ref is a per-row reference the kernel moves only when some probability of a 64-key
  * tile would make a lane's tile sum exceed 2^24 (then to about the row's running maximum
- * plus 32 log2 units); the normaliser l sums the FP32 probabilities; O = (PV accumulator)
- * / l rounded to BF16 RNE. Any reference gives the same softmax; this one keeps the work of
- * moving it rare.
+ * plus 32 log2 units); l sums the FP32 probabilities and gives the LSE. O = (PV
+ * accumulator) / (l + C) rounded to BF16 RNE, where C adds, for the tiles that hold more
+ * than half of a lane's running sum (or move the reference), the difference between the
+ * sum of their BF16 probabilities and their FP32 sum: the keys that dominate a row are
+ * normalised by the same BF16 values their products used, so their rounding cancels (a
+ * row dominated by one key returns that key's v up to the final rounding). Any reference
+ * gives the same softmax; this one keeps the work of moving it rare.
  *
  * Value range (every attention entry point): accepted probabilities never exceed 2^24, so
  * before normalisation |O| < N * 2^24 * max|v| (N: keys of the sequence): FP32 holds it while

@@ -152,6 +152,42 @@ def mfma_violations(asm_lines):
     return bad
 
 
+def dot_violations(asm_lines):
+    """A v_dot2c_f32_bf16 result read by any other instruction (or by a DOT as a multiplicand)
+    fewer than 3 wait states later, along the straight-line code."""
+    ins = [("<label>", []) if l.endswith(":") else parse(l) for l in asm_lines]
+    bad = []
+    for k, (op, ops) in enumerate(ins):
+        if not op.startswith("v_dot2"):
+            continue
+        dst = regs(ops[0])
+        ws = 0
+        for j in range(k + 1, min(k + 8, len(ins))):
+            qop, qops = ins[j]
+            if qop == "<label>" or is_block_end(qop):
+                break
+            if qop.startswith("v_dot2c"):
+                srcs = regs(qops[1]) | regs(qops[2])      # multiplicands; the accumulator is the dst
+            else:
+                srcs = set()
+                for t in qops[1:]:
+                    srcs |= regs(t)
+            if srcs & dst and ws < 3:
+                bad.append(("dot->read", k, qop))
+            ws += ws_of(qop, qops)
+            if ws >= 3:
+                break
+    return bad
+
+
+def test_dot_wait_states(asm_lines):
+    assert dot_violations(asm_lines) == []
+    # not vacuous: a read right after a DOT is reported
+    k = next(i for i, l in enumerate(asm_lines) if l.startswith("v_dot2c_f32_bf16"))
+    dst = parse(asm_lines[k])[1][0]
+    assert dot_violations(asm_lines[:k + 1] + ["v_add_f32 v199, %s, %s" % (dst, dst)] + asm_lines[k + 1:])
+
+
 def test_lds_results_waited(asm_lines):
     assert lds_violations(asm_lines) == []
 
@@ -297,10 +333,11 @@ def test_rebase_arithmetic_is_an_exact_power_of_two_shift(gen):
 def test_rebase_path_leaves_the_state_alone_until_it_commits(gen, asm_lines):
     """Each rebase path reads the packed probabilities and may still hand the tile to the full
     path (an inf/NaN maximum): up to that branch it writes only its temporaries, never m, l,
-    the tile sums, P or O, so the full path starts from the state the check saw."""
+    the correction, the tile sums, P or O, so the full path starts from the state the check
+    saw."""
     owned = {("v", r) for r in range(gen.TMP0, gen.TMP0 + 24)}
     for X in range(2):
-        start = asm_lines.index(".Lrare%d_%%=:" % X)
+        start = asm_lines.index(".Lmove%d_%%=:" % X)
         branch = next(i for i in range(start, len(asm_lines))
                       if asm_lines[i].startswith("s_cbranch_scc1 .Lfull%d_" % X))
         assert asm_lines[branch + 1:].index(".Lfull%d_%%=:" % X) > 0
@@ -310,7 +347,8 @@ def test_rebase_path_leaves_the_state_alone_until_it_commits(gen, asm_lines):
                 continue
             dst = regs(ops[0])
             assert dst <= owned or op.startswith("v_cmp"), line
-        # after the branch the path moves m, l, the tile sums, every packed P register and O
+        # after the branch the path moves m, l, the correction, the tile sums, every packed P
+        # register and O, then goes on to the tile's correction
         tail = asm_lines[branch:asm_lines.index(".Lfull%d_%%=:" % X)]
         written = set()
         for line in tail:
@@ -318,7 +356,51 @@ def test_rebase_path_leaves_the_state_alone_until_it_commits(gen, asm_lines):
             if ops and not op.startswith("s_"):
                 written |= regs(ops[0])
         for rb in range(2):
-            assert ("v", gen.M[rb]) in written and ("v", gen.L[rb]) in written and ("v", gen.TS[rb]) in written
+            assert {("v", gen.M[rb]), ("v", gen.L[rb]), ("v", gen.TS[rb]), ("v", gen.C[rb])} <= written
             assert {("v", r) for r in gen.packed_p(X, rb)} <= written
         assert {("a", i) for i in range(128)} <= written
-        assert tail[-1] == "s_setpc_b64 s[54:55]"
+        assert tail[-1] == "s_branch .Lfix%d_%%=" % X
+
+
+def test_slow_path_entry_and_correction(gen, asm_lines):
+    """The slow-path entry only tests whether a new reference is needed (a tile sum above 2^24
+    or not a number) before it branches to the rebase; the correction that every slow path
+    ends in reads the packed probabilities of its own S buffer and the tile sums, writes only
+    its four temporaries and C, and returns; the rebase and the full path both end in it."""
+    owned = {("v", gen.TMP0 + i) for i in range(2, 6)} | {("v", c) for c in gen.C}
+    for X in range(2):
+        start = asm_lines.index(".Lrare%d_%%=:" % X)
+        fix = asm_lines.index(".Lfix%d_%%=:" % X)
+        entry = asm_lines[start + 1:fix]
+        assert entry[-1] == "s_cbranch_scc1 .Lmove%d_%%=" % X
+        assert [l for l in entry if l.startswith("v_")] == ["v_cmp_nge_f32 vcc, s%d, v%d" % (gen.S_LIM, t)
+                                                            for t in gen.TS]
+        end = next(i for i in range(fix, len(asm_lines)) if asm_lines[i].startswith("s_setpc_b64"))
+        body = asm_lines[fix + 1:end]
+        read, written = set(), set()
+        for line in body:
+            op, ops = parse(line)
+            if op.startswith("s_") or not ops:
+                continue
+            written |= regs(ops[0])
+            for t in ops[1:]:
+                read |= regs(t)
+        assert written <= owned, written - owned
+        packed = {("v", r) for rb in range(2) for r in gen.packed_p(X, rb)}
+        assert packed <= read and read <= packed | owned | {("v", t) for t in gen.TS}
+        assert sum(l.startswith("v_dot2c_f32_bf16") for l in body) == 32
+        assert all("s%d" % gen.S_ONES in l for l in body if l.startswith("v_dot2"))
+        assert sum(l == "s_branch .Lfix%d_%%=" % X for l in asm_lines) == 2
+    assert any(l == "s_mov_b32 s%d, 0x3f803f80" % gen.S_ONES for l in asm_lines)
+
+
+def test_check_limit_follows_l(gen, asm_lines):
+    """The check compares each tile sum with the lane's own limit, which is set to
+    min(l, 2^24) right after every update of l."""
+    for i, line in enumerate(asm_lines):
+        if line.startswith("v_add_f32 v%d, v%d, v%d" % (gen.L[0], gen.L[0], gen.TS[0])):
+            nxt = asm_lines[i + 1:i + 4]
+            for rb in range(2):
+                assert "v_min_f32 v%d, s%d, v%d" % (gen.LIM[rb], gen.S_LIM, gen.L[rb]) in nxt, nxt
+    cmps = [l for l in asm_lines if l.startswith("v_cmp_nge_f32_e64")]
+    assert cmps and all(re.match(r"v_cmp_nge_f32_e64 s\[\d+:\d+\], v(170|171), v(174|175)$", l) for l in cmps), cmps[:2]

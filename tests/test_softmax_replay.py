@@ -2,15 +2,19 @@
 
 The kernel keeps, per query row, a reference m (log2 units of the scaled logit) and takes the
 probabilities of each 64-key tile as p = exp2(x - m) in FP32, rounded to BF16 for the PV
-product, with the normaliser l summing the FP32 p. It keeps m until some lane's tile sum
-exceeds 2^24; then
+product, with l summing the FP32 p per lane. A tile whose lane sum exceeds the lane's limit
+min(l, 2^24) takes the slow path. It keeps m until some lane's tile sum exceeds 2^24; then
   * rebase (fast exact path): if every BF16 p of the wave is finite, the row's largest BF16 p
     has binary exponent e and m moves up by k = max(e + 1 + 32, 0); P (BF16, exponent field
     minus k, flushed below 2^-126), the tile sums, l and O scale by 2^-k exactly;
   * full exact path: otherwise (the first tile, where m = -inf, or a p beyond the FP32
     range), m = max(row max + 32, m), O and l scale by exp2(m_old - m), and P and the tile
     sums are recomputed.
-Both keep the softmax exact in exact arithmetic; the replay shows they do in FP32/BF16 too,
+Every slow-path tile (with or without a move) then adds (sum of its BF16 p) - (its FP32 tile
+sum) to a correction C per lane, and O is divided by l + C, while the LSE takes l: the keys
+that end with half or more of a lane's weight sit in such tiles, so the normaliser of a row's
+dominant keys is the sum of exactly the BF16 values their products used.
+Both moves keep the softmax exact in exact arithmetic; the replay shows they do in FP32/BF16 too,
 on the outlier workload whose rows climb hundreds of log2 units (the rebase shifts reach
 k = 161 there), to the same bar as the GPU (rel-L2 <= 5e-3, max-abs <= 2e-2, |dLSE| <= 1e-3).
 
@@ -48,19 +52,21 @@ def lane_of_key():
     return (np.arange(64) % 16) // 8
 
 
-def replay(x, v, n, scale_mode="ldexp", divisor="fp32"):
+def replay(x, v, n, scale_mode="ldexp", divisor="corrected"):
     """Rows of one wave: x [R, N] FP32 scores in log2 units (scale*log2(e)*q.k), v [N, d] float64.
-    Returns o [R, d], lse [R] (natural log), the counts of rebase and full moves, and O before
-    normalisation. divisor: "fp32" (the kernel: O / l) or "bf16" (O divided by the sum of the
-    BF16 probabilities, a measured alternative)."""
+    Returns o [R, d], lse [R] (natural log), the counts of rebase moves, full moves and
+    slow-path tiles, and O before normalisation. divisor: "corrected" (the kernel: O / (l + C)),
+    "fp32" (O / l, without the correction) or "bf16" (O divided by the sum of every BF16
+    probability, which costs a second sum on every tile)."""
     R, N = x.shape
     ntk = -(-N // 64)
     lane = lane_of_key()
     m = np.full(R, -np.inf, f32)
     l = np.zeros((R, 2), f32)
+    cor = np.zeros((R, 2), f32)
     lb = np.zeros(R, f32)
     O = np.zeros((R, v.shape[1]))
-    moves = {"rebase": 0, "full": 0}
+    moves = {"rebase": 0, "full": 0, "slow": 0}
     for t in range(ntk):
         xs = np.full((R, 64), -np.inf, f32)
         w = min(64, n - 64 * t)
@@ -78,7 +84,10 @@ def replay(x, v, n, scale_mode="ldexp", divisor="fp32"):
         p = probs(m)
         ts = sums(p)
         pb = bf16(p)
-        if not np.all(ts <= LIMIT):                       # the wave leaves the common path
+        lim = np.minimum(l, LIMIT)
+        slow = not np.all(ts <= lim)                      # the wave leaves the common path
+        moves["slow"] += slow
+        if slow and not np.all(ts <= LIMIT):              # and needs a new reference
             if np.all(np.isfinite(pb)):
                 moves["rebase"] += 1
                 e = np.frexp(np.maximum(pb.max(axis=1), 0.0))[1] - 1        # binary exponent
@@ -88,11 +97,13 @@ def replay(x, v, n, scale_mode="ldexp", divisor="fp32"):
                 if scale_mode == "ldexp":
                     s = 2.0 ** -k.astype(np.float64)                         # exact scaling
                     ts, l = (ts * s[:, None]).astype(f32), (l * s[:, None]).astype(f32)
+                    cor = (cor * s[:, None]).astype(f32)
                     lb = (lb * s).astype(f32)
                     O *= s[:, None]
                 else:                                                        # the FP32 factor 2^-k
                     alpha = np.where(k <= 149, 2.0 ** -k.astype(np.float64), 0.0).astype(f32)
                     ts, l = (ts * alpha[:, None]).astype(f32), (l * alpha[:, None]).astype(f32)
+                    cor = (cor * alpha[:, None]).astype(f32)
                     lb = (lb * alpha).astype(f32)
                     O *= alpha[:, None]
                 m = (m + k.astype(f32)).astype(f32)
@@ -104,16 +115,21 @@ def replay(x, v, n, scale_mode="ldexp", divisor="fp32"):
                     alpha = np.where(np.isinf(m), f32(0), np.exp2((m - mn).astype(f32))).astype(f32)
                 O *= alpha[:, None]
                 l = (l * alpha[:, None]).astype(f32)
+                cor = (cor * alpha[:, None]).astype(f32)
                 lb = (lb * alpha).astype(f32)
                 m = mn
                 p = probs(m)
                 ts = sums(p)
                 pb = bf16(p)
+        if slow:   # the correction: lane sums of the BF16 probabilities minus the FP32 tile sums
+            bsum = np.stack([pb[:, lane == g].sum(axis=1) for g in (0, 1)], axis=1).astype(f32)
+            cor = (cor + (bsum - ts).astype(f32)).astype(f32)
         l = (l + ts).astype(f32)
         lb = (lb + pb.sum(axis=1)).astype(f32)
         O += pb[:, :w] @ v[64 * t:64 * t + w]
     ltot = l.sum(axis=1, dtype=f32).astype(np.float64)
-    div = {"bf16": lb.astype(np.float64), "fp32": ltot}[divisor]
+    ctot = cor.sum(axis=1, dtype=f32).astype(np.float64)
+    div = {"bf16": lb.astype(np.float64), "fp32": ltot, "corrected": ltot + ctot}[divisor]
     return O / div[:, None], (m.astype(np.float64) + np.log2(ltot)) * math.log(2), moves, O
 
 
@@ -139,11 +155,27 @@ def stress_wave(stress, b, h, q0):
 def test_replay_meets_the_bar_on_the_outlier_workload(stress, b, h, q0):
     x, v, o_ref, lse_ref = stress_wave(stress, b, h, q0)
     o, lse, moves, _ = replay(x, v, x.shape[1])
-    m = compare(o, o_ref, lse, lse_ref)
+    m = compare(bf16(o), o_ref, lse, lse_ref)
     print(f"[replay] b={b} h={h} rows {q0}..: {moves}, rel_l2 {m['rel_l2']:.2e}, max_abs {m['max_abs']:.2e}, "
           f"lse {m['lse_max_abs']:.2e}")
     assert moves["rebase"] > 0 and moves["full"] >= 1
     assert m["ok"], m
+
+
+@pytest.mark.parametrize("b,h,q0", [(0, 0, 2304), (1, 9, 4928), (1, 9, 6656), (1, 9, 7872)])
+def test_correction_removes_the_max_abs_tail(stress, b, h, q0):
+    """Waves of the outlier workload where a row's output, rounded to BF16, misses the oracle by
+    more than the 2e-2 bar when O is divided by the FP32 sum l alone (a few keys dominate such
+    rows, and the BF16 rounding of their probabilities, up to 2^-8 relative, adds to the half
+    ulp of the output's own rounding); dividing by l + C, as the kernel does, brings every row
+    of the wave to within 0.0158 with the LSE unchanged."""
+    x, v, o_ref, lse_ref = stress_wave(stress, b, h, q0)
+    plain, lse_p, _, _ = replay(x, v, x.shape[1], divisor="fp32")
+    o, lse, moves, _ = replay(x, v, x.shape[1])
+    assert np.abs(bf16(plain) - o_ref).max() > 2e-2
+    assert np.abs(bf16(o) - o_ref).max() <= 0.0158
+    np.testing.assert_array_equal(lse, lse_p)
+    assert moves["slow"] > moves["rebase"] + moves["full"]     # tiles corrected without a move
 
 
 def test_scaling_by_an_fp32_factor_fails_where_shifts_pass_149(stress):

@@ -99,15 +99,18 @@ __device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) 
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Row stride (floats) of a partial result: 128 unnormalised O values, then m_ref and l.
+// Row stride (floats) of a partial result: 128 unnormalised O values, then m_ref, l (the FP32
+// sum of the probabilities) and the correction that makes l + correction the sum of the BF16
+// probabilities O was accumulated with on the tiles that hold a lane's dominant keys.
 constexpr int PART_STRIDE = 132;
 constexpr size_t PART_BYTES = sizeof(float) * PART_STRIDE * BM;   // one workgroup's rows
 
 // One workgroup: query rows q0 .. q0+BM-1 of a sequence of n tokens whose rows are rs
 // elements apart (Q/K/V/O point at the sequence's first row; LSE at its first entry), over
 // key tiles kt0 .. kt1-1 (kt0 < kt1). With part == nullptr the range is all keys and O (and
-// LSE) get the final rows; otherwise the workgroup's unnormalised O, m_ref and l go to part
-// (PART_STRIDE floats per row) for a later merge. Rows past n are computed on row n-1 and
+// LSE) get the final rows; otherwise the workgroup's unnormalised O, m_ref, l and correction
+// go to part (PART_STRIDE floats per row) for a later merge. O is divided by l + correction,
+// the LSE takes l. Rows past n are computed on row n-1 and
 // not written. Every thread of the workgroup must call this (the key loop has barriers).
 // LIST: the key tiles are the kt1 entries of klist (ascending tile indices, readable 8
 // entries past kt1; kt0 is unused); the tile-list key loop clamps every entry to
@@ -184,7 +187,7 @@ __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16
     }
     const int bperm = (lane ^ 32) << 2;
     f32x16 o[4][2];
-    float mref[2], lsum[2];
+    float mref[2], lsum[2], lcor[2];
     if constexpr (LIST) {
 #include "key_loop_idx_gfx950.inc"
     } else {
@@ -194,6 +197,7 @@ __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+        const float ctot = lcor[rb] + __shfl_xor(lcor[rb], 32);
         const bool qvalid = qrow[rb] < n;
         if (part != nullptr) {
             if (qvalid) {
@@ -209,11 +213,12 @@ __device__ __forceinline__ void attn_rows(const bf16* __restrict__ Q, const bf16
                 if (g == 0) {
                     prow[128] = mref[rb];
                     prow[129] = ltot;
+                    prow[130] = ctot;
                 }
             }
             continue;
         }
-        const float inv = 1.0f / ltot;
+        const float inv = 1.0f / (ltot + ctot);
         if (qvalid) {
             bf16* orow = O + (long)qrow[rb] * rs;
 #pragma unroll
@@ -329,7 +334,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_dense_split_kernel(DenseArgs a
 }
 
 // One block per (cut query tile, 16 rows): combines the tile's partial results,
-// O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with M = max_p m_p, LSE = (M + log2 l) ln 2.
+// O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) (l_p + c_p) with M = max_p m_p,
+// LSE = (M + log2 sum_p 2^(m_p - M) l_p) ln 2.
 // Thread (row r, 8-dim chunk k) handles O[r, 8k .. 8k+7].
 __global__ __launch_bounds__(256) void merge_kernel(DenseArgs a, SplitArgs sp) {
     const int i = blockIdx.x >> 4, rblk = blockIdx.x & 15;
@@ -355,18 +361,19 @@ __global__ __launch_bounds__(256) void merge_kernel(DenseArgs a, SplitArgs sp) {
         M = fmaxf(M, sp.part[(size_t)slot * (PART_BYTES / sizeof(float)) + (size_t)r * PART_STRIDE + 128]);
     }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
+    float l = 0.f, lb = 0.f;
     for (int g = g0; g <= g1; ++g) {
         const int slot = 2 * g + (share_begin(sp, g) / sp.ntk == i ? 0 : 1);
         const float* prow = sp.part + (size_t)slot * (PART_BYTES / sizeof(float)) + (size_t)r * PART_STRIDE;
         const float wgt = exp2_hw(prow[128] - M);
         l += wgt * prow[129];
+        lb += wgt * (prow[129] + prow[130]);
         const float4 x0 = reinterpret_cast<const float4*>(prow + 8 * k)[0];
         const float4 x1 = reinterpret_cast<const float4*>(prow + 8 * k)[1];
         acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
         acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
     }
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / lb;
     bf16x8 ov;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ov[e] = (bf16)(acc[e] * inv);
@@ -623,17 +630,18 @@ __global__ __launch_bounds__(256) void varlen_merge_kernel(VarlenArgs a, VarlenS
     float M = -INFINITY;
     for (int g = g0; g <= g1; ++g) M = fmaxf(M, slot_row(g)[128]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
+    float l = 0.f, lb = 0.f;
     for (int g = g0; g <= g1; ++g) {
         const float* prow = slot_row(g);
         const float wgt = exp2_hw(prow[128] - M);
         l += wgt * prow[129];
+        lb += wgt * (prow[129] + prow[130]);
         const float4 x0 = reinterpret_cast<const float4*>(prow + 8 * k)[0];
         const float4 x1 = reinterpret_cast<const float4*>(prow + 8 * k)[1];
         acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
         acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
     }
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / lb;
     bf16x8 ov;
 #pragma unroll
     for (int x = 0; x < 8; ++x) ov[x] = (bf16)(acc[x] * inv);

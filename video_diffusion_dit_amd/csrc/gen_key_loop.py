@@ -26,23 +26,28 @@ buffer->LDS loads three tiles ahead. Tile t uses stage t%4 and S buffer t%2, so 
 holds four tiles.
 
 Softmax bookkeeping (per row block): m (the reference the probabilities are taken against,
-log2 units of the scaled logit) and l (the lane's partial row sum). The common path computes
-p = exp2(S*c - m) and checks that no lane's tile sum exceeds 2^24; when one does (always on the
-first tile, where m = -inf) the wave calls the exact path, which recomputes S of the tile
-from LDS, moves m to the running row maximum plus a headroom of 32, rescales O and l, and
-recomputes P.
+log2 units of the scaled logit), l (the lane's partial row sum of the FP32 probabilities) and C
+(the lane's normaliser correction). The common path computes p = exp2(S*c - m) and checks that
+no lane's tile sum exceeds its limit min(l, 2^24); when one does (always on the first tile,
+where m = -inf) the wave calls the slow path. If a tile sum exceeds 2^24 (or is not a
+number) the reference moves: the rebase path shifts it by a whole power of two using the
+packed BF16 probabilities, or, when one of them is inf or NaN, the full path recomputes S of
+the tile from LDS, moves m to the running row maximum plus a headroom of 32, rescales O and
+l, and recomputes P. Every slow path ends in the correction, C += (sum of the tile's BF16
+probabilities) - (its FP32 tile sum), so O / (l + C) normalises the tiles that hold a lane's
+dominant keys by the BF16 values O used for them.
 
 Register map (per lane):
     v[0:63], v[64:127]   S buffers: block (rb, kb) at 16*(2*kb + rb); P packed to BF16 in
                          place (pair j of a block at 8*(j/4) + j%4)
     v[128:143]           K fragment ring (4 x 4)       v[144:159]   V fragment ring (4 x 4)
-    v160..v175           m, l, partial sums, mask limit, -inf, tile sums (v168..v171 unused)
+    v160..v175           m, l, partial sums, C, check limits, mask limit, -inf, tile sums
     v176..v199           temporaries (check, exact path)
-    s[40:61]             resource cursors, counters, masks, return address; s61 keeps the
+    s[40:61]             resource cursors, counters, masks, return address, BF16 ones; s61 keeps the
                          caller's M0 (the loads move it), which is restored at the end
     a[0:127]             O^T: block (db, rb) at 16*(2*db + rb)
     a[128:191]           Q fragments: (rb, s) at 128 + 4*(8*rb + s)
-The block hands O^T back in v[0:127] (same numbering), m and l in operands.
+The block hands O^T back in v[0:127] (same numbering), m, l and C in operands.
 
 Tile-list variant (block-skip attention, page "PR #33702 report", motivation: KV blocks
 routed by a threshold are skipped): the tiles walked are the entries of an int32 list in
@@ -62,6 +67,8 @@ for the gfx950 wait states that hand-written code must provide itself:
     MFMA write -> MFMA read as A/B, or as a C that is not its own chain 12
     MFMA read as C -> VALU write of the register                        12
     transcendental write -> VALU read                                   1
+    DOT write -> read by another instruction (except a DOT of the same
+                 opcode that takes it as its accumulator)               3
     SALU write of M0 -> buffer load to LDS                              1
 """
 import os
@@ -75,6 +82,8 @@ M = (160, 161)
 L = (162, 163)
 H1 = ((164, 165), (166, 167))      # the tile's partial sums [rb][2]: the first key half starts
 H2 = H1                            # them, the second half adds to the same registers
+C = (168, 169)                     # normaliser correction: sum of BF16 minus FP32 probabilities
+LIM = (170, 171)                   # the next tile's check limit: min(l, 2^24)
 KLIM_R = 172                       # key limit the exact path masks with (1000: no mask)
 NEG_INF = 173
 TS = (174, 175)                    # tile sums
@@ -87,6 +96,7 @@ S_RA = 54                          # exact-path return address s[54:55]
 S_C1, S_C2 = 56, 58                # check masks
 S_STG = 60                         # K stage offset handed to the exact path
 S_M0 = 61                          # M0 of the caller, restored at the end
+S_ONES = 53                        # 0x3f803f80: BF16 1.0 in both halves (sums packed pairs)
 NS_LO, NS_HI = 40, 61
 # tile-list variant
 V_IDX, V_ZERO = 200, 201
@@ -181,6 +191,8 @@ def need(prev, cur):
             r = max(r, 12)
     if prev.kind == "trans" and cur.kind in ("valu", "trans") and prev.wr & cur.rd:
         r = max(r, 1)
+    if prev.kind == "dot" and prev.wr & (cur.rd | (cur.rdc if cur.kind != "dot" else set())):
+        r = max(r, 3)   # only a v_dot2c_f32_bf16 reading it as its accumulator (rdc) needs none
     if prev.m0w and cur.m0r:
         r = max(r, 1)
     return r
@@ -353,13 +365,14 @@ N_TILE_SUM_OPS = 2    # the VALU instructions of check_ops() that form the tile 
 
 def check_ops():
     """Tile sums per row block (into TS, from the two partial sums both key halves added to)
-    and the rescale condition (into S_C1/S_C2)."""
+    and the slow-path condition (into S_C1/S_C2): a lane's tile sum above its limit
+    min(l, 2^24), or not a number."""
     def add(d, x, y):
         return lambda E: E.valu("v_add_f32 %s, %s, %s" % (vr(d), vr(x), vr(y)), rd=vset(x) | vset(y), wr=vset(d))
     ops = [add(TS[0], *H1[0]), add(TS[1], *H1[1])]
     for rb, sc in ((0, S_C1), (1, S_C2)):
-        ops.append(lambda E, rb=rb, sc=sc: E.valu("v_cmp_nge_f32_e64 s[%d:%d], s%d, %s" % (sc, sc + 1, S_LIM, vr(TS[rb])),
-                                                  rd=vset(TS[rb])))
+        ops.append(lambda E, rb=rb, sc=sc: E.valu("v_cmp_nge_f32_e64 s[%d:%d], %s, %s" % (sc, sc + 1, vr(LIM[rb]), vr(TS[rb])),
+                                                  rd=vset(LIM[rb]) | vset(TS[rb])))
     return ops
 
 
@@ -481,8 +494,11 @@ def rare_call(E, X, stage, uid):
 
 
 def add_l(E):
+    """l += tile sum; the next tile's limit min(l, 2^24)."""
     for rb in range(2):
         E.valu("v_add_f32 %s, %s, %s" % (vr(L[rb]), vr(L[rb]), vr(TS[rb])), rd=vset(L[rb]) | vset(TS[rb]), wr=vset(L[rb]))
+    for rb in range(2):
+        E.valu("v_min_f32 %s, s%d, %s" % (vr(LIM[rb]), S_LIM, vr(L[rb])), rd=vset(L[rb]), wr=vset(LIM[rb]))
 
 
 KLIM_IN = ("%[klim]", set())
@@ -524,12 +540,9 @@ def rebase_path(E, X):
     lies up to 128 log2 units above the old reference, and 2^-k then is no FP32 number, while
     the tile's own sum times 2^-k is about 2^-33.) A probability that is inf or NaN (the first tile, where
     m = -inf, or a key beyond the FP32 range of the old reference) carries no usable maximum:
-    then the full path below recomputes S. Entered and left with all wait states satisfied."""
-    E.label(".Lrare%d_%%=" % X)
-    E.fresh()
-    E.nop(12)
-    E.raw("s_waitcnt lgkmcnt(0)")
-    E.pending = []
+    then the full path below recomputes S. Entered from the slow-path entry (no LDS read in
+    flight); goes on to the correction with all wait states satisfied."""
+    E.label(".Lmove%d_%%=" % X)
     mx, px, kk, negk = (TMP0 + 2, TMP0 + 3), (TMP0 + 4, TMP0 + 5), (TMP0 + 6, TMP0 + 7), (TMP0 + 8, TMP0 + 9)
     ki, t = TMP0 + 10, TMP0 + 11
     for rb in range(2):
@@ -564,12 +577,12 @@ def rebase_path(E, X):
         for r in packed_p(X, rb):
             E.valu("v_pk_max_u16 %s, %s, %s" % (vr(r), vr(r), vr(kk[rb])), rd=vset(r) | vset(kk[rb]), wr=vset(r))
             E.valu("v_pk_sub_u16 %s, %s, %s" % (vr(r), vr(r), vr(kk[rb])), rd=vset(r) | vset(kk[rb]), wr=vset(r))
-        for x in (L[rb], TS[rb]):
+        for x in (L[rb], TS[rb], C[rb]):
             E.valu("v_ldexp_f32 %s, %s, %s" % (vr(x), vr(x), vr(negk[rb])), rd=vset(x) | vset(negk[rb]), wr=vset(x))
     rescale_o(E, negk, "v_ldexp_f32")
     E.fresh()
     E.nop(12)
-    E.raw("s_setpc_b64 s[%d:%d]" % (S_RA, S_RA + 1))
+    E.raw("s_branch .Lfix%d_%%=" % X)
 
 
 def rare_path(E, X):
@@ -623,14 +636,64 @@ def rare_path(E, X):
         E.trans("v_exp_f32 %s, %s" % (vr(alpha[rb]), vr(alpha[rb])), rd=vset(alpha[rb]), wr=vset(alpha[rb]))
         E.valu("v_mov_b32 %s, %s" % (vr(M[rb]), vr(tm[rb])), rd=vset(tm[rb]), wr=vset(M[rb]))
     for rb in range(2):
-        E.valu("v_mul_f32 %s, %s, %s" % (vr(L[rb]), vr(L[rb]), vr(alpha[rb])), rd=vset(L[rb]) | vset(alpha[rb]), wr=vset(L[rb]))
+        for x in (L[rb], C[rb]):
+            E.valu("v_mul_f32 %s, %s, %s" % (vr(x), vr(x), vr(alpha[rb])), rd=vset(x) | vset(alpha[rb]), wr=vset(x))
     rescale_o(E, alpha)
     for f in softmax_half(X, 0, True, KLIM_EXACT, H1) + softmax_half(X, 1, True, KLIM_EXACT, H2) + \
             check_ops()[:N_TILE_SUM_OPS]:
         f(E)
     E.fresh()
     E.nop(12)
+    E.raw("s_branch .Lfix%d_%%=" % X)
+
+
+def slow_path(E, X):
+    """The wave's slow path for the tile in S buffer X, entered when some lane's tile sum
+    exceeds its limit min(l, 2^24) (or is not a number).
+
+    A tile sum above 2^24 or not a number needs a new reference: the rebase path, or the full
+    path when a probability is inf or NaN. Either way (and when the limit was l, which a tile
+    holding more than half of the lane's running sum exceeds) the tile's correction follows:
+    C += (sum of the tile's BF16 probabilities) - (their FP32 tile sum). O is later divided by
+    l + C, the sum of the BF16 probabilities that O's products used, for the keys of these
+    tiles: a key that ends with half or more of its lane's weight sits in such a tile, so the
+    weights of the keys that dominate a row add up to one exactly, whatever the BF16 rounding
+    of their probabilities. The LSE keeps the FP32 sum l."""
+    E.label(".Lrare%d_%%=" % X)
+    E.fresh()
+    E.nop(12)
+    E.raw("s_waitcnt lgkmcnt(0)")
+    E.pending = []
+    for rb in range(2):   # does any lane need a new reference (tile sum above 2^24, or NaN)?
+        E.valu("v_cmp_nge_f32 vcc, s%d, %s" % (S_LIM, vr(TS[rb])), rd=vset(TS[rb]), wr=VCC)
+        if rb == 0:
+            E.salu("s_mov_b64 s[%d:%d], vcc" % (S_C1, S_C1 + 1))
+    E.salu("s_or_b64 s[%d:%d], s[%d:%d], vcc" % (S_C1, S_C1 + 1, S_C1, S_C1 + 1))
+    E.raw("s_cbranch_scc1 .Lmove%d_%%=" % X)
+    at_move = E.state()
+    E.label(".Lfix%d_%%=" % X)
+    # four chains of v_dot2c_f32_bf16 (row block rb, odd/even packed register): a DOT result
+    # goes straight to the next DOT of the same opcode as its accumulator, but any other
+    # reader waits 3 wait states
+    acc = [[TMP0 + 2, TMP0 + 4], [TMP0 + 3, TMP0 + 5]]
+    for rb in range(2):
+        for a in acc[rb]:
+            E.valu("v_mov_b32 %s, 0" % vr(a), wr=vset(a))
+    for i in range(8):
+        for rb in range(2):
+            for half in range(2):
+                a, r = acc[rb][half], packed_p(X, rb)[2 * i + half]
+                E.emit(Ins("v_dot2c_f32_bf16 %s, s%d, %s" % (vr(a), S_ONES, vr(r)), "dot", rd=vset(r), wr=vset(a),
+                           rdc=vset(a)))
+    for rb in range(2):
+        a, b = acc[rb]
+        E.valu("v_add_f32 %s, %s, %s" % (vr(a), vr(a), vr(b)), rd=vset(a) | vset(b), wr=vset(a))
+        E.valu("v_sub_f32 %s, %s, %s" % (vr(a), vr(a), vr(TS[rb])), rd=vset(a) | vset(TS[rb]), wr=vset(a))
+        E.valu("v_add_f32 %s, %s, %s" % (vr(C[rb]), vr(C[rb]), vr(a)), rd=vset(C[rb]) | vset(a), wr=vset(C[rb]))
+    E.fresh()
+    E.nop(12)
     E.raw("s_setpc_b64 s[%d:%d]" % (S_RA, S_RA + 1))
+    E.set_state(at_move)
 
 
 def final_phase(E, Y, stage, uid):
@@ -668,9 +731,12 @@ def generate(backedge=None):
     E.salu("s_mov_b32 s%d, 0" % S_T)
     E.salu("s_sub_u32 s%d, %%[T], 2" % S_TLAST)
     E.salu("s_mov_b32 s%d, 0x%08x" % (S_LIM, OPTS["limit_bits"]))
+    E.salu("s_mov_b32 s%d, 0x3f803f80" % S_ONES)
     for rb in range(2):
         E.valu("v_mov_b32 %s, 0xff800000" % vr(M[rb]), wr=vset(M[rb]))
         E.valu("v_mov_b32 %s, 0" % vr(L[rb]), wr=vset(L[rb]))
+        E.valu("v_mov_b32 %s, 0" % vr(C[rb]), wr=vset(C[rb]))
+        E.valu("v_mov_b32 %s, 0" % vr(LIM[rb]), wr=vset(LIM[rb]))
     E.valu("v_mov_b32 %s, 1000" % vr(KLIM_R), wr=vset(KLIM_R))
     E.valu("v_mov_b32 %s, 0xff800000" % vr(NEG_INF), wr=vset(NEG_INF))
     for rb in range(2):
@@ -736,6 +802,7 @@ def generate(backedge=None):
     final_phase(E, 0, 0, "S")
 
     for X in range(2):
+        slow_path(E, X)
         rebase_path(E, X)
         rare_path(E, X)
 
@@ -749,6 +816,7 @@ def generate(backedge=None):
     for rb in range(2):
         E.raw("v_mov_b32 %%[m%d], %s" % (rb, vr(M[rb])))
         E.raw("v_mov_b32 %%[l%d], %s" % (rb, vr(L[rb])))
+        E.raw("v_mov_b32 %%[c%d], %s" % (rb, vr(C[rb])))
     return E.out, loop_end
 
 
@@ -775,7 +843,8 @@ def _render():
            ['"s%d"' % i for i in range(NS_LO, ns_hi + 1)] + ['"vcc"', '"scc"', '"memory"']
     outs = ['[o%d%d] "=&{v[%d:%d]}"(o[%d][%d])' % (db, rb, oblk(db, rb), oblk(db, rb) + 15, db, rb)
             for db in range(4) for rb in range(2)]
-    outs += ['[m0] "=v"(mref[0])', '[m1] "=v"(mref[1])', '[l0] "=v"(lsum[0])', '[l1] "=v"(lsum[1])']
+    outs += ['[m0] "=v"(mref[0])', '[m1] "=v"(mref[1])', '[l0] "=v"(lsum[0])', '[l1] "=v"(lsum[1])',
+             '[c0] "=v"(lcor[0])', '[c1] "=v"(lcor[1])']
     ins = ['[rk%d] "s"(rk[%d])' % (i, i) for i in range(4)] + ['[rv%d] "s"(rv[%d])' % (i, i) for i in range(4)]
     ins += ['[ka%d] "v"(ka[%d])' % (i, i) for i in range(8)] + ['[va%d] "v"(va[%d])' % (i, i) for i in range(8)]
     ins += ['[ko%d] "v"(ko[%d])' % (i, i) for i in range(4)] + ['[vo%d] "v"(vo[%d])' % (i, i) for i in range(4)]
