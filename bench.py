@@ -98,6 +98,31 @@ def measured_traffic(workload: str, kernel: str, split_kv: bool, kind: str = "de
         return None
 
 
+def _base_name(name: str) -> str:
+    """"void (anonymous namespace)::pool_kernel<64>(...)" -> "pool_kernel"."""
+    name = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
+    return name.split("::")[-1].split()[-1]
+
+
+def _of_call(order, names) -> set:
+    """Dispatch ids (of `order`, [(dispatch id, base name)] in dispatch order) that belong to
+    one call of the kernels `names`. A kernel that calls of several kinds share (the varlen
+    schedule builder, the longest-first sort) belongs to the call whose next own kernel
+    follows it."""
+    shared = {n for n in names if sum(n in v for v in CALL_KERNELS.values()) > 1}
+    known = {n for v in CALL_KERNELS.values() for n in v}
+    keep = set()
+    for i, (d, n) in enumerate(order):
+        if n not in names:
+            continue
+        if n in shared:
+            nxt = next((m for _, m in order[i + 1:] if m in known and m not in shared), None)
+            if nxt is not None and nxt not in names:
+                continue
+        keep.add(d)
+    return keep
+
+
 def _pmc_dispatches(csv_path: str, counter: str):
     """[(dispatch id, kernel name, value in KiB)] for one counter of a rocprofv3 CSV, in order."""
     import csv
@@ -122,16 +147,12 @@ def write_traffic_profile(args) -> int:
     if copy_bytes <= 0:
         raise SystemExit("--calibrate-copy-mib (the copy size of the profiled run) is required")
 
-    def base(name):   # "void (anonymous namespace)::pool_kernel<64>(...)" -> "pool_kernel"
-        name = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
-        return name.split("::")[-1].split()[-1]
-
-    def of_call(name):
-        return base(name) in names
+    base = _base_name
 
     def split(rows):
-        att = [(name, v) for _, name, v in rows if of_call(name)]
-        others = [(d, name, v) for d, name, v in rows if not of_call(name)]
+        mine = _of_call([(d, base(name)) for d, name, _ in rows], names)
+        att = [(name, v) for d, name, v in rows if d in mine]
+        others = [(d, name, v) for d, name, v in rows if base(name) not in names]
         calls = sum(1 for name, _ in att if base(name) == names[0])
         return att, calls, others[-1]    # the calibration copy is the last dispatch of the run
 
@@ -199,16 +220,17 @@ def write_mfma_profile(args) -> int:
     names = CALL_KERNELS[kind]
     kernel = names[0]
 
-    def base(name):
-        name = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
-        return name.split("::")[-1].split()[-1]
+    base = _base_name
+    with open(counter_csv) as f:
+        seen = {int(row["Dispatch_Id"]): base(row["Kernel_Name"]) for row in csv.DictReader(f)}
+    mine = _of_call(sorted(seen.items()), names)
 
     vals, spans, kname = {}, {}, {}
     with open(counter_csv) as f:
         for row in csv.DictReader(f):
-            if base(row["Kernel_Name"]) not in names:
-                continue
             d = int(row["Dispatch_Id"])
+            if d not in mine:
+                continue
             kname[d] = base(row["Kernel_Name"])
             key = (d, row["Counter_Name"])
             vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
@@ -694,7 +716,9 @@ def time_block_sparse_varlen(args, w, vd, q, k, v, qb, kb, vb, cu, dense_ms: flo
                 "256-row query tile (keep z >= max z - tau), then exact softmax over the kept tiles",
         "tau": tau, "order": order_name, "density": round(pairs / full, 4), "bound": "mfma",
         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-        "flops_per_call": flops, "traffic": None,
+        "flops_per_call": flops,
+        "traffic": measured_traffic(w.name, "attn_fwd_block_sparse_varlen_kernel", False, "block_sparse_varlen"),
+        "mfma_counters": measured_mfma(w.name, "attn_fwd_block_sparse_varlen_kernel", False, "block_sparse_varlen"),
         "ms": {"sparse": round(avg_s, 4), "sparse_min": round(min(sparse_ms), 4),
                "sparse_max": round(max(sparse_ms), 4), "route": round(avg_r, 4)},
         "speedup_vs_dense_call": round(dense_ms / (avg_s + avg_r), 3),

@@ -71,3 +71,45 @@ def test_record_of_other_sources_is_ignored(tmp_path, monkeypatch):
     bench.write_mfma_profile(args)
     monkeypatch.setattr(bench, "kernel_source_hash", lambda kind="dense": "0" * 64)
     assert bench.measured_mfma("video_720p", "attn_fwd_dense_kernel", True, "dense") is None
+
+
+PACKED_RUN = ["build_varlen_schedule", "varlen_split_plan", "attn_fwd_varlen_kernel", "attn_fwd_varlen_split_kernel",
+              "varlen_merge_kernel",                                   # one packed attention call
+              "tile_offsets_kernel", "pool_varlen_kernel", "route_varlen_kernel", "lpt_order_kernel",
+              "build_varlen_schedule", "attn_fwd_block_sparse_varlen_kernel",   # routing, then the sparse pass
+              "qk_norm_packed_kernel", "__amd_rocclr_copyBuffer"]
+
+
+def test_shared_kernels_go_to_the_call_they_precede():
+    order = list(enumerate(PACKED_RUN, start=1))
+    assert bench._of_call(order, bench.CALL_KERNELS["varlen"]) == {1, 2, 3, 4, 5}
+    assert bench._of_call(order, bench.CALL_KERNELS["block_sparse_varlen"]) == {6, 7, 8, 9, 10, 11}
+    assert bench._of_call(order, bench.CALL_KERNELS["packed_prologue"]) == {12}
+
+
+def test_traffic_record_of_a_packed_run(tmp_path, monkeypatch):
+    """FETCH/WRITE of the packed call's five kernels only, scaled by the calibration copy."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    last = len(PACKED_RUN)                              # the calibration copy's dispatch
+    fetch = {d: 100.0 * d for d in range(1, last)}
+    fetch[last] = 512.0                                 # a 1 MiB copy reads as 512 KiB: scale x2
+    write = {d: 10.0 * d for d in range(1, last)}
+    write[last] = 1024.0
+    paths = []
+    for counter, vals in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        p = tmp_path / f"{counter}.csv"
+        with open(p, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(HEADER)
+            for d, n in enumerate(PACKED_RUN, start=1):
+                name = n if n.startswith("__") else NS + n + "(" + NS + "Args)"
+                w.writerow([d, d, "Agent 1", 1, 1, 1, 1, 1, name, 256, 0, 0, 0, 0, 0, counter, vals[d], 0, 1])
+        paths.append(str(p))
+    args = argparse.Namespace(write_traffic_profile=tuple(paths), traffic_kind="varlen", workload="packed_varlen",
+                              calibrate_copy_mib=1, profile_command="")
+    assert bench.write_traffic_profile(args) == 0
+    copy_mib = 1 << 20
+    f_scale = copy_mib / (512.0 * 1024)
+    w_scale = copy_mib / (1024.0 * 1024)
+    want = (100 + 200 + 300 + 400 + 500) * 1024 * f_scale + (10 + 20 + 30 + 40 + 50) * 1024 * w_scale
+    assert bench.measured_traffic("packed_varlen", "attn_fwd_varlen_kernel", True, "varlen") == pytest.approx(want)
