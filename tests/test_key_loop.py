@@ -153,8 +153,9 @@ def mfma_violations(asm_lines):
 
 
 def dot_violations(asm_lines):
-    """A v_dot2c_f32_bf16 result read by any other instruction (or by a DOT as a multiplicand)
-    fewer than 3 wait states later, along the straight-line code."""
+    """A DOT result (v_dot2_f32_bf16, v_dot2c_f32_bf16) read fewer than 3 wait states later by
+    anything but a DOT of the same opcode that takes it as its accumulator, along the
+    straight-line code."""
     ins = [("<label>", []) if l.endswith(":") else parse(l) for l in asm_lines]
     bad = []
     for k, (op, ops) in enumerate(ins):
@@ -168,6 +169,8 @@ def dot_violations(asm_lines):
                 break
             if qop.startswith("v_dot2c"):
                 srcs = regs(qops[1]) | regs(qops[2])      # multiplicands; the accumulator is the dst
+                if qop != op:                             # another DOT opcode: its accumulator read counts
+                    srcs |= regs(qops[0])
             else:
                 srcs = set()
                 for t in qops[1:]:
@@ -186,6 +189,10 @@ def test_dot_wait_states(asm_lines):
     k = next(i for i, l in enumerate(asm_lines) if l.startswith("v_dot2c_f32_bf16"))
     dst = parse(asm_lines[k])[1][0]
     assert dot_violations(asm_lines[:k + 1] + ["v_add_f32 v199, %s, %s" % (dst, dst)] + asm_lines[k + 1:])
+    # and a chain that switches DOT opcode on its accumulator right away
+    k = next(i for i, l in enumerate(asm_lines) if l.startswith("v_dot2_f32_bf16"))
+    dst = parse(asm_lines[k])[1][0]
+    assert dot_violations(asm_lines[:k + 1] + ["v_dot2c_f32_bf16 %s, s53, v0" % dst] + asm_lines[k + 1:])
 
 
 def test_lds_results_waited(asm_lines):
@@ -388,7 +395,7 @@ def test_slow_path_entry_and_correction(gen, asm_lines):
         assert written <= owned, written - owned
         packed = {("v", r) for rb in range(2) for r in gen.packed_p(X, rb)}
         assert packed <= read and read <= packed | owned | {("v", t) for t in gen.TS}
-        assert sum(l.startswith("v_dot2c_f32_bf16") for l in body) == 32
+        assert sum(l.startswith(("v_dot2_f32_bf16", "v_dot2c_f32_bf16")) for l in body) == 32
         assert all("s%d" % gen.S_ONES in l for l in body if l.startswith("v_dot2"))
         assert sum(l == "s_branch .Lfix%d_%%=" % X for l in asm_lines) == 2
     assert any(l == "s_mov_b32 s%d, 0x3f803f80" % gen.S_ONES for l in asm_lines)
@@ -404,3 +411,37 @@ def test_check_limit_follows_l(gen, asm_lines):
                 assert "v_min_f32 v%d, s%d, v%d" % (gen.LIM[rb], gen.S_LIM, gen.L[rb]) in nxt, nxt
     cmps = [l for l in asm_lines if l.startswith("v_cmp_nge_f32_e64")]
     assert cmps and all(re.match(r"v_cmp_nge_f32_e64 s\[\d+:\d+\], v(170|171), v(174|175)$", l) for l in cmps), cmps[:2]
+
+
+def test_slow_path_wait_states_from_every_call(asm_lines):
+    """The slow path starts without s_nop of its own: the generator counts the wait states owed
+    by the code before each of its calls. Re-check that here: the straight-line code before every
+    call, followed by the entry and the correction (and by the entry and the rebase's opening),
+    passes the MFMA and DOT scans."""
+    def body(start_label, stop):
+        i = asm_lines.index(start_label) + 1
+        out = []
+        while not stop(asm_lines[i]):
+            if not asm_lines[i].endswith(":"):
+                out.append(asm_lines[i])
+            i += 1
+        return out
+    checked = 0
+    for X in range(2):
+        entry = body(".Lrare%d_%%=:" % X, lambda l: l.startswith("s_cbranch_scc1 .Lmove"))
+        fix = body(".Lfix%d_%%=:" % X, lambda l: l.startswith("s_setpc_b64"))
+        move = body(".Lmove%d_%%=:" % X, lambda l: l.startswith("s_cbranch"))
+        calls = [i for i, l in enumerate(asm_lines) if l == "s_branch .Lrare%d_%%=" % X]
+        assert calls
+        for i in calls:
+            pre = [l for l in asm_lines[max(0, i - 80):i] if not l.endswith(":") and not is_block_end(l.split()[0])]
+            for tail in (fix, move):
+                seq = pre + entry + tail
+                assert mfma_violations(seq) == [] and dot_violations(seq) == [], (X, i)
+            # not vacuous: reading the result of the call site's last MFMA at the entry is flagged
+            recent = [l for l in pre[-8:] if l.startswith("v_mfma")]
+            if recent:   # calls right after a QK phase (not those after the last tile's check)
+                res = parse(recent[-1])[1][0].split(":")[0].replace("[", "")
+                assert mfma_violations(pre + ["v_add_f32 v199, %s, %s" % (res, res)] + entry + fix)
+                checked += 1
+    assert checked >= 4   # the four calls of the loop body

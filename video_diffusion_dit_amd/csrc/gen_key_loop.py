@@ -191,8 +191,10 @@ def need(prev, cur):
             r = max(r, 12)
     if prev.kind == "trans" and cur.kind in ("valu", "trans") and prev.wr & cur.rd:
         r = max(r, 1)
-    if prev.kind == "dot" and prev.wr & (cur.rd | (cur.rdc if cur.kind != "dot" else set())):
-        r = max(r, 3)   # only a v_dot2c_f32_bf16 reading it as its accumulator (rdc) needs none
+    if prev.kind == "dot" and prev.wr & cur.rd:
+        r = max(r, 3)
+    if prev.kind == "dot" and prev.wr & cur.rdc and (cur.kind != "dot" or cur.text.split()[0] != prev.text.split()[0]):
+        r = max(r, 3)   # only a DOT of the same opcode reading it as its accumulator needs none
     if prev.m0w and cur.m0r:
         r = max(r, 1)
     return r
@@ -207,6 +209,7 @@ class Emitter:
         self.out = []
         self.hists = [[]]
         self.pending = []      # register sets written by LDS ops in flight, oldest first
+        self.calls = {0: [], 1: []}   # histories at the calls of each S buffer's slow path
 
     def fresh(self):
         self.hists = [[]]
@@ -489,6 +492,7 @@ def rare_call(E, X, stage, uid):
     E.label(".Lpc%s_%%=" % uid)
     E.raw("s_add_u32 s%d, s%d, .Lok%s_%%=-.Lpc%s_%%=" % (S_RA, S_RA, uid, uid))
     E.raw("s_addc_u32 s%d, s%d, 0" % (S_RA + 1, S_RA + 1))
+    E.calls[X].extend(list(h) for h in E.hists)
     E.raw("s_branch .Lrare%d_%%=" % X)
     E.label(".Lok%s_%%=" % uid)
 
@@ -660,8 +664,7 @@ def slow_path(E, X):
     weights of the keys that dominate a row add up to one exactly, whatever the BF16 rounding
     of their probabilities. The LSE keeps the FP32 sum l."""
     E.label(".Lrare%d_%%=" % X)
-    E.fresh()
-    E.nop(12)
+    E.hists = [list(h) for h in E.calls[X]] or [[]]   # wait states as seen from every call
     E.raw("s_waitcnt lgkmcnt(0)")
     E.pending = []
     for rb in range(2):   # does any lane need a new reference (tile sum above 2^24, or NaN)?
@@ -676,22 +679,22 @@ def slow_path(E, X):
     # goes straight to the next DOT of the same opcode as its accumulator, but any other
     # reader waits 3 wait states
     acc = [[TMP0 + 2, TMP0 + 4], [TMP0 + 3, TMP0 + 5]]
-    for rb in range(2):
-        for a in acc[rb]:
-            E.valu("v_mov_b32 %s, 0" % vr(a), wr=vset(a))
     for i in range(8):
         for rb in range(2):
             for half in range(2):
                 a, r = acc[rb][half], packed_p(X, rb)[2 * i + half]
-                E.emit(Ins("v_dot2c_f32_bf16 %s, s%d, %s" % (vr(a), S_ONES, vr(r)), "dot", rd=vset(r), wr=vset(a),
-                           rdc=vset(a)))
+                if i == 0:   # the chain starts with the three-operand form and a zero accumulator
+                    E.emit(Ins("v_dot2_f32_bf16 %s, %s, s%d, 0" % (vr(a), vr(r), S_ONES), "dot", rd=vset(r), wr=vset(a)))
+                else:
+                    E.emit(Ins("v_dot2c_f32_bf16 %s, s%d, %s" % (vr(a), S_ONES, vr(r)), "dot", rd=vset(r),
+                               wr=vset(a), rdc=vset(a)))
     for rb in range(2):
         a, b = acc[rb]
         E.valu("v_add_f32 %s, %s, %s" % (vr(a), vr(a), vr(b)), rd=vset(a) | vset(b), wr=vset(a))
         E.valu("v_sub_f32 %s, %s, %s" % (vr(a), vr(a), vr(TS[rb])), rd=vset(a) | vset(TS[rb]), wr=vset(a))
         E.valu("v_add_f32 %s, %s, %s" % (vr(C[rb]), vr(C[rb]), vr(a)), rd=vset(C[rb]) | vset(a), wr=vset(C[rb]))
-    E.fresh()
-    E.nop(12)
+    # no wait owed on return: the path writes only C and its temporaries, which no MFMA reads,
+    # and its DOT results are read inside it
     E.raw("s_setpc_b64 s[%d:%d]" % (S_RA, S_RA + 1))
     E.set_state(at_move)
 
