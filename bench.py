@@ -99,7 +99,12 @@ def measured_traffic(workload: str, kernel: str, split_kv: bool, kind: str = "de
 
 
 def _base_name(name: str) -> str:
-    """"void (anonymous namespace)::pool_kernel<64>(...)" -> "pool_kernel"."""
+    """"void (anonymous namespace)::pool_kernel<64>(...)" -> "pool_kernel"; a name the profiler
+    left mangled ("_ZN12_GLOBAL__N_118pool_varlen_kernelILi64EE...") -> "pool_varlen_kernel"."""
+    import re
+    m = re.match(r"_ZN(?:\d+_GLOBAL__N_1)?(\d+)", name)
+    if m:
+        return name[m.end():m.end() + int(m.group(1))]
     name = name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
     return name.split("::")[-1].split()[-1]
 

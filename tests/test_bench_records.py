@@ -113,3 +113,11 @@ def test_traffic_record_of_a_packed_run(tmp_path, monkeypatch):
     w_scale = copy_mib / (1024.0 * 1024)
     want = (100 + 200 + 300 + 400 + 500) * 1024 * f_scale + (10 + 20 + 30 + 40 + 50) * 1024 * w_scale
     assert bench.measured_traffic("packed_varlen", "attn_fwd_varlen_kernel", True, "varlen") == pytest.approx(want)
+
+
+def test_kernel_names_as_the_profiler_writes_them():
+    assert bench._base_name("void (anonymous namespace)::pool_kernel<64>(bool _Accum const*, float, int, int)") == \
+        "pool_kernel"
+    assert bench._base_name("(anonymous namespace)::merge_kernel((anonymous namespace)::DenseArgs)") == "merge_kernel"
+    assert bench._base_name("_ZN12_GLOBAL__N_118pool_varlen_kernelILi256EEEvPKDF16bPfPKiS5_iii") == "pool_varlen_kernel"
+    assert bench._base_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
