@@ -16,7 +16,7 @@
  * exp(x - m_ref) rounded to BF16 (round-to-nearest-even) before the PV product, where
  * m_ref is a per-row reference the kernel moves only when some probability of a 64-key
  * tile would make a lane's tile sum exceed 2^24 (then to about the row's running maximum
- * plus 32 log2 units); l sums the FP32 probabilities and gives the LSE. O = (PV
+ * plus 48 log2 units); l sums the FP32 probabilities and gives the LSE. O = (PV
  * accumulator) / (l + C) rounded to BF16 RNE, where C adds, for the tiles that hold more
  * than half of a lane's running sum (or move the reference), the difference between the
  * sum of their BF16 probabilities and their FP32 sum: the keys that dominate a row are
@@ -27,9 +27,9 @@
  * Value range (every attention entry point): accepted probabilities never exceed 2^24, so
  * before normalisation |O| < N * 2^24 * max|v| (N: keys of the sequence): FP32 holds it while
  * N * max|v| < 2^104, e.g. max|v| < 2^87 at N = 2^17. Right after a move the probabilities
- * are at most 2^-32, so keys whose weight is below 2^-94 of the row maximum's may fall under
+ * are at most 2^-48, so keys whose weight is below 2^-78 of the row maximum's may fall under
  * the FP32 normal range (their share of the output is far below its precision), and the
- * products p * v keep full precision while max|v| >= 2^-94. Q and K: any finite BF16 values
+ * products p * v keep full precision while max|v| >= 2^-78. Q and K: any finite BF16 values
  * (logits up to the FP32 range; the tests use up to about +-1150).
  *
  * Conventions for every entry point:

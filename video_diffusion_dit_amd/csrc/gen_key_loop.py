@@ -32,7 +32,7 @@ no lane's tile sum exceeds its limit min(l, 2^24); when one does (always on the 
 where m = -inf) the wave calls the slow path. If a tile sum exceeds 2^24 (or is not a
 number) the reference moves: the rebase path shifts it by a whole power of two using the
 packed BF16 probabilities, or, when one of them is inf or NaN, the full path recomputes S of
-the tile from LDS, moves m to the running row maximum plus a headroom of 32, rescales O and
+the tile from LDS, moves m to the running row maximum plus a headroom of 48, rescales O and
 l, and recomputes P. Every slow path ends in the correction, C += (sum of the tile's BF16
 probabilities) - (its FP32 tile sum), so O / (l + C) normalises the tiles that hold a lane's
 dominant keys by the BF16 values O used for them.
@@ -112,12 +112,12 @@ V_STAGE = 16384
 # running maximum keeps climbing (outlier channels).
 RESCALE_LIMIT_BITS = 0x4B800000
 
-# Headroom: the exact path sets the reference m to the row's running maximum + 32 instead of
-# the maximum itself, so a later key must exceed that maximum by more than 24 + 32 log2 units
-# before the wave takes the exact path again (rows whose maximum keeps climbing, as with
-# outlier channels, take it far less often). Probabilities right after a move are <= 2^-32;
-# a key more than 94 log2 units below the maximum (relative weight < 2^-94) can fall below
-# the FP32 normal range, and sum(p v) stays normal while max|v| >= 2^-94.
+# Headroom: the exact path sets the reference m to the row's running maximum + 48 instead of
+# the maximum itself, so a later key must exceed that maximum by more than 24 + 48 log2 units
+# before the wave moves the reference again (rows whose maximum keeps climbing, as with
+# outlier channels, move it far less often). Probabilities right after a move are <= 2^-48;
+# a key more than 78 log2 units below the maximum (relative weight < 2^-78) can fall below
+# the FP32 normal range, and sum(p v) stays normal while max|v| >= 2^-78.
 
 # Schedule knobs (the values the kernel is built with).
 OPTS = {
@@ -130,7 +130,7 @@ OPTS = {
     "vpre_after": 24,    # QK phase: the next PV phase's first V fragments read after this MFMA
     "limit_bits": RESCALE_LIMIT_BITS,
     "stagger": 1,        # softmax groups: fma, exp and sum/pack of a group this many groups apart
-    "headroom": 32,      # the exact path moves m to the running maximum plus this (log2 units)
+    "headroom": 48,      # the exact path moves m to the running maximum plus this (log2 units)
 }
 
 
@@ -540,9 +540,9 @@ def rebase_path(E, X):
     probability below 2^-headroom. Scaling by 2^-k is exact: P in place by subtracting k
     from each BF16 exponent field (u16 max then subtract, so values that would drop below the
     normal range, weights under 2^-126 of the new reference, become 0), l, the tile sums and
-    O by v_ldexp_f32 with -k. (Not by a multiplication with 2^-k: k reaches 161 when a key
+    O by v_ldexp_f32 with -k. (Not by a multiplication with 2^-k: k reaches 177 when a key
     lies up to 128 log2 units above the old reference, and 2^-k then is no FP32 number, while
-    the tile's own sum times 2^-k is about 2^-33.) A probability that is inf or NaN (the first tile, where
+    the tile's own sum times 2^-k is about 2^-49.) A probability that is inf or NaN (the first tile, where
     m = -inf, or a key beyond the FP32 range of the old reference) carries no usable maximum:
     then the full path below recomputes S. Entered from the slow-path entry (no LDS read in
     flight); goes on to the correction with all wait states satisfied."""
