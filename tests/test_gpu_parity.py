@@ -170,6 +170,17 @@ def test_varlen_full(attn, lens):
     check(f64_of(o), o_ref, lse.cpu().numpy(), lse_ref, f"varlen {lens[:8]}")
 
 
+def test_varlen_many_sorted_segments(attn):
+    # 3000 segments: the schedule builder sorts them (below its limit) and every one of its 16
+    # waves carries a share of the prefix of query tiles
+    from gpu_util import check, f64_of
+    lens = [int(x) for x in np.random.default_rng(5).integers(0, 300, 3000)]
+    q, k, v, cu = random_varlen(lens, H=1, seed=25)
+    o, lse = run_varlen(attn, q, k, v, cu)
+    o_ref, lse_ref = attention_varlen(q, k, v, cu, SCALE)
+    check(f64_of(o), o_ref, lse.cpu().numpy(), lse_ref, "varlen 3000 sorted segments")
+
+
 def test_varlen_many_segments_beyond_sort_limit(attn):
     from gpu_util import check, f64_of
     rng = np.random.default_rng(21)

@@ -407,8 +407,8 @@ __device__ __forceinline__ int seg_len(const int32_t* cu, int s, int T) {
 __global__ __launch_bounds__(1024) void build_varlen_schedule(const int32_t* __restrict__ cu,
                                                               int nseg, int T, char* ws, int H,
                                                               long long* __restrict__ cum) {
-    __shared__ int chunk[1024];
-    __shared__ long long cost_chunk[1024];
+    __shared__ int chunk[16];
+    __shared__ long long cost_chunk[16];
     int* count = reinterpret_cast<int*>(ws);
     int* order = reinterpret_cast<int*>(ws + WS_HEADER);
     int2* list = reinterpret_cast<int2*>(ws + ws_list_offset(nseg));
@@ -439,20 +439,34 @@ __global__ __launch_bounds__(1024) void build_varlen_schedule(const int32_t* __r
         sum += (len + BM - 1) / BM;
         csum += (long long)((len + BM - 1) / BM) * ((len + BN - 1) / BN);
     }
-    chunk[tid] = sum;
-    cost_chunk[tid] = csum;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        long long cacc = 0;
-        for (int i = 0; i < 1024; ++i) {
-            const int v = chunk[i];
-            const long long cv = cost_chunk[i];
-            chunk[i] = acc;
-            cost_chunk[i] = cacc;
-            acc += v;
-            cacc += cv;
+    // exclusive prefix of (sum, csum) over the threads: within each wave by shuffles, then
+    // over the 16 wave totals
+    const int lane = tid & 63, wv = tid >> 6;
+    int s_in = sum;
+    long long c_in = csum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int sv = __shfl_up(s_in, o);
+        const long long cv = __shfl_up(c_in, o);
+        if (lane >= o) {
+            s_in += sv;
+            c_in += cv;
         }
+    }
+    if (lane == 63) {
+        chunk[wv] = s_in;
+        cost_chunk[wv] = c_in;
+    }
+    __syncthreads();
+    int base = 0;
+    long long cbase = 0;
+    for (int i = 0; i < wv; ++i) {
+        base += chunk[i];
+        cbase += cost_chunk[i];
+    }
+    if (tid == 1023) {
+        const int acc = base + s_in;
+        const long long cacc = cbase + c_in;
         const int n = (int)min((long)acc, cap);   // malformed offsets cannot push readers past the list
         count[0] = n;
         count[1] = (int)min((long long)n * H, (long long)INT_MAX);   // every item runs whole
@@ -460,9 +474,8 @@ __global__ __launch_bounds__(1024) void build_varlen_schedule(const int32_t* __r
         count[3] = n == acc;   // every entry listed (the cost prefix is whole)
         if (cum != nullptr && n == acc) cum[n] = cacc;
     }
-    __syncthreads();
-    long off = chunk[tid];
-    long long cc = cost_chunk[tid];
+    long off = base + s_in - sum;
+    long long cc = cbase + c_in - csum;
     for (int r = r0; r < r1; ++r) {
         const int s = order[r];
         const int len = seg_len(cu, s, T);
