@@ -92,8 +92,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * Here the split serves the workgroups' last round on the device: the query tiles that
  * would leave most compute units idle at the end are cut into equal shares of
  * (query tile, key tile) pairs, one share per resident workgroup, and the pieces of a cut
- * tile are combined as o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p (M = max_p m_p).
- * The result equals attn_fwd's within rounding (BF16 P is taken relative to each piece's own
+ * tile are combined as o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) (l_p + C_p) and
+ * lse = (M + log2 sum_p 2^(m_p - M) l_p) ln 2 (M = max_p m_p; l_p + C_p the piece's
+ * normaliser as in the numerics note above). The result equals attn_fwd's within rounding (BF16 P is taken relative to each piece's own
  * reference); for the same inputs, slots and device it is bitwise repeatable.
  *   q, k, v, out, lse, B, H, N, d, scale, stream : as for attn_fwd.
  *   slots  : workgroups that run at once; <= 0 means the current device's compute units
