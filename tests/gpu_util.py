@@ -145,3 +145,18 @@ def varlen_cut_rows(seqlens, H, slots, per_item=2, seed=0):
         for r in {lo, hi - 1, *rng.integers(lo, hi, per_item).tolist()}:
             rows.add(h * T + int(starts[s]) + r)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def dominated_dense(N, H=2, seed=31, vmax=7.0):
+    """Host BF16 bits [1, H, N, 128] of rows that one key dominates: K = Q, so each query's own
+    key has logit |q|^2/sqrt(128) (about 11, weight about 0.98 over the N(0,1) logits of the
+    others), and V ~ 2.5 N(0,1) clipped to +-vmax, so many outputs sit in [4, 8) where half a
+    BF16 ulp is 0.0156. Dividing by the FP32 sum alone leaves the dominant key's BF16 rounding
+    (up to 2^-8 of |v|) on top of that and misses the 2e-2 bar (a CPU replay of the key loop
+    on this case: 0.038); the kernel's corrected normaliser does not."""
+    from oracle import bf16_bits_to_f64
+    from workloads import f32_to_bf16_bits, random_dense
+    qb, _, _ = random_dense(1, H, N, seed=seed)
+    _, _, vb = random_dense(1, H, N, seed=seed + 1)
+    v = np.clip(bf16_bits_to_f64(vb) * 2.5, -vmax, vmax)
+    return qb, qb.copy(), f32_to_bf16_bits(v.astype(np.float32))

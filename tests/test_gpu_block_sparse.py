@@ -146,6 +146,23 @@ def test_hook_with_caller_lists(vd, name, rows_of):
     check(f64_of(out), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref, label=f"hook: {name}")
 
 
+def test_hook_dominated_rows(vd):
+    """The tile-list loop carries the same normaliser correction: rows that one key dominates
+    (K = Q, large V), each query tile's list holding its own diagonal key tiles plus every third
+    other tile, meet the bar against the oracle over the kept tiles."""
+    from gpu_util import dominated_dense
+    B, H, N = 1, 2, 1500
+    q, k, v = dominated_dense(N, H, seed=51)
+    idx, cnt, keep = custom_lists(B, H, N, lambda b, h, i, ntk: sorted(
+        set(range(4 * i, min(4 * i + 4, ntk))) | set(range(i % 3, ntk, 3))))
+    out, lse = vd.attn_fwd_block_sparse(dev(q), dev(k), dev(v), dev_i32(idx), dev_i32(cnt), scale=SCALE,
+                                        return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_kept(q, k, v, SCALE, keep)
+    assert np.abs(o_ref).max() > 4.0
+    check(f64_of(out), o_ref, lse.cpu().numpy().astype(np.float64), lse_ref, label="hook: dominated rows")
+
+
 def test_hook_empty_tile_and_clamped_counts(vd):
     """kv_cnt <= 0 gives O = 0 and LSE = -inf for that query tile; a count above ntk is read
     as ntk; other tiles are unaffected."""
