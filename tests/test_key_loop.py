@@ -77,7 +77,9 @@ def ws_of(op, ops):
 
 
 def is_block_end(op):
-    return op.startswith("s_branch") or op.startswith("s_cbranch") or op == "s_setpc_b64"
+    """An instruction after which straight-line code does not continue (a conditional branch
+    falls through, so the scans go on past it)."""
+    return op.startswith("s_branch") or op == "s_setpc_b64"
 
 
 def lds_violations(asm_lines):

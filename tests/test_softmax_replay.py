@@ -8,10 +8,12 @@ min(l, 2^24) takes the slow path. It keeps m until some lane's tile sum exceeds 
     has binary exponent e and m moves up by k = max(e + 1 + h, 0), h the key loop's headroom
     (48); P (BF16, exponent field
     minus k, flushed below 2^-126), the tile sums, l and O scale by 2^-k exactly;
-  * full exact path: otherwise (the first tile, where m = -inf, or a p beyond the FP32
-    range), m = max(row max + h, m), O and l scale by exp2(m_old - m), and P and the tile
+  * full exact path: otherwise (the first tile of a one-tile range, where m = -inf, or a p
+    beyond the FP32 range), m = max(row max + h, m), O and l scale by exp2(m_old - m), and P and the tile
     sums are recomputed.
-Every slow-path tile (with or without a move) then adds (sum of its BF16 p) - (its FP32 tile
+The first tile of a longer range takes m = row max + h from its scores before its softmax (the
+value the full path would give), so it needs no move. Every slow-path tile (with or without a
+move) then adds (sum of its BF16 p) - (its FP32 tile
 sum) to a correction C per lane, and O is divided by l + C, while the LSE takes l: the keys
 that end with half or more of a lane's weight sit in such tiles, so the normaliser of a row's
 dominant keys is the sum of exactly the BF16 values their products used.
@@ -81,7 +83,7 @@ def replay(x, v, n, scale_mode="ldexp", divisor="corrected"):
     cor = np.zeros((R, 2), f32)
     lb = np.zeros(R, f32)
     O = np.zeros((R, v.shape[1]))
-    moves = {"rebase": 0, "full": 0, "slow": 0}
+    moves = {"first": 0, "rebase": 0, "full": 0, "slow": 0}
     for t in range(ntk):
         xs = np.full((R, 64), -np.inf, f32)
         w = min(64, n - 64 * t)
@@ -96,6 +98,9 @@ def replay(x, v, n, scale_mode="ldexp", divisor="corrected"):
         def sums(p):
             return np.stack([p[:, lane == g].sum(axis=1, dtype=f32) for g in (0, 1)], axis=1)
 
+        if t == 0 and ntk >= 2:   # the first tile of a longer range: m from its scores
+            moves["first"] += 1
+            m = (xs.max(axis=1) + f32(HEADROOM)).astype(f32)
         p = probs(m)
         ts = sums(p)
         pb = bf16(p)
@@ -173,7 +178,7 @@ def test_replay_meets_the_bar_on_the_outlier_workload(stress, b, h, q0):
     m = compare(bf16(o), o_ref, lse, lse_ref)
     print(f"[replay] b={b} h={h} rows {q0}..: {moves}, rel_l2 {m['rel_l2']:.2e}, max_abs {m['max_abs']:.2e}, "
           f"lse {m['lse_max_abs']:.2e}")
-    assert moves["rebase"] > 0 and moves["full"] >= 1
+    assert moves["rebase"] > 0 and moves["first"] == 1
     assert m["ok"], m
 
 
@@ -217,11 +222,11 @@ def test_worst_climb_stays_inside_the_stated_value_bound(N):
     exceeds N * 2^24 * max|v|, so FP32 holds it while N * max|v| < 2^104."""
     R = 2
     x = np.zeros((R, N), f32)
-    x[:, :64] = 0.0                                   # first tile: the full path sets m = 0 + headroom
+    x[:, :64] = 0.0                                   # first tile: m = 0 + headroom
     x[:, 64:] = f32(HEADROOM + 24 - 5 - 1e-3)         # 32 keys per lane at just under 2^19 each
     v = np.ones((N, 4))
     o, lse, moves, O = replay(x, v, N)
-    assert moves["full"] == 1 and moves["rebase"] == 0
+    assert moves["first"] == 1 and moves["full"] == 0 and moves["rebase"] == 0
     bound = N * 2.0 ** 24 * 1.0
     assert np.abs(O).max() <= bound
     assert np.abs(O).max() >= bound / 64              # the bound is reached within a factor 2^6

@@ -27,9 +27,10 @@ holds four tiles.
 
 Softmax bookkeeping (per row block): m (the reference the probabilities are taken against,
 log2 units of the scaled logit), l (the lane's partial row sum of the FP32 probabilities) and C
-(the lane's normaliser correction). The common path computes p = exp2(S*c - m) and checks that
-no lane's tile sum exceeds its limit min(l, 2^24); when one does (always on the first tile,
-where m = -inf) the wave calls the slow path. If a tile sum exceeds 2^24 (or is not a
+(the lane's normaliser correction). The first tile of a range of two or more tiles takes m =
+(row maximum of S*c) + 48 from its own scores before its softmax. The common path computes
+p = exp2(S*c - m) and checks that no lane's tile sum exceeds its limit min(l, 2^24); when one
+does (always on the first tile, where l = 0) the wave calls the slow path. If a tile sum exceeds 2^24 (or is not a
 number) the reference moves: the rebase path shifts it by a whole power of two using the
 packed BF16 probabilities, or, when one of them is inf or NaN, the full path recomputes S of
 the tile from LDS, moves m to the running row maximum plus a headroom of 48, rescales O and
@@ -542,8 +543,9 @@ def rebase_path(E, X):
     normal range, weights under 2^-126 of the new reference, become 0), l, the tile sums and
     O by v_ldexp_f32 with -k. (Not by a multiplication with 2^-k: k reaches 177 when a key
     lies up to 128 log2 units above the old reference, and 2^-k then is no FP32 number, while
-    the tile's own sum times 2^-k is about 2^-49.) A probability that is inf or NaN (the first tile, where
-    m = -inf, or a key beyond the FP32 range of the old reference) carries no usable maximum:
+    the tile's own sum times 2^-k is about 2^-49.) A probability that is inf or NaN (the tile of
+    a one-tile range, where m = -inf, or a key beyond the FP32 range of the old reference) carries
+    no usable maximum:
     then the full path below recomputes S. Entered from the slow-path entry (no LDS read in
     flight); goes on to the correction with all wait states satisfied."""
     E.label(".Lmove%d_%%=" % X)
@@ -699,6 +701,41 @@ def slow_path(E, X):
     E.set_state(at_move)
 
 
+def first_reference(E, X):
+    """Reference of a range's first tile (S buffer X) taken from its scores, for ranges of two or
+    more tiles, whose first tile holds no key past the sequence end: m = (row maximum of S*c) +
+    headroom. The row maximum's probability is then 2^-headroom (rounding aside) and the tile
+    needs no reference move, only the slow path's correction, instead of the full path that
+    m = -inf would send it to. The row maximum of S*c is c * max S for c >= 0 and c * min S
+    otherwise; both chains run over the lane's 32 scores per row block and the partner lane's
+    (l ^ 32), and the larger product wins."""
+    mx, mn = (TMP0 + 2, TMP0 + 3), (TMP0 + 4, TMP0 + 5)
+    px, pn = (TMP0 + 6, TMP0 + 7), (TMP0 + 8, TMP0 + 9)
+    for rb in range(2):
+        regs = [sblk(X, rb, kb) + r for kb in range(2) for r in range(16)]
+        for acc, op3, op2 in ((mx[rb], "v_max3_f32", "v_max_f32"), (mn[rb], "v_min3_f32", "v_min_f32")):
+            E.valu("%s %s, %s, %s, %s" % (op3, vr(acc), vr(regs[0]), vr(regs[1]), vr(regs[2])),
+                   rd=vset(regs[0]) | vset(regs[1]) | vset(regs[2]), wr=vset(acc))
+            i = 3
+            while i + 1 < len(regs):
+                E.valu("%s %s, %s, %s, %s" % (op3, vr(acc), vr(acc), vr(regs[i]), vr(regs[i + 1])),
+                       rd=vset(acc) | vset(regs[i]) | vset(regs[i + 1]), wr=vset(acc))
+                i += 2
+            if i < len(regs):
+                E.valu("%s %s, %s, %s" % (op2, vr(acc), vr(acc), vr(regs[i])), rd=vset(acc) | vset(regs[i]), wr=vset(acc))
+    for rb in range(2):
+        for src, dst in ((mx[rb], px[rb]), (mn[rb], pn[rb])):
+            E.emit(Ins("ds_bpermute_b32 %s, %%[bperm], %s" % (vr(dst), vr(src)), "lds", rd=vset(src), wr=vset(dst), lds=True))
+    hr = struct.unpack("<I", struct.pack("<f", float(OPTS["headroom"])))[0]
+    for rb in range(2):
+        E.valu("v_max_f32 %s, %s, %s" % (vr(mx[rb]), vr(mx[rb]), vr(px[rb])), rd=vset(mx[rb]) | vset(px[rb]), wr=vset(mx[rb]))
+        E.valu("v_min_f32 %s, %s, %s" % (vr(mn[rb]), vr(mn[rb]), vr(pn[rb])), rd=vset(mn[rb]) | vset(pn[rb]), wr=vset(mn[rb]))
+        E.valu("v_mul_f32 %s, %%[c], %s" % (vr(mx[rb]), vr(mx[rb])), rd=vset(mx[rb]), wr=vset(mx[rb]))
+        E.valu("v_mul_f32 %s, %%[c], %s" % (vr(mn[rb]), vr(mn[rb])), rd=vset(mn[rb]), wr=vset(mn[rb]))
+        E.valu("v_max_f32 %s, %s, %s" % (vr(M[rb]), vr(mx[rb]), vr(mn[rb])), rd=vset(mx[rb]) | vset(mn[rb]), wr=vset(M[rb]))
+        E.valu("v_add_f32 %s, 0x%08x, %s" % (vr(M[rb]), hr, vr(M[rb])), rd=vset(M[rb]), wr=vset(M[rb]))
+
+
 def final_phase(E, Y, stage, uid):
     """The last tile (S buffer Y, LDS stage): masked second softmax half, check, PV."""
     for f in softmax_half(Y, 1, True, KLIM_IN, H2):
@@ -757,6 +794,7 @@ def generate(backedge=None):
     qk_phase(E, 0, 0, [])
     E.raw("s_cmp_eq_u32 %[T], 1")
     E.raw("s_cbranch_scc1 .LT1_%=")
+    first_reference(E, 0)
     for f in softmax_half(0, 0, False, None, H1):
         f(E)
     prefetch_k(E, 1)
