@@ -330,15 +330,22 @@ def linear(lib, q=LQ, k=LK, qr=LQR, kr=LKR, v=LV, o=LO, B=1, N=300, H=2, d=128, 
 def test_linear_workspace_query(lib):
     f = lib.attn_linear_workspace_bytes
     # per head: one chunk partial (128*128 + 128 floats) per chunk, then kv as three BF16
-    # terms and ksum (FP32), each region 256-byte aligned. A chunk is 2048 tokens, halved down
-    # to 256 while B*H*chunks < 512.
+    # terms and ksum (FP32), each region 256-byte aligned. The chunk is the shortest multiple of
+    # 64 tokens (256 to 4096) whose B*H*chunks workgroups fit whole rounds of 3 per compute
+    # unit; without a GPU the query assumes 256 compute units (768 slots).
     a = lambda x: (x + 255) // 256 * 256
     one, terms, ks = (128 * 128 + 128) * 4, 3 * 128 * 128 * 2, 128 * 4
-    assert f(1, 300, 2, 128) == a(2 * 2 * one) + a(2 * terms) + a(2 * ks)            # 256-token chunks
-    assert f(1, 180320, 16, 128) == a(16 * 89 * one) + a(16 * terms) + a(16 * ks)    # 2048: 1424 groups
-    assert f(1, 180320, 2, 128) == a(2 * 353 * one) + a(2 * terms) + a(2 * ks)       # 512: 706 groups
-    assert f(1, 180320, 4, 128) == a(4 * 177 * one) + a(4 * terms) + a(4 * ks)       # 1024: 708 groups
-    assert f(1, 180320, 8, 128) == a(8 * 89 * one) + a(8 * terms) + a(8 * ks)        # 2048: 712 groups
+
+    def expect(B, N, H, chunks):
+        return a(B * H * chunks * one) + a(B * H * terms) + a(B * H * ks)
+    assert f(1, 300, 2, 128) == expect(1, 300, 2, 2)              # 256-token chunks: 4 groups
+    assert f(1, 180320, 16, 128) == expect(1, 180320, 16, 48)     # 3776: 768 groups, one round
+    assert f(1, 180320, 2, 128) == expect(1, 180320, 2, 353)      # 512: 706 groups
+    assert f(1, 180320, 4, 128) == expect(1, 180320, 4, 188)      # 960: 752 groups
+    assert f(1, 180320, 8, 128) == expect(1, 180320, 8, 94)       # 1920: 752 groups
+    assert f(1, 32760, 16, 128) == expect(1, 32760, 16, 47)       # 704: 752 groups
+    assert f(1, 32760, 2, 128) == expect(1, 32760, 2, 128)        # 86 -> 256 (the floor): 256 groups
+    assert f(4, 180320, 16, 128) == expect(4, 180320, 16, 48)     # 4096 needs 45 chunks a head: four rounds, 3776
     assert f(0, 300, 2, 128) == 0 and f(1, 300, 2, 64) == 0
 
 

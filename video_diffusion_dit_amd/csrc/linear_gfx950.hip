@@ -18,10 +18,12 @@
 //       (ds_read_b64_tr_b16) give each lane 8 consecutive tokens of one dim, the MFMA's
 //       operand layout for both A = V^T and B = K_rot.
 //   linear_kv_reduce_kernel   sums the chunk partials in a fixed order (deterministic) and
-//       splits kv exactly into three BF16 terms. A chunk is 2048 tokens, halved (down to 256)
-//       while the kv pass would have fewer than 512 workgroups, so calls with few heads
-//       (one GPU's share of a head-sharded call) still fill the compute units; the chunk
-//       depends only on B*H and N.
+//       splits kv exactly into three BF16 terms. The chunk (a multiple of 64 tokens, 256 to
+//       4096) is the shortest that lets the kv pass's B*H*chunks workgroups fill whole rounds
+//       of the device's resident workgroups (three per compute unit): one round where 4096-token
+//       chunks suffice, else the fewest rounds that allow them. So calls with few heads (one
+//       GPU's share of a head-sharded call) still fill the compute units, and no round runs
+//       part-empty; the chunk depends on B*H, N and the device's compute-unit count.
 //   linear_out_kernel         one workgroup per (b, h, 1024 tokens): out = kv q_rot / den;
 //       each wave keeps 32 rows of kv in registers, q_rot arrives in LDS by buffer->LDS loads.
 //       The FP32 product runs on the BF16 matrix cores: kv = hi + mid + lo with three BF16
@@ -31,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "attn_launch.h"
 
@@ -47,11 +51,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = 128;
 constexpr int NT = 256;              // threads per workgroup (4 waves)
 constexpr int TILE = 64;             // tokens per LDS tile in the kv pass
-constexpr int KV_CHUNK_MAX = 2048;   // tokens per workgroup in the kv pass (multiples of TILE)
-constexpr int KV_CHUNK_MIN = 256;
-#ifndef LIN_KV_MIN_GROUPS
-#define LIN_KV_MIN_GROUPS 512        // kv-pass workgroups below which the chunk is halved
-#endif
+constexpr int KV_CHUNK_MAX = 4096;   // tokens per workgroup in the kv pass (multiples of TILE)
+constexpr int KV_CHUNK_MIN = 256;    // shorter chunks pay their partial write and setup more often
+constexpr int KV_PER_CU = 3;         // kv-pass workgroups resident per compute unit (LDS bound)
 constexpr int ROW = D * 2 + 32;      // LDS row stride in bytes (padded: 8-bank shift per row)
 constexpr int KV_TERMS = 3;          // BF16 terms of the FP32 kv in the output pass
 #define LIN_OUT_SUB 128              // tokens per sub-block of the output pass (a multiple of 64)
@@ -513,10 +515,32 @@ __global__ __launch_bounds__(NT, LIN_OUT_SUB == 128 ? 2 : 1) void linear_out_ker
 
 namespace attn_impl {
 
+// Resident kv-pass workgroups of the current device (compute units x KV_PER_CU); without a
+// device (a host-only query) an MI355X's 256 compute units are assumed.
+static long kv_slots() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    return (long)cus * KV_PER_CU;
+}
+
+// Tokens per kv-pass chunk: the shortest multiple of TILE (at least KV_CHUNK_MIN, at most
+// KV_CHUNK_MAX) whose B*H*chunks workgroups fit in r whole rounds of the resident slots, for the
+// smallest r that allows chunks of at most KV_CHUNK_MAX.
 static int kv_chunk(size_t bh, int N) {
-    int c = KV_CHUNK_MAX;
-    while (c > KV_CHUNK_MIN && bh * (size_t)((N + c - 1) / c) < (size_t)LIN_KV_MIN_GROUPS) c >>= 1;
-    return c;
+    const long slots = kv_slots();
+    const long need = (N + KV_CHUNK_MAX - 1) / KV_CHUNK_MAX;          // chunks per sequence at the cap
+    long r = std::max(1L, (long)((need * (long)bh + slots - 1) / slots));
+    for (;; ++r) {
+        const long cps = r * slots / (long)bh;                        // chunks per sequence in r rounds
+        if (cps < 1) continue;
+        long c = (N + cps - 1) / cps;
+        c = std::max((long)KV_CHUNK_MIN, (c + TILE - 1) / TILE * TILE);
+        if (c <= KV_CHUNK_MAX) return (int)c;
+    }
 }
 
 static int linear_chunks(size_t bh, int N) {
