@@ -268,7 +268,9 @@ int attn_linear_fwd(const void* q, const void* k, const void* q_rot, const void*
                     void* out, int B, int N, int H, int d, float eps, void* workspace,
                     size_t workspace_bytes, void* stream);
 
-/* Workspace bytes attn_linear_fwd needs (0 if the sizes are invalid). */
+/* Workspace bytes attn_linear_fwd needs (0 if the sizes are invalid). The kv pass's token
+ * chunks fill whole rounds of the current device's resident workgroups, so query it with the
+ * device that will run the call current (without a device, 256 compute units are assumed). */
 size_t attn_linear_workspace_bytes(int B, int N, int H, int d);
 
 /*
