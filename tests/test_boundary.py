@@ -384,6 +384,7 @@ def test_block_list_stride_and_route_workspace(lib):
     assert lib.attn_block_list_stride(180320) == 2818 + 8
     assert lib.attn_block_list_stride(0) == 0
     # pooled query tiles (FP32 [B*H][ceil(N/256)][128], 256-byte aligned), then pooled key tiles
+    # (FP32 [B*H][32][ceil(N/64)][4])
     a = lambda x: (x + 255) // 256 * 256
     assert lib.attn_block_route_workspace_bytes(2, 3, 1000, 128) == a(6 * 4 * 512) + 6 * 16 * 512
     assert lib.attn_block_route_workspace_bytes(1, 2, 1000, 64) == 0

@@ -258,6 +258,17 @@ def test_long_sequence_routes_one_query_tile_per_workgroup(vd):
           lse_ref, label="block-sparse N=260000 tau=0.01 sampled rows")
 
 
+@pytest.mark.parametrize("N", [1300, 245760, 245761])
+def test_route_query_tiles_per_workgroup(vd, N):
+    """The routing groups 4 query tiles per workgroup while their proxies fit in LDS (up to
+    3840 key tiles, N = 245760), then 1: both sides of the bound, and a last group of 2 query
+    tiles (N = 1300), routed against the oracle over every tile."""
+    q, k, _ = random_dense(1, 1, N, seed=N % 1000 + 3)
+    kv_idx, kv_cnt = route(vd, q, k, 0.01)
+    keep_gpu = lists_to_keep(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), -(-N // 64))
+    check_route(keep_gpu, q, k, 0.01, 0)
+
+
 @pytest.fixture(scope="module")
 def video_720p():
     return make_dense(WORKLOADS["video_720p"])

@@ -14,13 +14,18 @@
 // hold ntk.
 //
 // Kernels (HBM-bound pooling, then L2-resident routing):
-//   pool_kernel<RB>: one workgroup per 256 rows of one (b, h); thread (row lane rl, 16-byte
+//   pool_kernel<RB, KT>: one workgroup per 256 rows of one (b, h); thread (row lane rl, 16-byte
 //     chunk ch) sums rows rl, rl+16, ... of each RB-row block in FP32, the 16 row lanes are
-//     added in order through LDS, and the sum is divided by the block's valid rows.
+//     added in order through LDS, and the sum is divided by the block's valid rows. The query
+//     means are stored row by row ([BH][ntq][128]); the key means (KT) by groups of four
+//     dimensions, tile-minor ([BH][32][ntk] float4), so that the lanes of a wave, which take
+//     consecutive key tiles, read one contiguous kilobyte per load.
 //   route_kernel<QPW>: one workgroup per QPW query tiles of one (b, h); thread J computes the
-//     QPW proxies of key tile J (128-term FP32 dot products) into LDS; then per query tile a
-//     block-wide max, the threshold, and an ordered compaction (each thread owns a contiguous
-//     run of tiles; a wave-level scan of the run counts gives the write offsets).
+//     QPW proxies of key tile J (128-term FP32 dot products, dimensions in order, the query
+//     means read through scalar loads) into LDS;
+//     then per query tile a block-wide max, the threshold, and an ordered compaction (each
+//     thread owns a contiguous run of tiles; a wave-level scan of the run counts gives the
+//     write offsets).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -40,7 +45,7 @@ constexpr int ROUTE_LDS_LIMIT = 61440;   // bytes of proxies a workgroup keeps i
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <int RB>
+template <int RB, bool KT>
 __global__ __launch_bounds__(256) void pool_kernel(const bf16* __restrict__ x, float* __restrict__ out, int N,
                                                    int nblk) {
     constexpr int NB = 256 / RB;    // pooled blocks per workgroup
@@ -71,19 +76,22 @@ __global__ __launch_bounds__(256) void pool_kernel(const bf16* __restrict__ x, f
     }
     __syncthreads();
     for (int t = tid; t < NB * D; t += 256) {
-        const int b = t / D, c = t - b * D;
+        // KT: 4 consecutive threads take 4 dimensions of one block, the next 4 the next block
+        const int b = KT ? (t >> 2) % NB : t / D;
+        const int c = KT ? 4 * (t / (4 * NB)) + (t & 3) : t - b * D;
         const int blk = w * NB + b;
         const int rows = min(RB, N - blk * RB);
         if (rows <= 0) continue;
         float s = 0.f;
         for (int j = 0; j < 16; ++j) s += red[j][b][c];
-        out[((long)bh * nblk + blk) * D + c] = s / (float)rows;
+        const long o = KT ? (((long)bh * (D / 4) + (c >> 2)) * nblk + blk) * 4 + (c & 3) : ((long)bh * nblk + blk) * D + c;
+        out[o] = s / (float)rows;
     }
 }
 
 struct RouteArgs {
     const float* qbar;   // [BH][ntq][128]
-    const float* kbar;   // [BH][ntk][128]
+    const float* kbar;   // [BH][32][ntk][4]: dimensions 4c..4c+3 of key tile J at [bh][c][J]
     int32_t* kidx;
     int32_t* kcnt;
     int ntq, ntk, stride, nsink;
@@ -102,33 +110,31 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 template <int QPW>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     extern __shared__ float zs[];   // [QPW][ntk]
-    __shared__ float qs[QPW][D];
     __shared__ float red[4];
     __shared__ int wsum[4];
     const int gpb = (a.ntq + QPW - 1) / QPW;
     const int bh = blockIdx.x / gpb, g = blockIdx.x - bh * gpb;
     const int qt0 = g * QPW, nq = min(QPW, a.ntq - qt0);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    for (int t = tid; t < QPW * D; t += 256) {
-        const int qi = t / D;
-        qs[qi][t - qi * D] = qi < nq ? a.qbar[((long)bh * a.ntq + qt0 + qi) * D + (t - qi * D)] : 0.f;
-    }
-    __syncthreads();
-    const float* kb = a.kbar + (long)bh * a.ntk * D;
+    // the query means are the same for every lane: read at wave-uniform addresses (scalar
+    // loads); a group's missing last tiles repeat tile ntq - 1 and are never compacted
+    const float* __restrict__ qg[QPW];
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) qg[qi] = a.qbar + ((long)bh * a.ntq + min(qt0 + qi, a.ntq - 1)) * D;
+    const float4* kb = reinterpret_cast<const float4*>(a.kbar) + (long)bh * (D / 4) * a.ntk;
     for (int J = tid; J < a.ntk; J += 256) {
         float z[QPW];
 #pragma unroll
         for (int qi = 0; qi < QPW; ++qi) z[qi] = 0.f;
-        const float4* kr = reinterpret_cast<const float4*>(kb + (long)J * D);
 #pragma unroll 4
         for (int c4 = 0; c4 < D / 4; ++c4) {
-            const float4 kv = kr[c4];
+            const float4 kv = kb[(long)c4 * a.ntk + J];
 #pragma unroll
             for (int qi = 0; qi < QPW; ++qi) {
-                z[qi] = fmaf(qs[qi][4 * c4 + 0], kv.x, z[qi]);
-                z[qi] = fmaf(qs[qi][4 * c4 + 1], kv.y, z[qi]);
-                z[qi] = fmaf(qs[qi][4 * c4 + 2], kv.z, z[qi]);
-                z[qi] = fmaf(qs[qi][4 * c4 + 3], kv.w, z[qi]);
+                z[qi] = fmaf(qg[qi][4 * c4 + 0], kv.x, z[qi]);
+                z[qi] = fmaf(qg[qi][4 * c4 + 1], kv.y, z[qi]);
+                z[qi] = fmaf(qg[qi][4 * c4 + 2], kv.z, z[qi]);
+                z[qi] = fmaf(qg[qi][4 * c4 + 3], kv.w, z[qi]);
             }
         }
 #pragma unroll
@@ -224,11 +230,13 @@ __device__ __forceinline__ int tile_segment(const int* off, int nseg, int g) {
 }
 
 // Mean of one RB-row tile of one head: workgroup (tile g, head h); thread (row lane rl, chunk
-// ch) sums rows rl, rl+16, ...; the 16 row lanes are added in order through LDS.
+// ch) sums rows rl, rl+16, ...; the 16 row lanes are added in order through LDS. Stored at
+// [g][h][128] (kt = 0), or, for the key means, by groups of four dimensions, tile-minor, at
+// [h][32][kt][4] (kt = the tile capacity), as pool_kernel stores them.
 template <int RB>
 __global__ __launch_bounds__(256) void pool_varlen_kernel(const bf16* __restrict__ x, float* __restrict__ out,
                                                           const int32_t* __restrict__ cu, const int* __restrict__ off,
-                                                          int nseg, int H, int T) {
+                                                          int nseg, int H, int T, int kt) {
     __shared__ float red[16][D];
     const int g = blockIdx.x / H, h = blockIdx.x - g * H;
     if (g >= off[nseg]) return;
@@ -254,18 +262,19 @@ __global__ __launch_bounds__(256) void pool_varlen_kernel(const bf16* __restrict
     if (tid < D) {
         float sum = 0.f;
         for (int j = 0; j < 16; ++j) sum += red[j][tid];
-        out[((long)g * H + h) * D + tid] = sum / (float)rows;
+        const long o = kt > 0 ? (((long)h * (D / 4) + (tid >> 2)) * kt + g) * 4 + (tid & 3) : ((long)g * H + h) * D + tid;
+        out[o] = sum / (float)rows;
     }
 }
 
 struct RouteVarlenArgs {
     const float* qbar;   // [tiles_q][H][128]
-    const float* kbar;   // [tiles_k][H][128]
+    const float* kbar;   // [H][32][ktiles][4]: dimensions 4c..4c+3 of key tile j at [h][c][j]
     const int* off_q;
     const int* off_k;
     int32_t* kidx;       // [tiles_q * H][stride]
     int32_t* kcnt;       // [tiles_q * H]
-    int nseg, H, stride, nsink;
+    int nseg, H, stride, nsink, ktiles;
     float scale, tau;
 };
 
@@ -273,7 +282,6 @@ struct RouteVarlenArgs {
 // then the threshold and the ordered compaction as route_kernel does.
 __global__ __launch_bounds__(256) void route_varlen_kernel(RouteVarlenArgs a) {
     extern __shared__ float zs[];
-    __shared__ float qs[D];
     __shared__ float red[4];
     __shared__ int wsum[4];
     const int g = blockIdx.x / a.H, h = blockIdx.x - g * a.H;
@@ -281,18 +289,17 @@ __global__ __launch_bounds__(256) void route_varlen_kernel(RouteVarlenArgs a) {
     const int s = tile_segment(a.off_q, a.nseg, g);
     const int k0 = a.off_k[s], ntk = a.off_k[s + 1] - k0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (tid < D) qs[tid] = a.qbar[((long)g * a.H + h) * D + tid];
-    __syncthreads();
+    const float* __restrict__ qg = a.qbar + ((long)g * a.H + h) * D;   // wave-uniform (scalar loads)
+    const float4* kb = reinterpret_cast<const float4*>(a.kbar) + (long)h * (D / 4) * a.ktiles + k0;
     for (int J = tid; J < ntk; J += 256) {
-        const float4* kr = reinterpret_cast<const float4*>(a.kbar + ((long)(k0 + J) * a.H + h) * D);
         float z = 0.f;
 #pragma unroll 4
         for (int c4 = 0; c4 < D / 4; ++c4) {
-            const float4 kv = kr[c4];
-            z = fmaf(qs[4 * c4 + 0], kv.x, z);
-            z = fmaf(qs[4 * c4 + 1], kv.y, z);
-            z = fmaf(qs[4 * c4 + 2], kv.z, z);
-            z = fmaf(qs[4 * c4 + 3], kv.w, z);
+            const float4 kv = kb[(long)c4 * a.ktiles + J];
+            z = fmaf(qg[4 * c4 + 0], kv.x, z);
+            z = fmaf(qg[4 * c4 + 1], kv.y, z);
+            z = fmaf(qg[4 * c4 + 2], kv.z, z);
+            z = fmaf(qg[4 * c4 + 3], kv.w, z);
         }
         zs[J] = z * a.scale;
     }
@@ -439,11 +446,11 @@ hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t
     float* qbar = reinterpret_cast<float*>(ws + tile_offsets_bytes(nseg));
     float* kbar = reinterpret_cast<float*>(ws + tile_offsets_bytes(nseg) + align256(tq * H * D * sizeof(float)));
     hipLaunchKernelGGL(pool_varlen_kernel<BMQ>, dim3((unsigned)(tq * H)), dim3(256), 0, stream,
-                       static_cast<const bf16*>(q), qbar, cu, off_q, nseg, H, T);
+                       static_cast<const bf16*>(q), qbar, cu, off_q, nseg, H, T, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pool_varlen_kernel<BNK>, dim3((unsigned)(tk * H)), dim3(256), 0, stream,
-                       static_cast<const bf16*>(k), kbar, cu, off_k, nseg, H, T);
+                       static_cast<const bf16*>(k), kbar, cu, off_k, nseg, H, T, (int)tk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     RouteVarlenArgs a;
@@ -455,6 +462,7 @@ hipError_t launch_block_route_varlen(const void* q, const void* k, const int32_t
     a.kcnt = kv_cnt;
     a.nseg = nseg;
     a.H = H;
+    a.ktiles = (int)tk;
     a.stride = (T + BNK - 1) / BNK + LIST_PAD;
     a.nsink = sink_tokens > 0 ? (int)(((long)sink_tokens + BNK - 1) / BNK) : 0;
     a.scale = scale;
@@ -481,11 +489,11 @@ hipError_t launch_block_route(const void* q, const void* k, int B, int H, int N,
     const size_t qb = ((size_t)bh * ntq * D * sizeof(float) + 255) & ~size_t(255);
     float* kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + qb);
     const unsigned pool_grid = (unsigned)(bh * ((N + 255) / 256));
-    hipLaunchKernelGGL(pool_kernel<BMQ>, dim3(pool_grid), dim3(256), 0, stream, static_cast<const bf16*>(q), qbar,
+    hipLaunchKernelGGL((pool_kernel<BMQ, false>), dim3(pool_grid), dim3(256), 0, stream, static_cast<const bf16*>(q), qbar,
                        N, ntq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pool_kernel<BNK>, dim3(pool_grid), dim3(256), 0, stream, static_cast<const bf16*>(k), kbar,
+    hipLaunchKernelGGL((pool_kernel<BNK, true>), dim3(pool_grid), dim3(256), 0, stream, static_cast<const bf16*>(k), kbar,
                        N, ntk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
