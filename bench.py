@@ -3,8 +3,9 @@
 
 A step is one call of the hot path -- the HIP attention forward (``attn_fwd``, or
 ``attn_fwd_varlen`` for the packed workload) -- over one batch of seeded synthetic BF16
-inputs that are already resident in HBM. W untimed warm-up steps, then exactly K timed
-steps between device synchronisations. Throughput counts 4*B*H*N^2*d flops per step
+inputs that are already resident in HBM. W untimed warm-up steps (by default as many as
+take about half a second, at least 3), then exactly K timed steps between device
+synchronisations. Throughput counts 4*B*H*N^2*d flops per step
 (packed: sum over segments of 4*H*n^2*d) and is reported in TFLOP/s against the MI355X
 dense BF16 MFMA peak; the kernel's own duration is measured with HIP events recorded on
 the stream it is launched on.
@@ -42,6 +43,7 @@ KERNEL_SOURCES = {
     "block_sparse_varlen": ("attn_fwd_gfx950.hip", "key_loop_idx_gfx950.inc", "block_route_gfx950.hip"),
 }
 PROFILES = os.path.join(ROOT, "profiles")
+WARMUP_S = 0.5   # default warm-up length in seconds
 
 
 def kernel_source_hash(kind: str = "dense") -> str:
@@ -791,7 +793,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed calls before the timed ones (default: enough for about half a second, at "
+                         "least 3; short calls timed from a cold GPU run before the shader clock has settled)")
     ap.add_argument("--workload", default="video_720p")
     ap.add_argument("--heads", type=int, default=0,
                     help="dense workloads: run the first HEADS heads only (the same values), i.e. one "
@@ -887,7 +891,17 @@ def main() -> int:
             vd.attention._launch_varlen(q, k, v, cu_d, out, lse, w.scale, cu_host)
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    done = 0
+    if args.warmup is None:   # size the warm-up from the second call's duration
+        step()
+        torch.cuda.synchronize()
+        t_one = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        one_s = max(time.perf_counter() - t_one, 1e-6)
+        args.warmup = max(3, int(np.ceil(WARMUP_S / one_s)))
+        done = 2
+    for _ in range(args.warmup - done):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
