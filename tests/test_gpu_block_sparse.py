@@ -373,6 +373,18 @@ def test_varlen_route_and_attention_small(vd, lens, H, tau, sink):
           label=f"block-sparse varlen {lens} H{H} tau={tau} sink={sink}")
 
 
+def test_varlen_route_at_the_routing_limit(vd):
+    """A packed batch of T = 983040 tokens, route_max_tiles (15360) key tiles, the most the
+    routing takes: one segment of 900000 tokens and one of 83040, one head. Each query tile's
+    proxies fill the routing workgroup's LDS allowance (60 KiB), and the key means are read at
+    the largest tile stride. Routing against the oracle over every tile of both segments."""
+    lens, H = (900000, 83040), 1
+    q, k, _, cu = random_varlen(lens, H, seed=983)
+    _, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, 0.01)
+    keeps = varlen_keeps(vd, kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), cu, H)
+    check_route_varlen(keeps, q, k, cu, 0.01, 0)
+
+
 def test_varlen_every_tile_listed_equals_varlen_bits(vd):
     q, k, v, cu = random_varlen((700, 1, 64, 300), 3, seed=77)
     cu_d, kv_idx, kv_cnt = run_varlen_route(vd, q, k, cu, math.inf)
