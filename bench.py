@@ -801,8 +801,8 @@ def main() -> int:
                     help="dense workloads: run the first HEADS heads only (the same values), i.e. one "
                          "GPU's share of a head-sharded call at full N (0: all heads)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
-                    help="query rows of the seeded sample the FP64 oracle is timed and checked on (8192: 10-20 s of "
-                         "FP64 work on 16 host cores at 720p)")
+                    help="query rows of the seeded sample the FP64 oracle is timed and checked on (8192: 7-20 s of "
+                         "FP64 work on 16 host cores at 720p, depending on the box)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split-kv", action="store_true",
                     help="plain attn_fwd / attn_fwd_varlen, without cutting the last tiles over keys")
