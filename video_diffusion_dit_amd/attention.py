@@ -530,7 +530,7 @@ def attn_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
 def block_skip_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tau: float,
                          sink_tokens: int = 0, scale: float | None = None, return_lse: bool = False):
     """block_route, then attn_fwd_block_sparse over its lists in the routing's order: head by
-    head, the longest lists first (7.5 % faster than item order on the 720p grid)."""
+    head, the longest lists first (8 % faster than item order on the 720p grid)."""
     kv_idx, kv_cnt, order = block_route(q, k, tau=tau, sink_tokens=sink_tokens, scale=scale, with_order=True)
     return attn_fwd_block_sparse(q, k, v, kv_idx, kv_cnt, scale=scale, return_lse=return_lse, order=order)
 
