@@ -46,6 +46,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 WARMUP_S = 0.5   # default warm-up length in seconds
 
 
+def default_warmup(one_call_s: float) -> int:
+    """Warm-up calls for a call of one_call_s seconds: about WARMUP_S seconds of them, at
+    least 3 (the two calls that measured the duration included)."""
+    import math
+    return max(3, math.ceil(WARMUP_S / max(one_call_s, 1e-6)))
+
+
 def kernel_source_hash(kind: str = "dense") -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
@@ -898,8 +905,7 @@ def main() -> int:
         t_one = time.perf_counter()
         step()
         torch.cuda.synchronize()
-        one_s = max(time.perf_counter() - t_one, 1e-6)
-        args.warmup = max(3, int(np.ceil(WARMUP_S / one_s)))
+        args.warmup = default_warmup(time.perf_counter() - t_one)
         done = 2
     for _ in range(args.warmup - done):
         step()

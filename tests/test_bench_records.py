@@ -121,3 +121,11 @@ def test_kernel_names_as_the_profiler_writes_them():
     assert bench._base_name("(anonymous namespace)::merge_kernel((anonymous namespace)::DenseArgs)") == "merge_kernel"
     assert bench._base_name("_ZN12_GLOBAL__N_118pool_varlen_kernelILi256EEEvPKDF16bPfPKiS5_iii") == "pool_varlen_kernel"
     assert bench._base_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_default_warmup_lasts_about_half_a_second():
+    assert bench.default_warmup(0.19) == 3          # the 720p call: three calls, ~0.6 s
+    assert bench.default_warmup(0.00085) == 589     # the stress call: ~0.5 s of calls
+    assert bench.default_warmup(0.0) == 500000      # no measurable duration: bounded
+    n = bench.default_warmup(0.0064)
+    assert 0.5 <= n * 0.0064 < 0.5 + 0.0064
